@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for the KDA prefill and decode paths.
+
+This module only draws random numbers and casts them; it holds none of the
+recurrence's arithmetic.  Both the GPU path's tests/benchmark and the CPU
+oracle's tests take their inputs from here, so the two sides see the same
+values.  (q, k are L2-normalised here because the prefill workloads hand the
+kernel already-normalised q, k; that normalisation is part of the input recipe,
+not of the kernel under test.)
+
+Workloads (shapes as named; every value is synthetic):
+  tiny_fp32      B=1  H=2  T=256    d=64   fp32  chunk 16  S0 = 0          seed 0 (CPU)
+  prefill_b4h32  B=4  H=32 T=4096   d=128  bf16  S0 ~ 0.02 N(0,1)         seed 1 (CPU)
+  k3_prefill     B=1  H=96 T=65536  d=128  bf16  + 10% of tokens g=-4.99   seed 2
+  stream_1m      16 segments of k3_prefill's shape, state carried          seed 3000+s
+  decode         N=256 H=96 d=128, 64 steps, bf16                          seed 4000+step
+Long-memory variants (make the state matter across chunks):
+  L1  tiny_fp32 shape, g = -5 sigmoid(N(0,1) - 7), upper half of the key channels g = 0
+  L2  prefill_b4h32 shape with the L1 gate distribution
+  L3  prefill_b4h32 shape, beta = 0, g = -1e-3, S0 ~ N(0,1)
+
+Draw order per call: q, k, v, beta logits, g logits, S0, then the bound mask
+(k3_prefill only).  Decode state: conv weights, conv cache, S.  Decode step:
+q_pre, k_pre, v_pre, beta logits, g logits.
+"""
+from dataclasses import dataclass, field
+
+import torch
+
+G_MIN = -5.0
+
+
+@dataclass(frozen=True)
+class PrefillSpec:
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    dtype: str = "bf16"          # "bf16" or "fp32"
+    seed: int = 0
+    s0_std: float = 0.02         # 0 -> S0 is None (zero state)
+    gate: str = "standard"       # "standard" | "long" | "const"
+    g_const: float = 0.0
+    beta_zero: bool = False
+    bound_frac: float = 0.0      # fraction of tokens whose g is set to bound_value
+    bound_value: float = -4.99
+    chunk: int = 32
+
+
+@dataclass(frozen=True)
+class DecodeSpec:
+    N: int
+    H: int
+    dk: int
+    dv: int
+    width: int = 4
+    steps: int = 64
+    dtype: str = "bf16"
+    seed_base: int = 4000
+    state_seed: int = 4999
+    gate: str = "standard"
+
+
+WORKLOADS = {
+    "tiny_fp32": PrefillSpec(B=1, H=2, T=256, dk=64, dv=64, dtype="fp32", seed=0, s0_std=0.0, chunk=16),
+    "prefill_b4h32": PrefillSpec(B=4, H=32, T=4096, dk=128, dv=128, seed=1),
+    "k3_prefill": PrefillSpec(B=1, H=96, T=65536, dk=128, dv=128, seed=2, bound_frac=0.1),
+    "L1": PrefillSpec(B=1, H=2, T=256, dk=64, dv=64, dtype="fp32", seed=10, s0_std=0.0, gate="long", chunk=16),
+    "L1_bf16": PrefillSpec(B=1, H=2, T=256, dk=64, dv=64, dtype="bf16", seed=11, s0_std=0.0, gate="long"),
+    "L2": PrefillSpec(B=4, H=32, T=4096, dk=128, dv=128, seed=12, gate="long"),
+    "L3": PrefillSpec(B=4, H=32, T=4096, dk=128, dv=128, seed=13, s0_std=1.0, gate="const",
+                      g_const=-1e-3, beta_zero=True),
+}
+STREAM_1M = dict(base=WORKLOADS["k3_prefill"], segments=16, seed_base=3000)
+DECODE = DecodeSpec(N=256, H=96, dk=128, dv=128)
+
+
+def torch_dtype(name):
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[name]
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, gen, device):
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def _unit(x):
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def prefill_inputs(spec: PrefillSpec, device="cpu", seed=None, T=None):
+    """Return dict(q, k, v, g, beta, S0) for one prefill call.
+
+    q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H] in spec.dtype;
+    S0: [B,H,dk,dv] fp32, or None when spec.s0_std == 0.
+    """
+    seed = spec.seed if seed is None else seed
+    T = spec.T if T is None else T
+    B, H, dk, dv = spec.B, spec.H, spec.dk, spec.dv
+    dt = torch_dtype(spec.dtype)
+    gen = _gen(device, seed)
+    q = _unit(_randn((B, T, H, dk), gen, device))
+    k = _unit(_randn((B, T, H, dk), gen, device))
+    v = _randn((B, T, H, dv), gen, device)
+    beta_logit = _randn((B, T, H), gen, device)
+    g_logit = _randn((B, T, H, dk), gen, device)
+    if spec.beta_zero:
+        beta = torch.zeros_like(beta_logit)
+    else:
+        beta = torch.sigmoid(beta_logit)
+    if spec.gate == "standard":
+        g = G_MIN * torch.sigmoid(g_logit)
+    elif spec.gate == "long":
+        g = G_MIN * torch.sigmoid(g_logit - 7.0)
+        g[..., dk // 2:] = 0.0
+    elif spec.gate == "const":
+        g = torch.full_like(g_logit, spec.g_const)
+    else:
+        raise ValueError(spec.gate)
+    S0 = None
+    if spec.s0_std > 0:
+        S0 = spec.s0_std * _randn((B, H, dk, dv), gen, device)
+    if spec.bound_frac > 0:
+        mask = torch.rand((B, T, H), generator=gen, device=device) < spec.bound_frac
+        g = torch.where(mask[..., None], torch.full_like(g, spec.bound_value), g)
+    return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(), v=v.to(dt).contiguous(),
+                g=g.to(dt).contiguous(), beta=beta.to(dt).contiguous(),
+                S0=None if S0 is None else S0.contiguous())
+
+
+def decode_state(spec: DecodeSpec, device="cpu", N=None):
+    """Initial decode state: conv_w fp32 [H, 2dk+dv, width] ~ 0.5 N(0,1);
+    conv_cache [N, H, width-1, 2dk+dv] ~ N(0,1) in spec.dtype; S fp32 [N,H,dk,dv] ~ 0.02 N(0,1)."""
+    N = spec.N if N is None else N
+    H, dk, dv, W = spec.H, spec.dk, spec.dv, spec.width
+    nch = 2 * dk + dv
+    gen = _gen(device, spec.state_seed)
+    conv_w = 0.5 * _randn((H, nch, W), gen, device)
+    cache = _randn((N, H, W - 1, nch), gen, device).to(torch_dtype(spec.dtype))
+    S = 0.02 * _randn((N, H, dk, dv), gen, device)
+    return dict(conv_w=conv_w.contiguous(), conv_cache=cache.contiguous(), S=S.contiguous())
+
+
+def decode_step_inputs(spec: DecodeSpec, step: int, device="cpu", N=None):
+    """Per-step decode inputs: q_pre, k_pre [N,H,dk]; v_pre [N,H,dv] ~ N(0,1);
+    beta = sigmoid(N(0,1)) [N,H]; g = -5 sigmoid(N(0,1)) [N,H,dk] (or near 0 for gate="long")."""
+    N = spec.N if N is None else N
+    H, dk, dv = spec.H, spec.dk, spec.dv
+    dt = torch_dtype(spec.dtype)
+    gen = _gen(device, spec.seed_base + step)
+    q = _randn((N, H, dk), gen, device)
+    k = _randn((N, H, dk), gen, device)
+    v = _randn((N, H, dv), gen, device)
+    beta = torch.sigmoid(_randn((N, H), gen, device))
+    g_logit = _randn((N, H, dk), gen, device)
+    if spec.gate == "standard":
+        g = G_MIN * torch.sigmoid(g_logit)
+    elif spec.gate == "long":
+        g = G_MIN * torch.sigmoid(g_logit - 7.0)
+    else:
+        raise ValueError(spec.gate)
+    return dict(q_pre=q.to(dt).contiguous(), k_pre=k.to(dt).contiguous(), v_pre=v.to(dt).contiguous(),
+                g=g.to(dt).contiguous(), beta=beta.to(dt).contiguous())
+
+
+def to_f64(t):
+    """Exact upcast of a (possibly bf16) torch tensor to a float64 numpy array."""
+    import numpy as np
+    if t is None:
+        return None
+    return t.detach().to("cpu", torch.float64).numpy().astype(np.float64, copy=False)

@@ -1,0 +1,101 @@
+"""fp64 CPU oracle of the Kimi Delta Attention recurrence -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the GPU path (``gated_delta_rule_18_amd``)
+and imports nothing from it.
+
+The arithmetic lives in ``kda_oracle.c`` (plain sequential loops in double
+precision; see its header for the cited passages).  This module only converts
+numpy arrays to contiguous float64 and calls the C entry points through ctypes.
+
+Functions
+---------
+prefill(q, k, v, g, beta, S0=None, nthreads=None) -> (o, S_T)
+    q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; S0 [B,H,dk,dv] or None.
+decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
+            eps=1e-6, nthreads=None) -> o
+    conv_cache and S are updated in place (they must be float64 C-contiguous
+    arrays owned by the caller).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+L2NORM_EPS = 1e-6
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_prefill.argtypes = [_dp] * 8 + [ctypes.c_long] * 5 + [ctypes.c_int]
+        lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.kda_oracle_decode_step.argtypes = (
+            [_dp] * 5 + [ctypes.c_long] + [_dp] * 4 + [ctypes.c_long] * 5 + [ctypes.c_double, ctypes.c_int])
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def default_threads():
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def prefill(q, k, v, g, beta, S0=None, nthreads=None):
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("oracle.prefill: inconsistent shapes")
+    S0a = None if S0 is None else _f64(S0)
+    if S0a is not None and S0a.shape != (B, H, dk, dv):
+        raise ValueError("oracle.prefill: S0 shape")
+    o = np.empty((B, T, H, dv))
+    S_T = np.empty((B, H, dk, dv))
+    rc = _load().kda_oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0a),
+                                    _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill failed ({rc})")
+    return o, S_T
+
+
+def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
+                eps=L2NORM_EPS, nthreads=None):
+    q_pre, k_pre, v_pre, conv_w, g, beta = (_f64(x) for x in (q_pre, k_pre, v_pre, conv_w, g, beta))
+    for name, a in (("conv_cache", conv_cache), ("S", S)):
+        if not (isinstance(a, np.ndarray) and a.dtype == np.float64 and a.flags.c_contiguous):
+            raise TypeError(f"oracle.decode_step: {name} must be a C-contiguous float64 array (updated in place)")
+    N, H, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    width = conv_w.shape[-1]
+    nch = 2 * dk + dv
+    if (k_pre.shape != (N, H, dk) or v_pre.shape != (N, H, dv) or conv_w.shape != (H, nch, width)
+            or conv_cache.shape != (N, H, width - 1, nch) or g.shape != (N, H, dk)
+            or beta.shape != (N, H) or S.shape != (N, H, dk, dv)):
+        raise ValueError("oracle.decode_step: inconsistent shapes")
+    o = np.empty((N, H, dv))
+    rc = _load().kda_oracle_decode_step(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w),
+                                        _ptr(conv_cache), int(conv_pos), _ptr(g), _ptr(beta),
+                                        _ptr(S), _ptr(o), N, H, dk, dv, width, float(eps),
+                                        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_decode_step failed ({rc})")
+    return o

@@ -1,0 +1,53 @@
+"""fp64 numpy model of the chunkwise (UT/WY) form of the KDA recurrence.
+
+A second, independent derivation used only to pin the oracle and to lock the
+algebra the GPU prefill kernel follows.  The pages state the chunk interface
+(X_[c], S_in) -> (Y_[c], S_out) with S_in of chunk c+1 equal to S_out of chunk
+c, name the WY/UT organisation and the 16-position secondary tile, but print no
+derivation (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section
+3.3).  The derivation used here: inside a chunk with incoming state S and
+chunk-relative cumulative log-decay G_r = sum_{s<=r} g_s,
+    A[r,i] = beta_r sum_c k[r,c] k[i,c] exp(G[r,c] - G[i,c])      (i < r)
+    M[r,i] =        sum_c q[r,c] k[i,c] exp(G[r,c] - G[i,c])      (i <= r)
+    U      = (I + A)^{-1} Diag(beta) (V - (k*exp(G)) S)
+    O      = (q*exp(G)) S + M U
+    S_out  = Diag(exp(G_C)) S + (k*exp(G_C - G))^T U
+`ref` selects where each exp(G_r - G_i) is split into a row and a column factor:
+    "direct"  -- the product is formed from the difference (no split),
+    "center"  -- split at the middle of the chunk, as the GPU kernel does (each
+                 factor then spans at most C/2 positions of decay).
+"""
+import numpy as np
+
+
+def chunk_forward(q, k, v, g, beta, S0, C, ref="direct"):
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for c0 in range(0, T, C):
+        sl = slice(c0, min(T, c0 + C))
+        qc, kc, vc, gc, bc = q[sl], k[sl], v[sl], g[sl], beta[sl]
+        n = qc.shape[0]
+        G = np.cumsum(gc, axis=0)
+        if ref == "direct":
+            D = G[:, None, :] - G[None, :, :]                    # [r, i, c]
+            E = np.exp(np.where(np.arange(n)[:, None, None] >= np.arange(n)[None, :, None], D, -np.inf))
+            KK = np.einsum("rc,ic,ric->ri", kc, kc, E)
+            QK = np.einsum("rc,ic,ric->ri", qc, kc, E)
+        elif ref == "center":
+            h = min(C // 2, n)
+            R = G[h - 1]
+            rowf = np.exp(G - R)
+            colf = np.exp(R - G)
+            KK = (kc * rowf) @ (kc * colf).T
+            QK = (qc * rowf) @ (kc * colf).T
+        else:
+            raise ValueError(ref)
+        A = np.tril(bc[:, None] * KK, -1)
+        M = np.tril(QK)
+        Tm = np.linalg.solve(np.eye(n) + A, np.diag(bc))
+        U = Tm @ (vc - (kc * np.exp(G)) @ S)
+        o[sl] = (qc * np.exp(G)) @ S + M @ U
+        S = np.exp(G[-1])[:, None] * S + (kc * np.exp(G[-1] - G)).T @ U
+    return o, S

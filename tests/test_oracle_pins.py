@@ -1,0 +1,285 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Every check here is independent of the oracle's own loop: hand-derived exact
+values, closed forms of special cases, explicit matrix products, invariants,
+a second (chunkwise) derivation, and library routines for the preprocessing.
+Page cited throughout: "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读"
+(sections 3.1-3.3) and "Kimi K3 架构篇：一文详解 2.8 万亿参数的巨型怪兽".
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.chunk_model import chunk_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-12
+
+
+def _rand_inputs(rng, B, T, H, dk, dv, unit=True, gscale=1.0):
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    if unit:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    g = -5.0 * gscale / (1 + np.exp(-rng.standard_normal((B, T, H, dk))))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((B, T, H))))
+    S0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    return q, k, v, g, beta, S0
+
+
+def _close(a, b, tol=RTOL):
+    scale = max(1.0, float(np.abs(b).max()))
+    assert np.abs(a - b).max() <= tol * scale, float(np.abs(a - b).max())
+
+
+def test_scalar_worked_example():
+    """d_k = d_v = 1 worked by hand with exact fractions (section 3.2 edit order)."""
+    with open(os.path.join(GOLDEN, "scalar_recurrence.json")) as f:
+        gd = json.load(f)
+    T = len(gd["q"])
+    shp = (1, T, 1, 1)
+    o, S = oracle.prefill(np.array(gd["q"]).reshape(shp), np.array(gd["k"]).reshape(shp),
+                          np.array(gd["v"]).reshape(shp), np.log(np.array(gd["alpha"])).reshape(shp),
+                          np.array(gd["beta"]).reshape(1, T, 1), np.full((1, 1, 1, 1), gd["S0"]))
+    np.testing.assert_allclose(o.ravel(), gd["o"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(S.ravel(), [gd["S_T"]], rtol=0, atol=1e-15)
+
+
+def test_bound_facts():
+    """g_min = -5: alpha > e^-5 ~ 0.0067; a 16-position tile sums to >= -80; e^80 fits bf16."""
+    with open(os.path.join(GOLDEN, "bound_facts.json")) as f:
+        gd = json.load(f)
+    assert round(math.exp(gd["g_min"]), gd["alpha_min_decimals"]) == gd["alpha_min_approx"]
+    assert gd["tile_positions"] * gd["g_min"] == gd["tile_cumulative_log_decay_min"]
+    assert math.exp(-gd["tile_cumulative_log_decay_min"]) < torch.finfo(torch.bfloat16).max
+    # the workload's bound-stress value rounds onto the bound itself in bf16
+    assert torch.tensor(-4.99).to(torch.bfloat16).item() == gd["g_min"]
+
+
+def test_decay_only_closed_form():
+    """beta = 0: S_t = Diag(exp(sum_{s<=t} g_s)) S0 and o_t = S_t^T q_t -- decay scales rows only."""
+    rng = np.random.default_rng(1)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 40, 3, 8, 5)
+    beta[:] = 0.0
+    o, S = oracle.prefill(q, k, v, g, beta, S0)
+    G = np.cumsum(g, axis=1)                                   # [B,T,H,dk]
+    St = np.exp(G)[..., None] * S0[:, None]                    # [B,T,H,dk,dv]
+    _close(o, np.einsum("bthij,bthi->bthj", St, q))
+    _close(S, St[:, -1])
+
+
+def test_linear_attention_reduction():
+    """alpha = 1, S0 = 0, orthonormal keys: S_t = sum_{i<=t} beta_i k_i v_i^T;
+    with beta = 1 this is the plain linear-attention prefix sum of section 3.1 eq. 1."""
+    rng = np.random.default_rng(2)
+    T, dk, dv = 12, 16, 7
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T].reshape(1, T, 1, dk)
+    q = rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv))
+    g = np.zeros((1, T, 1, dk))
+    for beta in (rng.random((1, T, 1)), np.ones((1, T, 1))):
+        o, S = oracle.prefill(q, k, v, g, beta, None)
+        outer = beta[0, :, 0, None, None] * k[0, :, 0, :, None] * v[0, :, 0, None, :]
+        St = np.cumsum(outer, axis=0)
+        _close(o[0, :, 0], np.einsum("tij,ti->tj", St, q[0, :, 0]))
+        _close(S[0, 0], St[-1])
+
+
+def test_delta_recall():
+    """beta = 1 and unit k: S_t^T k_t = v_t exactly, for any alpha (read with q = k).
+    General beta and non-unit k: S_t^T k_t = vhat_t + beta_t |k_t|^2 (v_t - vhat_t)."""
+    rng = np.random.default_rng(3)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 30, 2, 8, 6)
+    beta1 = np.ones_like(beta)
+    o, _ = oracle.prefill(k, k, v, g, beta1, S0)
+    _close(o, v, 1e-12)
+    k2 = 1.7 * k
+    o2, _ = oracle.prefill(k2, k2, v, g, beta, S0)
+    for t in (0, 5, 29):
+        if t == 0:
+            Sprev = S0
+        else:
+            _, Sprev = oracle.prefill(q[:, :t], k2[:, :t], v[:, :t], g[:, :t], beta[:, :t], S0)
+        for h in range(2):
+            vhat = (np.exp(g[0, t, h])[:, None] * Sprev[0, h]).T @ k2[0, t, h]
+            nk2 = k2[0, t, h] @ k2[0, t, h]
+            expect = vhat + beta[0, t, h] * nk2 * (v[0, t, h] - vhat)
+            _close(o2[0, t, h], expect)
+
+
+def test_unrolled_product_bruteforce():
+    """T <= 8: S_T = (prod A_t) S0 + sum_i (prod_{t>i} A_t) beta_i k_i v_i^T with
+    A_t = (I - beta_t k_t k_t^T) Diag(alpha_t) formed explicitly (section 3.1 eq. 3)."""
+    rng = np.random.default_rng(4)
+    for T in (1, 2, 5, 8):
+        q, k, v, g, beta, S0 = _rand_inputs(rng, 1, T, 1, 6, 4, unit=False)
+        o, S = oracle.prefill(q, k, v, g, beta, S0)
+        dk = 6
+        Ss = S0[0, 0].copy()
+        for t in range(T):
+            kt = k[0, t, 0]
+            At = (np.eye(dk) - beta[0, t, 0] * np.outer(kt, kt)) @ np.diag(np.exp(g[0, t, 0]))
+            Ss = At @ Ss + beta[0, t, 0] * np.outer(kt, v[0, t, 0])
+            _close(o[0, t, 0], Ss.T @ q[0, t, 0])
+        # closed product form of the final state
+        P = np.eye(dk)
+        acc = np.zeros_like(S0[0, 0])
+        for t in reversed(range(T)):
+            kt = k[0, t, 0]
+            acc += P @ (beta[0, t, 0] * np.outer(kt, v[0, t, 0]))
+            P = P @ ((np.eye(dk) - beta[0, t, 0] * np.outer(kt, kt)) @ np.diag(np.exp(g[0, t, 0])))
+        _close(S[0, 0], P @ S0[0, 0] + acc)
+        _close(Ss, S[0, 0])
+
+
+def test_linearity_and_value_permutation():
+    """(V, S0) -> (O, S_T) is linear; permuting value channels permutes o and S columns."""
+    rng = np.random.default_rng(5)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 25, 2, 8, 6)
+    v2 = rng.standard_normal(v.shape)
+    S02 = rng.standard_normal(S0.shape)
+    o1, s1 = oracle.prefill(q, k, v, g, beta, S0)
+    o2, s2 = oracle.prefill(q, k, v2, g, beta, S02)
+    o3, s3 = oracle.prefill(q, k, v - 2.5 * v2, g, beta, S0 - 2.5 * S02)
+    _close(o3, o1 - 2.5 * o2, 1e-11)
+    _close(s3, s1 - 2.5 * s2, 1e-11)
+    perm = rng.permutation(6)
+    o4, s4 = oracle.prefill(q, k, v[..., perm], g, beta, S0[..., perm])
+    _close(o4, o1[..., perm])
+    _close(s4, s1[..., perm])
+
+
+def test_state_passing():
+    """One call over T equals two calls over T1 and T-T1 with S0 = S_T of the first (section 3.3)."""
+    rng = np.random.default_rng(6)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 37, 3, 8, 5)
+    o, S = oracle.prefill(q, k, v, g, beta, S0)
+    for T1 in (1, 16, 36):
+        oa, Sa = oracle.prefill(q[:, :T1], k[:, :T1], v[:, :T1], g[:, :T1], beta[:, :T1], S0)
+        ob, Sb = oracle.prefill(q[:, T1:], k[:, T1:], v[:, T1:], g[:, T1:], beta[:, T1:], Sa)
+        _close(np.concatenate([oa, ob], axis=1), o)
+        _close(Sb, S)
+
+
+def test_zero_length_and_threads():
+    """T = 0 returns S_T = S0; thread count does not change the result."""
+    rng = np.random.default_rng(7)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 0, 3, 4, 4)
+    o, S = oracle.prefill(q, k, v, g, beta, S0)
+    assert o.shape == (2, 0, 3, 4)
+    np.testing.assert_array_equal(S, S0)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 9, 3, 4, 4)
+    a = oracle.prefill(q, k, v, g, beta, S0, nthreads=1)
+    b = oracle.prefill(q, k, v, g, beta, S0, nthreads=5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("C", [5, 8, 16, 32, 64])
+@pytest.mark.parametrize("ref", ["direct", "center"])
+def test_chunk_form_matches_oracle(C, ref):
+    """The chunkwise WY/UT form (a separate derivation) reproduces the sequential oracle."""
+    if ref == "center" and C > 32:
+        pytest.skip("centre split of a 64-chunk spans 32 positions: e^160 overflows")
+    rng = np.random.default_rng(8 + C)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 150, 2, 16, 8)
+    o, S = oracle.prefill(q, k, v, g, beta, S0)
+    for h in range(2):
+        oc, Sc = chunk_forward(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h], beta[0, :, h], S0[0, h], C, ref)
+        _close(oc, o[0, :, h], 1e-10)
+        _close(Sc, S[0, h], 1e-10)
+
+
+def test_chunk_form_at_the_bound():
+    """g = -5 everywhere (the bound): the centre-split 32-chunk stays finite and exact in fp64."""
+    rng = np.random.default_rng(9)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 96, 1, 16, 8)
+    g[:] = -5.0
+    o, S = oracle.prefill(q, k, v, g, beta, S0)
+    oc, Sc = chunk_forward(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0], S0[0, 0], 32, "center")
+    assert np.isfinite(oc).all()
+    _close(oc, o[0, :, 0], 1e-10)
+    _close(Sc, S[0, 0], 1e-10)
+
+
+# ------------------------------------------------------------------- decode --
+
+def _decode_expected(qp, kp, vp, w, cache0, g, beta, S0, eps):
+    """Preprocessing from library routines: np.convolve for the causal conv,
+    torch's silu for Swish, np.linalg.norm for L2Norm; then the (pinned) prefill oracle."""
+    Tn, N, H, dk = qp.shape
+    dv = vp.shape[-1]
+    W = w.shape[-1]
+    x = np.concatenate([qp, kp, vp], axis=-1)                 # [T, N, H, nch]
+    hist = np.concatenate([np.transpose(cache0, (2, 0, 1, 3)), x], axis=0)  # [W-1+T, N, H, nch]
+    u = np.zeros_like(x)
+    for n in range(N):
+        for h in range(H):
+            for c in range(x.shape[-1]):
+                full = np.convolve(hist[:, n, h, c], w[h, c, ::-1], mode="valid")
+                u[:, n, h, c] = full[:Tn]
+    s = torch.nn.functional.silu(torch.from_numpy(u)).numpy()
+    q = s[..., :dk] / np.sqrt(np.linalg.norm(s[..., :dk], axis=-1, keepdims=True) ** 2 + eps)
+    k = s[..., dk:2 * dk] / np.sqrt(np.linalg.norm(s[..., dk:2 * dk], axis=-1, keepdims=True) ** 2 + eps)
+    vv = s[..., 2 * dk:]
+    # prefill oracle over T steps with (B, T, H) = (N, Tn, H)
+    tr = lambda a: np.ascontiguousarray(np.transpose(a, (1, 0, 2, 3)))
+    o, S = oracle.prefill(tr(q), tr(k), tr(vv), np.ascontiguousarray(np.transpose(g, (1, 0, 2, 3))),
+                          np.ascontiguousarray(np.transpose(beta, (1, 0, 2))), S0)
+    return np.transpose(o, (1, 0, 2, 3)), S
+
+
+@pytest.mark.parametrize("W", [4, 2])
+def test_decode_matches_preprocessing_and_prefill(W):
+    rng = np.random.default_rng(11)
+    Tn, N, H, dk, dv = 7, 2, 3, 8, 6
+    nch = 2 * dk + dv
+    qp = rng.standard_normal((Tn, N, H, dk))
+    kp = rng.standard_normal((Tn, N, H, dk))
+    vp = rng.standard_normal((Tn, N, H, dv))
+    w = 0.5 * rng.standard_normal((H, nch, W))
+    cache0 = rng.standard_normal((N, H, W - 1, nch))
+    g = -5 / (1 + np.exp(-rng.standard_normal((Tn, N, H, dk))))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((Tn, N, H))))
+    S0 = 0.1 * rng.standard_normal((N, H, dk, dv))
+    eo, eS = _decode_expected(qp, kp, vp, w, cache0, g, beta, S0, oracle.L2NORM_EPS)
+    cache = cache0.copy()
+    S = S0.copy()
+    pos = 5   # any start offset of the ring: rotate the initial cache to match
+    cache = np.roll(cache0, shift=pos % (W - 1), axis=2).copy()
+    for t in range(Tn):
+        o = oracle.decode_step(qp[t], kp[t], vp[t], w, cache, pos + t, g[t], beta[t], S)
+        _close(o, eo[t], 1e-11)
+    _close(S, eS, 1e-11)
+
+
+def test_decode_identity_conv_and_unit_norm():
+    """Conv taps (0,...,0,1) pass x_t through; with beta = 1, g = 0, S = 0 the new state is
+    k v^T with |k| = 1 (L2Norm) and v = silu(v_pre)."""
+    rng = np.random.default_rng(12)
+    N, H, dk, dv, W = 3, 2, 8, 5, 4
+    nch = 2 * dk + dv
+    w = np.zeros((H, nch, W))
+    w[..., -1] = 1.0
+    cache = rng.standard_normal((N, H, W - 1, nch))
+    qp, kp = rng.standard_normal((N, H, dk)), rng.standard_normal((N, H, dk))
+    vp = rng.standard_normal((N, H, dv))
+    S = np.zeros((N, H, dk, dv))
+    o = oracle.decode_step(qp, kp, vp, w, cache, 0, np.zeros((N, H, dk)), np.ones((N, H)), S)
+    vs = torch.nn.functional.silu(torch.from_numpy(vp)).numpy()
+    ks = torch.nn.functional.silu(torch.from_numpy(kp)).numpy()
+    kn = ks / np.sqrt((ks ** 2).sum(-1, keepdims=True) + oracle.L2NORM_EPS)
+    _close(S, kn[..., :, None] * vs[..., None, :], 1e-13)
+    # the oldest slot now holds x_t
+    np.testing.assert_array_equal(cache[:, :, 0, :dk], qp)
+    np.testing.assert_array_equal(cache[:, :, 0, 2 * dk:], vp)
+    assert np.allclose(np.linalg.norm(kn, axis=-1), 1.0, atol=1e-6)
+    assert o.shape == (N, H, dv)
