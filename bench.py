@@ -1,0 +1,204 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Two timed phases, each W untimed steps then K timed steps bracketed by
+torch.cuda.synchronize():
+  prefill  one kda_chunk_fwd over the K3-shaped layer: B=1, H=96, T=65536,
+           dk=dv=128, bf16 inputs, fp32 state, chunk 32, 10 % of tokens at
+           g = -4.99 (the headline: `value` is its tokens/s);
+  decode   one kda_decode_step over N=256 sequences x H=96 heads, dk=dv=128,
+           bf16, ShortConv width 4 (reported under "decode").
+Inputs are synthetic, seeded, and resident in HBM before the timed region.
+Kernel durations come from HIP events recorded on the stream the kernels are
+launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
+prefill workload on the host cores.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def prefill_bytes(B, T, H, dk, dv):
+    """Algorithmic HBM bytes of one kda_chunk_fwd call (bf16 activations, fp32 state):
+    per token-head 2(2dk+dv) [q,k,v] + 2dk [g] + 2 [beta] + 2dv [o]; per head 8 dk dv [S0 in, S_T out]."""
+    per_token_head = 2 * (2 * dk + dv) + 2 * dk + 2 + 2 * dv
+    return B * T * H * per_token_head + B * H * 8 * dk * dv
+
+
+def prefill_flops(B, T, H, dk, dv, C):
+    """Chunk-form flops at chunk C: per token-head C(6dk + 4dv) + 6 dk dv + C^2/3."""
+    return B * T * H * (C * (6 * dk + 4 * dv) + 6 * dk * dv + C * C / 3.0)
+
+
+def decode_bytes(N, H, dk, dv, W=4):
+    """Algorithmic HBM bytes of one kda_decode_step: per (sequence, head) the fp32 state
+    read + write 8 dk dv, x_t 2(2dk+dv), cache read 2(W-1)(2dk+dv), cache append 2(2dk+dv),
+    g 2dk, beta 2, o 2dv."""
+    nch = 2 * dk + dv
+    return N * H * (8 * dk * dv + 2 * nch + 2 * (W - 1) * nch + 2 * nch + 2 * dk + 2 + 2 * dv)
+
+
+def _timed(fn, steps, warmup, torch):
+    """W warmups, then K steps between synchronisations.  Returns (wall ms/step,
+    mean kernel ms from events on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall, kern
+
+
+def cpu_baseline(x, H_total, heads=32, tokens=65536):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the prefill workload:
+    the first `heads` heads of the generated K3-shaped inputs over `tokens` tokens."""
+    import oracle
+    from gated_delta_rule_18_amd.inputs import to_f64
+    tokens = min(tokens, x["q"].shape[1])
+    heads = min(heads, x["q"].shape[2])
+    sl = lambda t: to_f64(t[:, :tokens, :heads].contiguous())
+    args = [sl(x[n]) for n in ("q", "k", "v", "g", "beta")] + [to_f64(x["S0"][:, :heads].contiguous())]
+    nthreads = oracle.default_threads()
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    nthreads = max(1, min(nthreads, avail))
+    t0 = time.perf_counter()
+    oracle.prefill(*args, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    token_heads = heads * tokens
+    return {
+        "value": token_heads / dt / H_total,
+        "unit": "tokens/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on {nthreads} threads: prefill of {heads} of {H_total} heads x {tokens} "
+                   f"tokens (d=128) of the same K3-shaped inputs, {dt:.2f} s; value = token-heads/s / "
+                   f"{H_total}, i.e. layer tokens/s"),
+        "seconds": dt,
+        "gflops_fp64": token_heads * 7 * 128 * 128 / dt / 1e9,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--skip-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_18_amd import binding
+    from gated_delta_rule_18_amd.inputs import DECODE, WORKLOADS, decode_state, decode_step_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    binding.lib()
+
+    # ---------------- prefill --------------------------------------------------
+    spec = WORKLOADS["k3_prefill"]
+    B, T, H, dk, dv, C = spec.B, spec.T, spec.H, spec.dk, spec.dv, args.chunk
+    x = prefill_inputs(spec, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill_step(i=0):
+        binding.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], chunk=C, o=o, S_T=S_T)
+
+    p_wall, p_kern = _timed(prefill_step, args.steps, args.warmup, torch)
+    p_bytes = prefill_bytes(B, T, H, dk, dv)
+    p_flops = prefill_flops(B, T, H, dk, dv, C)
+    p_gbps = p_bytes / (p_kern * 1e-3) / 1e9
+    p_tflops = p_flops / (p_kern * 1e-3) / 1e12
+    cpu = None if args.no_cpu else cpu_baseline(x, H)
+    del x, o
+
+    # ---------------- decode ---------------------------------------------------
+    decode = None
+    if not args.skip_decode:
+        ds = DECODE
+        st = decode_state(ds, device=dev)
+        nin = args.steps + args.warmup
+        steps_in = [decode_step_inputs(ds, s % ds.steps, device=dev) for s in range(min(nin, ds.steps))]
+        od = torch.empty((ds.N, ds.H, ds.dv), dtype=torch.bfloat16, device=dev)
+        pos = [0]
+        torch.cuda.synchronize()
+
+        def decode_step(i=0):
+            d = steps_in[pos[0] % len(steps_in)]
+            binding.decode_step(d["q_pre"], d["k_pre"], d["v_pre"], st["conv_w"], st["conv_cache"], pos[0],
+                                d["g"], d["beta"], st["S"], o=od)
+            pos[0] += 1
+
+        d_wall, d_kern = _timed(decode_step, args.steps, args.warmup, torch)
+        d_bytes = decode_bytes(ds.N, ds.H, ds.dk, ds.dv, ds.width)
+        d_gbps = d_bytes / (d_kern * 1e-3) / 1e9
+        decode = {
+            "workload": f"decode N{ds.N} H{ds.H} dk=dv={ds.dk} bf16 ShortConv{ds.width}",
+            "ms_per_step": d_wall,
+            "kernel_ms": d_kern,
+            "tokens_per_s": ds.N / (d_wall * 1e-3),
+            "gbps": d_gbps,
+            "roofline": {"bound": "hbm", "achieved": d_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": d_gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "bytes_per_launch": d_bytes},
+        }
+        del st, steps_in
+
+    line = {
+        "metric": "KDA prefill tokens/s & TFLOP/s (% MFMA peak); decode-step HBM GB/s (% peak)",
+        "value": B * T / (p_wall * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p_wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"k3_prefill B{B} H{H} T{T} dk=dv={dk} bf16 chunk{C} "
+                               "(10% tokens g=-4.99)", "global_batch": B, "seq_len": T, "heads": H,
+                   "chunk": C},
+        "kernel_ms": p_kern,
+        "tflops": p_tflops,
+        "mfma_frac": p_tflops / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": p_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": p_gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": p_bytes},
+        "decode": decode,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

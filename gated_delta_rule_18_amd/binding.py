@@ -1,0 +1,144 @@
+"""Python binding of libkda.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; torch is used
+for device memory and for the current HIP stream.  If the library is missing
+the calls raise (there is no fallback).
+
+    o, S_T = chunk_fwd(q, k, v, g, beta, S0=None, chunk=32)
+    o      = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
+
+Shapes and dtypes follow include/kda.h: bf16 activations with an fp32 state,
+or fp32 everywhere (test mode).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16, KDA_FP32 = 0, 1
+KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
+EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_strerror", "kda_version")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (kda status {code})")
+        self.code = code
+
+
+def lib():
+    """Load libkda.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is missing: build it with "
+                              "`python -m gated_delta_rule_18_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        L.kda_chunk_fwd.restype = i
+        L.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp]
+        L.kda_decode_step.restype = i
+        L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
+        L.kda_strerror.restype = ctypes.c_char_p
+        L.kda_strerror.argtypes = [i]
+        L.kda_version.restype = i
+        L.kda_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().kda_version()
+
+
+def _check(rc):
+    if rc != KDA_OK:
+        raise KdaError(rc, lib().kda_strerror(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32")
+
+
+def _want(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device or device.type != "cuda":
+        raise ValueError(f"{name}: device {t.device}, expected the GPU tensor device {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, g, beta, S0=None, chunk=32, o=None, S_T=None, return_state=True):
+    """Chunkwise prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
+    S0 [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv] fp32 or None).
+    S_T may be passed as S0 itself for in-place streaming over segments."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H))):
+        _want(t, name, shp, dt, dev)
+    if S0 is not None:
+        _want(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _want(o, "o", (B, T, H, dv), dt, dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _want(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    rc = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                             _ptr(S_T), B, T, H, dk, dv, code, int(chunk), _stream(dev))
+    _check(rc)
+    return o, S_T
+
+
+def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o=None):
+    """One decode step.  q_pre, k_pre [N,H,dk]; v_pre [N,H,dv]; conv_w fp32 [H,2dk+dv,W];
+    conv_cache [N,H,W-1,2dk+dv] (updated); g [N,H,dk]; beta [N,H]; S fp32 [N,H,dk,dv]
+    (updated in place).  Returns o [N,H,dv]."""
+    N, H, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    W = conv_w.shape[-1]
+    nch = 2 * dk + dv
+    dev, dt = q_pre.device, q_pre.dtype
+    code = _dtype_code(q_pre)
+    for name, t, shp in (("q_pre", q_pre, (N, H, dk)), ("k_pre", k_pre, (N, H, dk)),
+                         ("v_pre", v_pre, (N, H, dv)), ("g", g, (N, H, dk)), ("beta", beta, (N, H)),
+                         ("conv_cache", conv_cache, (N, H, W - 1, nch))):
+        _want(t, name, shp, dt, dev)
+    _want(conv_w, "conv_w", (H, nch, W), torch.float32, dev)
+    _want(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _want(o, "o", (N, H, dv), dt, dev)
+    rc = lib().kda_decode_step(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(conv_cache),
+                               int(conv_pos), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
+                               W, code, _stream(dev))
+    _check(rc)
+    return o

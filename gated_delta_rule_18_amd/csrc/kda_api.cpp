@@ -1,0 +1,100 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument validation,
+// error mapping and dispatch to the HIP launchers.  No allocation, no global
+// state, no host synchronisation.
+#include "kda.h"
+
+#include <cstdint>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
+bool head_ok(int d) { return d == 64 || d == 128; }
+
+} // namespace
+
+extern "C" {
+
+int kda_version(void) { return KDA_VERSION; }
+
+const char *kda_strerror(int status)
+{
+    switch (status) {
+    case KDA_OK:
+        return "success";
+    case KDA_ERR_INVALID:
+        return "invalid argument (null pointer, bad size, dtype, chunk, width or misaligned buffer)";
+    case KDA_ERR_UNSUPPORTED:
+        return "unsupported head size (dk and dv must be 64 or 128)";
+    case KDA_ERR_LAUNCH:
+        return "HIP kernel launch failed";
+    default:
+        return "unknown kda status";
+    }
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                  const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv,
+                  int dtype, int chunk, void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (chunk != 16 && chunk != 32)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk) || !head_ok(dv))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40))
+        return KDA_ERR_INVALID;
+    const bool has_tokens = (long long)B * T * H > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !o))
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, g, o, S0, S_T};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDA_ERR_INVALID;
+    // S_T may be S0 itself; a partial overlap would let one head's write race
+    // with another head's read.
+    if (S0 && S_T && S0 != S_T) {
+        const char *a = reinterpret_cast<const char *>(S0), *b = reinterpret_cast<const char *>(S_T);
+        const long long bytes = (long long)B * H * dk * dv * 4;
+        if (a < b + bytes && b < a + bytes)
+            return KDA_ERR_INVALID;
+    }
+    hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
+                                         dtype == KDA_FP32, chunk,
+                                         reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                    void *conv_cache, int conv_pos, const void *g, const void *beta, float *S,
+                    void *o, int N, int H, int dk, int dv, int width, int dtype, void *stream)
+{
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || conv_pos < 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (width != 4)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk) || !head_ok(dv))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)N * H == 0)
+        return KDA_OK;
+    if (!q_pre || !k_pre || !v_pre || !conv_w || !conv_cache || !g || !beta || !S || !o)
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q_pre, k_pre, v_pre, conv_w, conv_cache, g, S, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return KDA_ERR_INVALID;
+    if ((long long)N * H > 0x7fffffffLL)
+        return KDA_ERR_INVALID;
+    hipError_t e = kda::launch_decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache,
+                                           conv_pos % (width - 1), g, beta, S, o, N, H, dk, dv,
+                                           dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+} // extern "C"

@@ -1,0 +1,271 @@
+// kda_decode.hip -- one KDA decode step on gfx950.
+//
+// Method: page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 3.2:
+// the decode interface (x_t, S_{t-1}, C^conv_{t-1}) -> (y_t, S_t, C^conv_t); the
+// input branches q, k = L2Norm(Swish(ShortConv(.))), v = Swish(ShortConv(.));
+// and the one-token edit Sbar = Diag(alpha) S, vhat = Sbar^T k,
+// S' = Sbar + beta k (v - vhat)^T, o = S'^T q (read after the write).
+//
+// The step is bound by HBM traffic: the 4*dk*dv-byte fp32 state of every
+// (sequence, head) is read once and written once.  One workgroup of 256
+// threads owns one (sequence, head):
+//   * each thread holds a float4 column strip of ROWS key rows of S in
+//     registers from the read to the write, so HBM sees exactly one read and
+//     one write of the state (loads are issued first, before the conv work);
+//   * 64 consecutive lanes read rows 512 or 256 contiguous bytes wide;
+//   * the readout does not re-read S': with d = v - vhat,
+//       o = S'^T q = Sbar^T q + beta (q . k) d,
+//     so both column sums (Sbar^T k and Sbar^T q) come out of one pass.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWidth = 4;
+constexpr float kL2Eps = 1e-6f;
+
+__device__ __forceinline__ void load2(const __bf16 *p, float &a, float &b)
+{
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    v2 x = *reinterpret_cast<const v2 *>(p);
+    a = (float)x[0];
+    b = (float)x[1];
+}
+__device__ __forceinline__ void load2(const float *p, float &a, float &b)
+{
+    float2 x = *reinterpret_cast<const float2 *>(p);
+    a = x.x;
+    b = x.y;
+}
+__device__ __forceinline__ void store2(__bf16 *p, float a, float b)
+{
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    v2 x;
+    x[0] = (__bf16)a;
+    x[1] = (__bf16)b;
+    *reinterpret_cast<v2 *>(p) = x;
+}
+__device__ __forceinline__ void store2(float *p, float a, float b)
+{
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d)
+{
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+    v4 x;
+    x[0] = (__bf16)a;
+    x[1] = (__bf16)b;
+    x[2] = (__bf16)c;
+    x[3] = (__bf16)d;
+    *reinterpret_cast<v4 *>(p) = x;
+}
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d)
+{
+    *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+
+__device__ __forceinline__ float swish(float u) { return u / (1.0f + exp_f(-u)); }
+
+template <int DK, int DV, typename E>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const E *__restrict__ q_pre, const E *__restrict__ k_pre, const E *__restrict__ v_pre,
+    const float *__restrict__ conv_w, E *__restrict__ conv_cache, int oldest,
+    const E *__restrict__ g, const E *__restrict__ beta, float *__restrict__ S,
+    E *__restrict__ o, int H)
+{
+    constexpr int NCH = 2 * DK + DV;      // conv channels q | k | v
+    constexpr int CG = DV / 4;            // float4 column groups
+    constexpr int RG = kThreads / CG;     // row groups
+    constexpr int ROWS = DK / RG;         // rows per thread
+    constexpr int NW = kThreads / 64;
+    static_assert(NCH / 2 <= kThreads && DK <= kThreads && ROWS >= 1, "shape");
+
+    const int nh = blockIdx.x;            // sequence * H + head
+    const int h = nh % H;
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int lane = t & 63, wave = t >> 6;
+
+    __shared__ float act[NCH];
+    __shared__ float alpha[DK];
+    __shared__ float red[NW][2 * DV];
+    __shared__ float scal[3];
+
+    // 1. the state strip, loaded before anything else so the reads are in flight
+    float *Sp = S + (size_t)nh * DK * DV;
+    f32x4 s[ROWS];
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j)
+        s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (size_t)(rg + RG * j) * DV) + cg);
+
+    // 2. ShortConv over the window (3 cached tokens, oldest first, then x_t) + Swish
+    if (t < NCH / 2) {
+        const int c = 2 * t;
+        const E *src;
+        int off;
+        if (c < DK) {
+            src = q_pre + (size_t)nh * DK;
+            off = c;
+        } else if (c < 2 * DK) {
+            src = k_pre + (size_t)nh * DK;
+            off = c - DK;
+        } else {
+            src = v_pre + (size_t)nh * DV;
+            off = c - 2 * DK;
+        }
+        float x0, x1;
+        load2(src + off, x0, x1);
+        const float4 w0 = *reinterpret_cast<const float4 *>(conv_w + ((size_t)h * NCH + c) * kWidth);
+        const float4 w1 = *reinterpret_cast<const float4 *>(conv_w + ((size_t)h * NCH + c + 1) * kWidth);
+        E *cache = conv_cache + (size_t)nh * (kWidth - 1) * NCH;
+        const float wa0[3] = {w0.x, w0.y, w0.z}, wa1[3] = {w1.x, w1.y, w1.z};
+        float u0 = w0.w * x0, u1 = w1.w * x1;
+#pragma unroll
+        for (int j = 0; j < kWidth - 1; ++j) {
+            int slot = oldest + j;
+            slot = slot >= kWidth - 1 ? slot - (kWidth - 1) : slot;
+            float a0, a1;
+            load2(cache + slot * NCH + c, a0, a1);
+            u0 += wa0[j] * a0;
+            u1 += wa1[j] * a1;
+        }
+        store2(cache + oldest * NCH + c, x0, x1);   // x_t replaces the oldest token
+        act[c] = swish(u0);
+        act[c + 1] = swish(u1);
+    }
+    if (t < DK)
+        alpha[t] = exp_f(to_f(g[(size_t)nh * DK + t]));
+    __syncthreads();
+
+    // 3. L2Norm scales of q and k, and q . k, by wavefront 0
+    if (wave == 0) {
+        float sq = 0.f, sk = 0.f, qk = 0.f;
+        for (int c = lane; c < DK; c += 64) {
+            const float a = act[c], b = act[DK + c];
+            sq += a * a;
+            sk += b * b;
+            qk += a * b;
+        }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        qk = wave_sum(qk);
+        if (lane == 0) {
+            const float rq = rsqrtf(sq + kL2Eps), rk = rsqrtf(sk + kL2Eps);
+            scal[0] = rq;
+            scal[1] = rk;
+            scal[2] = qk * rq * rk;
+        }
+    }
+    __syncthreads();
+    const float rq = scal[0], rk = scal[1], qdotk = scal[2];
+    const float bt = to_f(beta[nh]);
+
+    // 4. decay the rows, then the two column sums over this thread's rows
+    float vh[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        const int i = rg + RG * j;
+        const float a = alpha[i], kk = act[DK + i] * rk, qq = act[i] * rq;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s[j][c] *= a;
+            vh[c] += s[j][c] * kk;
+            pq[c] += s[j][c] * qq;
+        }
+    }
+    // row groups inside a wavefront are CG lanes apart
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            vh[c] += __shfl_xor(vh[c], off, 64);
+            pq[c] += __shfl_xor(pq[c], off, 64);
+        }
+    }
+    if (lane < CG) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            red[wave][4 * cg + c] = vh[c];
+            red[wave][DV + 4 * cg + c] = pq[c];
+        }
+    }
+    __syncthreads();
+
+    // 5. the edit S' = Sbar + beta k d^T and the readout o = Sbar^T q + beta (q.k) d
+    float d[4], p[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float vs = 0.f, ps = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            vs += red[w][4 * cg + c];
+            ps += red[w][DV + 4 * cg + c];
+        }
+        d[c] = act[2 * DK + 4 * cg + c] - vs;
+        p[c] = ps;
+    }
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+        const int i = rg + RG * j;
+        const float bk = bt * act[DK + i] * rk;
+        f32x4 r = s[j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            r[c] += bk * d[c];
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(Sp + (size_t)i * DV) + cg);
+    }
+    if (rg == 0) {
+        const float bq = bt * qdotk;
+        store4(o + (size_t)nh * DV + 4 * cg, p[0] + bq * d[0], p[1] + bq * d[1], p[2] + bq * d[2],
+               p[3] + bq * d[3]);
+    }
+}
+
+template <int DK, int DV, typename E>
+hipError_t launch(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                  void *conv_cache, int oldest, const void *g, const void *beta, float *S, void *o,
+                  int N, int H, hipStream_t stream)
+{
+    const long blocks = (long)N * H;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w, (E *)conv_cache,
+                       oldest, (const E *)g, (const E *)beta, S, (E *)o, H);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t dispatch(int dk, int dv, const void *q_pre, const void *k_pre, const void *v_pre,
+                    const float *conv_w, void *conv_cache, int oldest, const void *g,
+                    const void *beta, float *S, void *o, int N, int H, hipStream_t stream)
+{
+#define KDA_DECODE_CASE(A, B)                                                                    \
+    if (dk == A && dv == B)                                                                     \
+        return launch<A, B, E>(q_pre, k_pre, v_pre, conv_w, conv_cache, oldest, g, beta, S, o, N, \
+                               H, stream);
+    KDA_DECODE_CASE(128, 128)
+    KDA_DECODE_CASE(128, 64)
+    KDA_DECODE_CASE(64, 128)
+    KDA_DECODE_CASE(64, 64)
+#undef KDA_DECODE_CASE
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
+                              const float *conv_w, void *conv_cache, int oldest_slot,
+                              const void *g, const void *beta, float *S, void *o, int N, int H,
+                              int dk, int dv, bool fp32, hipStream_t stream)
+{
+    if (fp32)
+        return dispatch<float>(dk, dv, q_pre, k_pre, v_pre, conv_w, conv_cache, oldest_slot, g,
+                               beta, S, o, N, H, stream);
+    return dispatch<__bf16>(dk, dv, q_pre, k_pre, v_pre, conv_w, conv_cache, oldest_slot, g, beta,
+                            S, o, N, H, stream);
+}
+
+} // namespace kda

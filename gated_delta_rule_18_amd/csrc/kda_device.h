@@ -1,0 +1,90 @@
+// kda_device.h -- device-side helpers shared by the KDA kernels (gfx950 only).
+//
+// Element types: __bf16 (bf16 mode) or float (fp32 test mode).  Conversions to
+// and from float use the compiler's native __bf16 casts, which gfx950 lowers to
+// its round-to-nearest-even conversion instruction.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename E> struct Vec;
+template <> struct Vec<__bf16> {
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+};
+template <> struct Vec<float> {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    typedef float v8 __attribute__((ext_vector_type(8)));
+};
+
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename E> __device__ __forceinline__ E from_f(float x) { return (E)x; }
+
+template <typename E>
+__device__ __forceinline__ typename Vec<E>::v4 cvt4(f32x4 x)
+{
+    typename Vec<E>::v4 r;
+    r[0] = (E)x[0];
+    r[1] = (E)x[1];
+    r[2] = (E)x[2];
+    r[3] = (E)x[3];
+    return r;
+}
+
+template <typename V4>
+__device__ __forceinline__ auto cat8(V4 a, V4 b)
+{
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// D += A * B over a 32-deep contraction slice, 16x16 output tile.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B; its 8 operand
+// elements are 8 contraction indices.  Which 8 indices a lane holds is up to
+// the caller, as long as A and B agree element by element: the hardware pairs
+// element e of A's lane (i + 16 g) with element e of B's lane (n + 16 g).
+__device__ __forceinline__ f32x4 mma32(Vec<__bf16>::v8 a, Vec<__bf16>::v8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(Vec<float>::v8 a, Vec<float>::v8 b, f32x4 c)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+}
+// Same with a 16-deep slice (4 elements per lane).  The bf16 form zero-pads to
+// the 32-deep instruction instead of using the 16-deep one: a kernel then uses a
+// single MFMA opcode, so an accumulation never chains two MFMAs of different
+// pass counts onto the same accumulator (this toolchain was seen to issue such
+// a pair back to back without the wait states the dependency needs).
+__device__ __forceinline__ f32x4 mma16(Vec<__bf16>::v4 a, Vec<__bf16>::v4 b, f32x4 c)
+{
+    const Vec<__bf16>::v4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(a, z), cat8(b, z), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(Vec<float>::v4 a, Vec<float>::v4 b, f32x4 c)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+}
+
+// e^x through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// Sum over the 64 lanes of a wavefront (result valid in every lane).
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+} // namespace kda

@@ -1,0 +1,18 @@
+// kda_internal.h -- host-side launch entry points of the KDA kernels.  Only the
+// C-ABI layer (kda_api.cpp) calls these; arguments are validated there.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *S0, void *o, float *S_T,
+                            int B, int T, int H, int dk, int dv, bool fp32, int chunk,
+                            hipStream_t stream);
+
+hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
+                              const float *conv_w, void *conv_cache, int oldest_slot,
+                              const void *g, const void *beta, float *S, void *o,
+                              int N, int H, int dk, int dv, bool fp32, hipStream_t stream);
+
+} // namespace kda

@@ -1,0 +1,568 @@
+// kda_prefill.hip -- chunkwise-parallel KDA prefill on gfx950 (kda_chunk_fwd).
+//
+// Method: page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读"
+//   section 3.1, KDA recurrence: S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+//                                o_t = S_t^T q_t, a_t = exp(g_t) per key channel;
+//   section 3.3, chunk interface: (X_[c], S_in) -> (Y_[c], S_out), S_in(c+1) = S_out(c),
+//                parallel inside a chunk (WY/UT organisation), serial across chunks;
+//   section 3.3, lower-bounded decay: g >= -5, so 16 positions of decay sum to
+//                > -80 and e^{+80} still fits bf16 (Figure 3's point: the
+//                diagonal tiles can then be dense matrix products too).
+//
+// Chunk algebra (the pages name it only; derived from the recurrence).  For a
+// chunk of C tokens r = 0..C-1 with incoming state S and G_r = sum_{s<=r} g_s:
+//   A[r,i] = b_r sum_c k_rc k_ic e^{G_rc - G_ic}   (i < r)
+//   M[r,i] =     sum_c q_rc k_ic e^{G_rc - G_ic}   (i <= r)
+//   T      = (I + A)^{-1} Diag(b)                 (UT transform)
+//   U      = T (V - Kt S),   Kt = k * e^{G}
+//   O      = Qt S + M U,     Qt = q * e^{G}
+//   S_out  = Diag(e^{G_C}) S + Ke^T U,  Ke = k * e^{G_C - G}
+// The factor e^{G_rc - G_ic} (i <= r) is split around the chunk centre R =
+// G_{C/2-1}: row factor e^{G_r - R}, column factor e^{R - G_i}.  Each factor
+// spans at most C/2 <= 16 positions of decay, so with g >= -5 both lie in
+// [e^-80, e^80] -- the same bound the pages give for a 16-position tile, here
+// used once per chunk instead of once per tile pair.  Every chunk-relative
+// factor (Kt, Qt, Ke, e^{G_C}) is <= 1 and only underflows where the true
+// contribution is negligible.
+//
+// Work decomposition.  One workgroup (4 wavefronts, 256 threads) owns one
+// (sequence, head, 64-wide value slice); value columns of S evolve
+// independently (Diag(a) scales rows), so the slices never communicate.  The
+// workgroup walks the chunks in order.  Wavefront w owns value columns
+// [16w, 16w+16) of the slice and keeps that dk x 16 strip of S in fp32 MFMA
+// accumulators for the whole sequence; the strip is fed straight back as the
+// B operand of Kt S and Qt S, and U (also an accumulator) straight into
+// M U and Ke^T U, without transposes (the contraction index order inside a
+// lane only has to agree between A and B).
+//
+// Per chunk: (1) the decayed operands, (2) A and M on MFMA, (3) T by forward
+// substitution on the 16x16 diagonal blocks plus one block product, (4) the
+// state-dependent products, (5) o written through LDS as full rows.  The next
+// chunk's q, k, v, g, b are prefetched into registers while (1)-(4) run.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNV = 64;          // value columns per workgroup
+constexpr int kXCD = 8;          // MI355X: 8 accelerator dies, workgroups dealt round-robin
+
+template <typename E, int DK, int C>
+struct Layout {
+    static constexpr int PAD = 16 / (int)sizeof(E);   // 16-byte row padding against bank conflicts
+    static constexpr int LDK = DK + PAD;              // row stride of [C][DK] arrays
+    static constexpr int LC = C + PAD;                // row stride of [*][C] arrays
+    static constexpr int LNV = kNV + PAD;
+    static constexpr int H2 = C / 2;                  // half-chunk, <= 16 positions
+    static constexpr int NB = C / 16;                 // 16-token tiles per chunk
+    static constexpr int VEC = 16 / (int)sizeof(E);   // elements per 16-byte load
+    // element offsets inside the dynamic LDS block (E-typed part)
+    static constexpr int oQ = 0;                      // raw q, then Qt  [C][LDK]
+    static constexpr int oK = oQ + C * LDK;           // raw k, then Kt
+    static constexpr int oG = oK + C * LDK;           // raw g, then Kc (column factor)
+    static constexpr int oKm = oG + C * LDK;          // Km (row factor)
+    static constexpr int oQm = oKm + C * LDK;         // Qm (row factor)
+    static constexpr int oKeT = oQm + C * LDK;        // Ke^T  [DK][LC]
+    static constexpr int oVT = oKeT + DK * LC;        // V^T   [kNV][LC]
+    static constexpr int oM = oVT + kNV * LC;         // M     [C][LC]
+    static constexpr int oT = oM + C * LC;            // T     [C][LC]
+    static constexpr int oO = oT + C * LC;            // o staging [C][LNV]
+    static constexpr int nE = oO + C * LNV;
+    // fp32 part (float offsets after the E part, 16-byte aligned)
+    static constexpr int fBase = ((nE * (int)sizeof(E) + 15) / 16) * 16 / 4;
+    static constexpr int fA = 0;                      // A   [C][C+1]
+    static constexpr int fD = fA + C * (C + 1);       // diagonal-block inverses [NB][16][17]
+    static constexpr int fP = fD + NB * 16 * 17;      // block product scratch [16][17]
+    static constexpr int fGam = fP + 16 * 17;         // e^{G_C}   [DK]
+    static constexpr int fBeta = fGam + DK;           // beta      [C]
+    static constexpr int nF = fBeta + C;
+    static constexpr int bytes = (fBase + nF) * 4;
+};
+
+// Which head/slice a workgroup takes: the slices of one head share an XCD (and
+// so its L2), because every slice re-reads the head's q, k and g.
+__device__ __forceinline__ bool map_block(int id, int nbh, int nsl, int &bh, int &slice)
+{
+    const int x = id % kXCD, r = id / kXCD;
+    bh = (r / nsl) * kXCD + x;
+    slice = r % nsl;
+    return bh < nbh;
+}
+
+template <typename E, int DK, int C>
+struct Prefetch {
+    typedef Layout<E, DK, C> L;
+    static constexpr int VPR = DK / L::VEC;                       // 16-B vectors per q/k/g row
+    static constexpr int NQ = (C * VPR + kThreads - 1) / kThreads;  // per thread per tensor
+    static constexpr int VPV = kNV / L::VEC;
+    static constexpr int NVV = (C * VPV + kThreads - 1) / kThreads;
+    uint4 q[NQ], k[NQ], g[NQ], v[NVV];
+    E b;
+};
+
+template <typename E, int DK, int C>
+__device__ __forceinline__ void prefetch(Prefetch<E, DK, C> &P, const E *q, const E *k,
+                                         const E *g, const E *v, const E *beta, long tok0,
+                                         int valid, int H, int DV, int slice, int tid)
+{
+    typedef Prefetch<E, DK, C> PF;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < PF::NQ; ++n) {
+        const int i = tid + n * kThreads;
+        const int r = i / PF::VPR, cv = i % PF::VPR;
+        P.q[n] = P.k[n] = P.g[n] = zero;
+        if (i < C * PF::VPR && r < valid) {
+            const long off = ((tok0 + r) * H) * (long)DK + cv * Layout<E, DK, C>::VEC;
+            P.q[n] = *reinterpret_cast<const uint4 *>(q + off);
+            P.k[n] = *reinterpret_cast<const uint4 *>(k + off);
+            P.g[n] = *reinterpret_cast<const uint4 *>(g + off);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < PF::NVV; ++n) {
+        const int i = tid + n * kThreads;
+        const int r = i / PF::VPV, cv = i % PF::VPV;
+        P.v[n] = zero;
+        if (i < C * PF::VPV && r < valid) {
+            const long off = ((tok0 + r) * H) * (long)DV + slice * kNV + cv * Layout<E, DK, C>::VEC;
+            P.v[n] = *reinterpret_cast<const uint4 *>(v + off);
+        }
+    }
+    P.b = from_f<E>(0.f);
+    if (tid < valid && tid < C)
+        P.b = beta[(tok0 + tid) * H];
+}
+
+// Registers -> LDS raw buffers (q, k, g row-major; v transposed; beta as fp32).
+template <typename E, int DK, int C>
+__device__ __forceinline__ void commit(const Prefetch<E, DK, C> &P, E *sE, float *sF, int tid)
+{
+    typedef Layout<E, DK, C> L;
+    typedef Prefetch<E, DK, C> PF;
+#pragma unroll
+    for (int n = 0; n < PF::NQ; ++n) {
+        const int i = tid + n * kThreads;
+        if (i < C * PF::VPR) {
+            const int r = i / PF::VPR, c = (i % PF::VPR) * L::VEC;
+            *reinterpret_cast<uint4 *>(sE + L::oQ + r * L::LDK + c) = P.q[n];
+            *reinterpret_cast<uint4 *>(sE + L::oK + r * L::LDK + c) = P.k[n];
+            *reinterpret_cast<uint4 *>(sE + L::oG + r * L::LDK + c) = P.g[n];
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < PF::NVV; ++n) {
+        const int i = tid + n * kThreads;
+        if (i < C * PF::VPV) {
+            const int r = i / PF::VPV, j0 = (i % PF::VPV) * L::VEC;
+            const E *e = reinterpret_cast<const E *>(&P.v[n]);
+#pragma unroll
+            for (int u = 0; u < L::VEC; ++u)
+                sE[L::oVT + (j0 + u) * L::LC + r] = e[u];
+        }
+    }
+    if (tid < C)
+        sF[L::fBeta + tid] = to_f(P.b);
+}
+
+template <typename E, int DK, int C>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
+    float *S_T, int T, int H, int DV, int nbh, int nsl)
+{
+    typedef Layout<E, DK, C> L;
+    typedef typename Vec<E>::v4 V4;
+    typedef typename Vec<E>::v8 V8;
+    constexpr int NCT = DK / 16;        // 16-channel tiles of the state strip
+    constexpr int NKS = DK / 32;        // 32-deep contraction steps over channels
+    constexpr int H2 = L::H2, NB = L::NB;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    E *sE = reinterpret_cast<E *>(smem);
+    float *sF = reinterpret_cast<float *>(smem) + L::fBase;
+
+    int bh, slice;
+    if (!map_block(blockIdx.x, nbh, nsl, bh, slice))
+        return;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;        // MFMA row/column index, lane group
+    const int col = slice * kNV + wave * 16 + l16;    // this lane's value column
+
+    // Base pointers of this head: token t's row is at ((b*T + t)*H + h) * width.
+    const long tokb = (long)b * T;
+    const E *qh = q + (long)h * DK, *kh = k + (long)h * DK, *gh = g + (long)h * DK;
+    const E *vh = v + (long)h * DV, *bh_ = beta + h;
+    E *oh = o + (long)h * DV;
+
+    // zero the upper 16x16 blocks of M and T once (never written afterwards)
+    for (int i = tid; i < C * C; i += kThreads) {
+        const int r = i / C, c = i % C;
+        if (c >= 16 * (r / 16 + 1)) {
+            sE[L::oM + r * L::LC + c] = from_f<E>(0.f);
+            sE[L::oT + r * L::LC + c] = from_f<E>(0.f);
+        }
+    }
+
+    // the fp32 state strip: Sacc[ct][j] = S[16 ct + 4 g4 + j][col]
+    f32x4 Sacc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            Sacc[ct][j] = S0 ? S0[((long)bh * DK + 16 * ct + 4 * g4 + j) * DV + col] : 0.f;
+
+    const int nchunks = (T + C - 1) / C;
+    Prefetch<E, DK, C> P;
+    if (nchunks > 0) {
+        prefetch<E, DK, C>(P, qh, kh, gh, vh, bh_, tokb, T < C ? T : C, H, DV, slice, tid);
+        commit<E, DK, C>(P, sE, sF, tid);
+        if (nchunks > 1)
+            prefetch<E, DK, C>(P, qh, kh, gh, vh, bh_, tokb + C, T - C < C ? T - C : C, H, DV, slice, tid);
+    }
+    __syncthreads();
+
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int t0 = ci * C;
+        const int valid = T - t0 < C ? T - t0 : C;
+
+        // ---- (1) decayed operands, one (channel, half-chunk) per thread --------
+        // Read everything first: the g buffer is overwritten by Kc below.
+        float xq[H2], xk[H2], xg[H2], other = 0.f;
+        const int pc = tid % DK, ph = tid / DK;       // channel, half (0 or 1)
+        const bool pact = tid < 2 * DK;
+        if (pact) {
+#pragma unroll
+            for (int r = 0; r < H2; ++r) {
+                const int row = ph * H2 + r;
+                xq[r] = to_f(sE[L::oQ + row * L::LDK + pc]);
+                xk[r] = to_f(sE[L::oK + row * L::LDK + pc]);
+                xg[r] = to_f(sE[L::oG + row * L::LDK + pc]);
+            }
+#pragma unroll
+            for (int r = 0; r < H2; ++r)
+                other += to_f(sE[L::oG + ((1 - ph) * H2 + r) * L::LDK + pc]);
+        }
+        __syncthreads();
+        if (pact) {
+            // half 0: E_r = G_r - R = -sum_{s=r+1}^{H2-1} g_s >= 0, G_r forward sum,
+            //         R = G_{H2-1}, F = other half's total; G_C - G_r = F - E_r.
+            // half 1: E_r = sum_{s=H2}^{r} g_s <= 0, R = other half's total,
+            //         G_r = R + E_r, G_C - G_r = sum_{s=r+1}^{C-1} g_s.
+            float Er[H2], Gr[H2], Zr[H2];
+            if (ph == 0) {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < H2; ++r) {
+                    acc += xg[r];
+                    Gr[r] = acc;
+                }
+                float rev = 0.f;
+#pragma unroll
+                for (int r = H2 - 1; r >= 0; --r) {
+                    Er[r] = -rev;
+                    Zr[r] = other + rev;
+                    rev += xg[r];
+                }
+                sF[L::fGam + pc] = exp_f(acc + other);
+            } else {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < H2; ++r) {
+                    acc += xg[r];
+                    Er[r] = acc;
+                    Gr[r] = other + acc;
+                }
+                float rev = 0.f;
+#pragma unroll
+                for (int r = H2 - 1; r >= 0; --r) {
+                    Zr[r] = rev;
+                    rev += xg[r];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < H2; ++r) {
+                const int row = ph * H2 + r;
+                const float eE = exp_f(Er[r]), enE = exp_f(-Er[r]);
+                const float eG = exp_f(Gr[r]), eZ = exp_f(Zr[r]);
+                sE[L::oKm + row * L::LDK + pc] = from_f<E>(xk[r] * eE);
+                sE[L::oQm + row * L::LDK + pc] = from_f<E>(xq[r] * eE);
+                sE[L::oG + row * L::LDK + pc] = from_f<E>(xk[r] * enE);       // Kc
+                sE[L::oK + row * L::LDK + pc] = from_f<E>(xk[r] * eG);        // Kt
+                sE[L::oQ + row * L::LDK + pc] = from_f<E>(xq[r] * eG);        // Qt
+                sE[L::oKeT + pc * L::LC + row] = from_f<E>(xk[r] * eZ);       // Ke^T
+            }
+        }
+        __syncthreads();
+
+        // ---- (2) A and M on MFMA: lower 16x16 tiles, K = DK channels -------------
+        // tile list: A(rb,cb) for cb <= rb, then M(rb,cb); NB(NB+1)/2 of each
+        {
+            constexpr int NTILE = NB * (NB + 1) / 2;
+            for (int tix = wave; tix < 2 * NTILE; tix += kThreads / 64) {
+                const bool isM = tix >= NTILE;
+                int tt = isM ? tix - NTILE : tix, rb = 0;
+                while (tt > rb) {
+                    tt -= rb + 1;
+                    ++rb;
+                }
+                const int cb = tt;
+                const E *rowop = sE + (isM ? L::oQm : L::oKm) + (16 * rb + l16) * L::LDK;
+                const E *colop = sE + L::oG + (16 * cb + l16) * L::LDK;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) {
+                    const V8 a = cat8(*reinterpret_cast<const V4 *>(rowop + 32 * m + 8 * g4),
+                                      *reinterpret_cast<const V4 *>(rowop + 32 * m + 8 * g4 + 4));
+                    const V8 bb = cat8(*reinterpret_cast<const V4 *>(colop + 32 * m + 8 * g4),
+                                       *reinterpret_cast<const V4 *>(colop + 32 * m + 8 * g4 + 4));
+                    acc = mma32(a, bb, acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rb + 4 * g4 + j, i = 16 * cb + l16;
+                    if (isM) {
+                        sE[L::oM + r * L::LC + i] = from_f<E>(i <= r ? acc[j] : 0.f);
+                    } else {
+                        sF[L::fA + r * (C + 1) + i] = i < r ? sF[L::fBeta + r] * acc[j] : 0.f;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (3) T = (I + A)^{-1} Diag(beta) ---------------------------------------
+        // diagonal blocks by forward substitution: lane (block, column j)
+        if (wave == 0 && lane < 16 * NB) {
+            const int blk = lane >> 4, j = lane & 15;
+            const float *Ab = sF + L::fA + (16 * blk) * (C + 1) + 16 * blk;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i)
+                    s -= Ab[r * (C + 1) + i] * x[i];
+                x[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sF[L::fD + (blk * 16 + r) * 17 + j] = x[r];
+        }
+        __syncthreads();
+        if (NB == 2) {
+            // off-diagonal block: X10 = -D1 A10 D0, via P = A10 D0
+            {
+                const int r = tid >> 4, j = tid & 15;
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s += sF[L::fA + (16 + r) * (C + 1) + i] * sF[L::fD + i * 17 + j];
+                sF[L::fP + r * 17 + j] = s;
+            }
+            __syncthreads();
+            {
+                const int r = tid >> 4, j = tid & 15;
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s -= sF[L::fD + (16 + r) * 17 + i] * sF[L::fP + i * 17 + j];
+                sE[L::oT + (16 + r) * L::LC + j] = from_f<E>(s * sF[L::fBeta + j]);
+            }
+        }
+        for (int i = tid; i < NB * 256; i += kThreads) {
+            const int blk = i >> 8, r = (i >> 4) & 15, j = i & 15;
+            sE[L::oT + (16 * blk + r) * L::LC + 16 * blk + j] =
+                from_f<E>(sF[L::fD + (blk * 16 + r) * 17 + j] * sF[L::fBeta + 16 * blk + j]);
+        }
+        __syncthreads();
+
+        // ---- (4) state-dependent part, wavefront = 16 value columns --------------
+        {
+            // S strip as B operands: contraction slice m covers channels
+            // {32m + 4g4 + e, 32m + 16 + 4g4 + e}, e = 0..3 (accumulator order)
+            V8 Bs[NKS];
+#pragma unroll
+            for (int m = 0; m < NKS; ++m)
+                Bs[m] = cat8(cvt4<E>(Sacc[2 * m]), cvt4<E>(Sacc[2 * m + 1]));
+
+            f32x4 X[NB], Y[NB];
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt) {
+                X[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const E *kt = sE + L::oK + (16 * rt + l16) * L::LDK + 4 * g4;
+                const E *qt = sE + L::oQ + (16 * rt + l16) * L::LDK + 4 * g4;
+#pragma unroll
+                for (int m = 0; m < NKS; ++m) {
+                    const V8 a = cat8(*reinterpret_cast<const V4 *>(kt + 32 * m),
+                                      *reinterpret_cast<const V4 *>(kt + 32 * m + 16));
+                    const V8 aq = cat8(*reinterpret_cast<const V4 *>(qt + 32 * m),
+                                       *reinterpret_cast<const V4 *>(qt + 32 * m + 16));
+                    X[rt] = mma32(a, Bs[m], X[rt]);
+                    Y[rt] = mma32(aq, Bs[m], Y[rt]);
+                }
+                // X <- V - Kt S   (rows 16 rt + 4 g4 + j, column l16 of the strip)
+                const V4 vv = *reinterpret_cast<const V4 *>(sE + L::oVT + (wave * 16 + l16) * L::LC +
+                                                            16 * rt + 4 * g4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    X[rt][j] = to_f(vv[j]) - X[rt][j];
+            }
+
+            // U = T X ; O = Y + M U ; S <- e^{G_C} S + Ke^T U.  Token contraction
+            // order inside a lane: {4g4 + e, 16 + 4g4 + e} (the accumulator rows).
+            f32x4 U[NB];
+            if (NB == 2) {
+                const V8 bx = cat8(cvt4<E>(X[0]), cvt4<E>(X[NB - 1]));
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt) {
+                    const E *tr = sE + L::oT + (16 * rt + l16) * L::LC + 4 * g4;
+                    const V8 a = cat8(*reinterpret_cast<const V4 *>(tr), *reinterpret_cast<const V4 *>(tr + 16));
+                    U[rt] = mma32(a, bx, f32x4{0.f, 0.f, 0.f, 0.f});
+                }
+                const V8 bu = cat8(cvt4<E>(U[0]), cvt4<E>(U[NB - 1]));
+#pragma unroll
+                for (int rt = 0; rt < NB; ++rt) {
+                    const E *mr = sE + L::oM + (16 * rt + l16) * L::LC + 4 * g4;
+                    const V8 a = cat8(*reinterpret_cast<const V4 *>(mr), *reinterpret_cast<const V4 *>(mr + 16));
+                    Y[rt] = mma32(a, bu, Y[rt]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const E *kr = sE + L::oKeT + (16 * ct + l16) * L::LC + 4 * g4;
+                    const V8 a = cat8(*reinterpret_cast<const V4 *>(kr), *reinterpret_cast<const V4 *>(kr + 16));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        Sacc[ct][j] *= sF[L::fGam + 16 * ct + 4 * g4 + j];
+                    Sacc[ct] = mma32(a, bu, Sacc[ct]);
+                }
+            } else {
+                const V4 bx = cvt4<E>(X[0]);
+                const V4 at = *reinterpret_cast<const V4 *>(sE + L::oT + l16 * L::LC + 4 * g4);
+                U[0] = mma16(at, bx, f32x4{0.f, 0.f, 0.f, 0.f});
+                const V4 bu = cvt4<E>(U[0]);
+                const V4 am = *reinterpret_cast<const V4 *>(sE + L::oM + l16 * L::LC + 4 * g4);
+                Y[0] = mma16(am, bu, Y[0]);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const V4 a = *reinterpret_cast<const V4 *>(sE + L::oKeT + (16 * ct + l16) * L::LC + 4 * g4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        Sacc[ct][j] *= sF[L::fGam + 16 * ct + 4 * g4 + j];
+                    Sacc[ct] = mma16(a, bu, Sacc[ct]);
+                }
+            }
+            // O tile -> LDS staging
+#pragma unroll
+            for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sE[L::oO + (16 * rt + 4 * g4 + j) * L::LNV + wave * 16 + l16] = from_f<E>(Y[rt][j]);
+        }
+        __syncthreads();
+
+        // ---- (5) o rows out; next chunk's raw data in; prefetch the one after ---
+        {
+            constexpr int VPV = kNV / L::VEC;
+            for (int i = tid; i < C * VPV; i += kThreads) {
+                const int r = i / VPV, cv = i % VPV;
+                if (r < valid)
+                    *reinterpret_cast<uint4 *>(oh + ((tokb + t0 + r) * H) * (long)DV + slice * kNV + cv * L::VEC) =
+                        *reinterpret_cast<const uint4 *>(sE + L::oO + r * L::LNV + cv * L::VEC);
+            }
+        }
+        if (ci + 1 < nchunks) {
+            commit<E, DK, C>(P, sE, sF, tid);
+            if (ci + 2 < nchunks) {
+                const int t2 = t0 + 2 * C;
+                prefetch<E, DK, C>(P, qh, kh, gh, vh, bh_, tokb + t2, T - t2 < C ? T - t2 : C, H, DV, slice, tid);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (S_T) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S_T[((long)bh * DK + 16 * ct + 4 * g4 + j) * DV + col] = Sacc[ct][j];
+    }
+}
+
+// T == 0: S_T = S0 (or 0).  One thread per state element.
+__global__ void copy_state_kernel(const float *S0, float *S_T, long n)
+{
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        S_T[i] = S0 ? S0[i] : 0.f;
+}
+
+template <typename E, int DK, int C>
+hipError_t launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                  const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
+                  hipStream_t stream)
+{
+    typedef Layout<E, DK, C> L;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    // at least 81 KiB so that a CU never holds two of these workgroups (the
+    // sequence loop is serial: two on one CU would halve both)
+    constexpr int lds = L::bytes > 81 * 1024 ? L::bytes : 81 * 1024;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<E, DK, C>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    const int nbh = B * H, nsl = dv / kNV;
+    const int grid = ((nbh + kXCD - 1) / kXCD) * kXCD * nsl;
+    hipLaunchKernelGGL((prefill_kernel<E, DK, C>), dim3(grid), dim3(kThreads), lds, stream,
+                       (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
+                       (E *)o, S_T, T, H, dv, nbh, nsl);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t dispatch(int dk, int chunk, const void *q, const void *k, const void *v, const void *g,
+                    const void *beta, const float *S0, void *o, float *S_T, int B, int T, int H,
+                    int dv, hipStream_t stream)
+{
+#define KDA_PREFILL_CASE(D, CC)                                                         \
+    if (dk == D && chunk == CC)                                                         \
+        return launch<E, D, CC>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+    KDA_PREFILL_CASE(128, 32)
+    KDA_PREFILL_CASE(128, 16)
+    KDA_PREFILL_CASE(64, 32)
+    KDA_PREFILL_CASE(64, 16)
+#undef KDA_PREFILL_CASE
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *S0, void *o, float *S_T, int B, int T,
+                            int H, int dk, int dv, bool fp32, int chunk, hipStream_t stream)
+{
+    if ((long)B * H == 0)
+        return hipSuccess;
+    if (T == 0) {
+        if (!S_T || S_T == S0)
+            return hipSuccess;
+        const long n = (long)B * H * dk * dv;
+        hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           S0, S_T, n);
+        return hipGetLastError();
+    }
+    if (fp32)
+        return dispatch<float>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+    return dispatch<__bf16>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+}
+
+} // namespace kda

@@ -1,0 +1,123 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) layer recurrence
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.1, KDA recurrence equation; restated on page "Kimi K3 架构篇：一文详解
+ * 2.8 万亿参数的巨型怪兽", section "KDA 到底在算什么"): per head, with state
+ * S_t in R^{dk x dv} (row = key channel, column = value channel),
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * where alpha_t = exp(g_t) per key channel and g_t lies in [g_min, 0] with
+ * g_min = -5 (same page, section 3.3, lower-bounded decay equation).  The
+ * query is not scaled.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers, row-major and contiguous, with
+ *     16-byte aligned base addresses.  The caller allocates and frees them; the
+ *     library allocates nothing and keeps no global state, so concurrent calls
+ *     on different buffers are safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; the call returns without synchronising.  Kernel
+ *     faults surface on the stream, not in the return code.
+ *   - dtype KDA_BF16: q, k, v, g, beta, o (and the decode conv cache) are
+ *     bfloat16; the state is fp32.  dtype KDA_FP32 (test mode): every tensor is
+ *     fp32.
+ *   - Return 0 on success or a negative KDA_ERR_* code; nothing is enqueued
+ *     when a code other than KDA_ERR_LAUNCH is returned.
+ *   - Values outside the stated domains (g outside [-5, 0], beta outside
+ *     [0, 1], non-finite inputs) are not diagnosed and give unspecified output.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 100 /* 1.0.0 */
+
+enum kda_dtype {
+    KDA_BF16 = 0, /* bf16 activations, fp32 state */
+    KDA_FP32 = 1  /* everything fp32 (test mode) */
+};
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID = -1,     /* null required pointer, bad size, bad dtype/chunk/width/misalignment */
+    KDA_ERR_UNSUPPORTED = -2, /* a head size this build has no kernel for (dk, dv not in {64, 128}) */
+    KDA_ERR_LAUNCH = -3       /* the HIP runtime rejected the launch */
+};
+
+/*
+ * kda_chunk_fwd -- chunkwise-parallel prefill of one KDA layer.
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.3, chunk-interface equation): the sequence is cut into chunks of
+ * `chunk` tokens processed in parallel inside a chunk, and the state leaving
+ * chunk c is the state entering chunk c+1.  The result equals the token-serial
+ * recurrence above up to floating-point association order.
+ *
+ *   q, k, g : [B, T, H, dk]   (dtype)    queries, keys (normally unit length), log-decay g
+ *   v       : [B, T, H, dv]   (dtype)    values
+ *   beta    : [B, T, H]       (dtype)    write strength
+ *   S0      : [B, H, dk, dv]  fp32       initial state; NULL means zero
+ *   o       : [B, T, H, dv]   (dtype)    output, o_t = S_t^T q_t (written)
+ *   S_T     : [B, H, dk, dv]  fp32       final state (written); NULL = not returned.
+ *                                        S_T may equal S0 (in-place streaming over
+ *                                        segments); any other overlap is invalid.
+ *   dk, dv  : 64 or 128
+ *   chunk   : 16 or 32 (tokens per chunk; both give the same result up to rounding)
+ * T may be any value >= 0 (a ragged last chunk is handled); T == 0 copies S0
+ * to S_T (or zeroes S_T when S0 is NULL).
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                  const void *beta, const float *S0, void *o, float *S_T,
+                  int B, int T, int H, int dk, int dv, int dtype, int chunk,
+                  void *stream);
+
+/*
+ * kda_decode_step -- one generated token of one KDA layer for N sequences.
+ *
+ * Defines (same page, section 3.2): the decode interface
+ * (x_t, S_{t-1}, C^conv_{t-1}) -> (y_t, S_t, C^conv_t), the input branches
+ * q, k = L2Norm(Swish(ShortConv(W x))), v = Swish(ShortConv(W_v x)), and the
+ * step order Sbar = Diag(alpha) S, vhat = Sbar^T k, S = Sbar + beta k (v - vhat)^T,
+ * o = S^T q (read after the write).  The projections W x are done by the
+ * caller; this call starts from their outputs.  Readings where the pages are
+ * silent: ShortConv is depthwise and causal with no bias, tap 0 multiplies
+ * the oldest token; Swish(u) = u * sigmoid(u); L2Norm(x) = x / sqrt(sum x^2 + 1e-6).
+ *
+ *   q_pre, k_pre : [N, H, dk]  (dtype)   projected pre-activations of x_t
+ *   v_pre        : [N, H, dv]  (dtype)
+ *   conv_w       : [H, 2dk+dv, width] fp32   taps, channel order q | k | v
+ *   conv_cache   : [N, H, width-1, 2dk+dv] (dtype), a ring of the previous
+ *                  width-1 pre-activations; slot (conv_pos mod (width-1)) holds
+ *                  the oldest and is overwritten with x_t (read and written)
+ *   conv_pos     : >= 0; the caller advances it by one per step
+ *   g            : [N, H, dk] (dtype)     log-decay of this step
+ *   beta         : [N, H]     (dtype)
+ *   S            : [N, H, dk, dv] fp32    state, updated in place
+ *   o            : [N, H, dv] (dtype)     output o_t = S_t^T q_t (written)
+ *   width        : 4
+ *   dk, dv       : 64 or 128
+ */
+int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
+                    const float *conv_w, void *conv_cache, int conv_pos,
+                    const void *g, const void *beta, float *S, void *o,
+                    int N, int H, int dk, int dv, int width, int dtype,
+                    void *stream);
+
+/* Human-readable text for a kda_status code (static storage, never NULL). */
+const char *kda_strerror(int status);
+
+/* KDA_VERSION of the loaded library. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

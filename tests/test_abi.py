@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every symbol include/kda.h declares, and rejects
+bad arguments before touching the GPU (no compute calls here: runs on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_18_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "kda.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(kda_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exports():
+    assert _declared() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror():
+    assert binding.version() == 100
+    L = binding.lib()
+    for code in (0, -1, -2, -3, 17):
+        assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
+
+
+# fake, 16-byte aligned device addresses: validation rejects before any use
+A = 0x10000
+MIS = 0x10002
+
+
+def _prefill(**kw):
+    args = dict(q=A, k=A, v=A, g=A, beta=A, S0=A, o=A, S_T=A, B=1, T=8, H=2, dk=64, dv=64,
+                dtype=0, chunk=32, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_chunk_fwd(vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]),
+                                       vp(args["beta"]), vp(args["S0"]), vp(args["o"]), vp(args["S_T"]),
+                                       args["B"], args["T"], args["H"], args["dk"], args["dv"],
+                                       args["dtype"], args["chunk"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(chunk=64), -1), (dict(chunk=7), -1), (dict(dtype=2), -1), (dict(B=-1), -1),
+    (dict(T=-3), -1), (dict(dk=0), -1), (dict(dk=96), -2), (dict(dv=256), -2),
+    (dict(q=None), -1), (dict(o=None), -1), (dict(k=MIS), -1), (dict(S_T=A + 64), -1),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_batch_is_a_no_op():
+    assert _prefill(B=0, q=None, k=None, v=None, g=None, beta=None, o=None) == 0
+    assert _prefill(H=0) == 0
+
+
+def _decode(**kw):
+    args = dict(qp=A, kp=A, vp=A, w=A, cache=A, pos=0, g=A, beta=A, S=A, o=A, N=2, H=3, dk=64,
+                dv=64, width=4, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_decode_step(vp(args["qp"]), vp(args["kp"]), vp(args["vp"]), vp(args["w"]),
+                                         vp(args["cache"]), args["pos"], vp(args["g"]), vp(args["beta"]),
+                                         vp(args["S"]), vp(args["o"]), args["N"], args["H"], args["dk"],
+                                         args["dv"], args["width"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(width=3), -1), (dict(width=5), -1), (dict(pos=-1), -1), (dict(dtype=7), -1),
+    (dict(dk=32), -2), (dict(S=None), -1), (dict(cache=MIS), -1), (dict(N=-2), -1),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_is_a_no_op():
+    assert _decode(N=0, S=None) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        binding.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))

@@ -1,0 +1,140 @@
+"""GPU prefill (kda_chunk_fwd through the C ABI) against the fp64 CPU oracle.
+
+Inputs are seeded and synthetic (gated_delta_rule_18_amd.inputs); the oracle gets
+the exact upcast of the tensors the GPU consumed.  Bars: bf16 max|do| <= 2e-2 |o|_inf,
+max|dS| <= 1e-2 |S|_inf; fp32 test mode <= 1e-5 for both.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_18_amd import binding
+from gated_delta_rule_18_amd.inputs import WORKLOADS, PrefillSpec, prefill_inputs, to_f64
+from tests.util import TOL, assert_parity, oracle_prefill_heads
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, chunk, S0="inp", S_T=None):
+    s0 = inp["S0"] if S0 == "inp" else S0
+    o, st = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], s0, chunk=chunk, S_T=S_T)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def _full_oracle(inp):
+    return oracle.prefill(*(to_f64(inp[n]) for n in ("q", "k", "v", "g", "beta")), to_f64(inp["S0"]))
+
+
+def _check_full(spec, gpu, chunk, tag):
+    inp = prefill_inputs(spec, device=gpu)
+    o, st = _run(inp, chunk)
+    oo, so = _full_oracle(inp)
+    to, ts = TOL[spec.dtype]
+    eo = assert_parity(to_f64(o), oo, to, f"{tag} o")
+    es = assert_parity(to_f64(st), so, ts, f"{tag} S_T")
+    print(f"{tag}: chunk {chunk} err_o {eo:.2e} err_S {es:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_tiny_fp32(gpu, chunk):
+    """B1 H2 T256 d64 fp32 (configs' tiny case, native chunk 16; chunk 32 too)."""
+    _check_full(WORKLOADS["tiny_fp32"], gpu, chunk, "tiny_fp32")
+
+
+@pytest.mark.parametrize("name,chunk", [("L1", 16), ("L1", 32), ("L1_bf16", 32), ("L1_bf16", 16)])
+def test_long_memory_small(gpu, name, chunk):
+    """Gates near 1 so the state carried across chunks dominates the output."""
+    _check_full(WORKLOADS[name], gpu, chunk, name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("T", [1, 15, 33, 100])
+def test_shapes_and_ragged_tails(gpu, dtype, dk, dv, T):
+    spec = PrefillSpec(B=2, H=3, T=T, dk=dk, dv=dv, dtype=dtype, seed=100 + T + dk + dv, s0_std=0.5)
+    for chunk in (16, 32):
+        _check_full(spec, gpu, chunk, f"B2H3T{T} dk{dk} dv{dv} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bound_stress_all_minus5(gpu, dtype):
+    """g = -5 on every token and channel (the bound): the e^80 factors stay finite."""
+    spec = PrefillSpec(B=1, H=2, T=200, dk=128, dv=128, dtype=dtype, seed=7, s0_std=0.02,
+                       gate="const", g_const=-5.0)
+    for chunk in (16, 32):
+        _check_full(spec, gpu, chunk, f"g=-5 {dtype}")
+
+
+def test_zero_state_variants_and_in_place(gpu):
+    spec = PrefillSpec(B=2, H=2, T=70, dk=128, dv=128, seed=21, s0_std=0.3)
+    inp = prefill_inputs(spec, device=gpu)
+    # S0 = None equals an explicit zero state
+    o1, s1 = _run(inp, 32, S0=None)
+    o2, s2 = _run(inp, 32, S0=torch.zeros_like(inp["S0"]))
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    # S_T = None still writes o
+    o3, s3 = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"],
+                               return_state=False)
+    assert s3 is None
+    o4, s4 = _run(inp, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o4)
+    # in place: S_T is S0
+    S = inp["S0"].clone()
+    o5, s5 = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S, S_T=S)
+    torch.cuda.synchronize()
+    assert s5 is S and torch.equal(S, s4) and torch.equal(o5, o4)
+
+
+def test_empty_sequence(gpu):
+    spec = PrefillSpec(B=2, H=3, T=0, dk=64, dv=128, seed=3, s0_std=1.0)
+    inp = prefill_inputs(spec, device=gpu)
+    o, st = _run(inp, 32)
+    assert o.shape == (2, 0, 3, 128)
+    assert torch.equal(st, inp["S0"])
+    o, st = _run(inp, 32, S0=None)
+    assert torch.count_nonzero(st) == 0
+
+
+def test_segments_equal_one_call(gpu):
+    """State passing: two chunk-aligned segments equal one call (same kernel order)."""
+    spec = PrefillSpec(B=1, H=4, T=192, dk=128, dv=128, seed=5)
+    inp = prefill_inputs(spec, device=gpu)
+    o, st = _run(inp, 32)
+    cut = 96
+    a = {n: inp[n][:, :cut].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    b = {n: inp[n][:, cut:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    oa, sa = binding.chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], inp["S0"])
+    ob, sb = binding.chunk_fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], sa)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([oa, ob], 1), o)
+    assert torch.equal(sb, st)
+
+
+def test_chunk_size_independence_and_determinism(gpu):
+    spec = WORKLOADS["prefill_b4h32"]
+    inp = prefill_inputs(PrefillSpec(**{**spec.__dict__, "T": 1024}), device=gpu)
+    o32, s32 = _run(inp, 32)
+    o32b, s32b = _run(inp, 32)
+    assert torch.equal(o32, o32b) and torch.equal(s32, s32b), "run-to-run bitwise"
+    o16, s16 = _run(inp, 16)
+    assert_parity(to_f64(o16), to_f64(o32), 2e-2, "chunk 16 vs 32 o")
+    assert_parity(to_f64(s16), to_f64(s32), 1e-2, "chunk 16 vs 32 S")
+
+
+@pytest.mark.parametrize("name", ["prefill_b4h32", "L2", "L3"])
+def test_prefill_b4h32_sampled_heads(gpu, name):
+    """B4 H32 T4096 d128 bf16 at full size; the oracle checks 6 (b, h) pairs in full."""
+    spec = WORKLOADS[name]
+    inp = prefill_inputs(spec, device=gpu)
+    o, st = _run(inp, 32)
+    heads = [(0, 0), (0, 31), (1, 7), (2, 16), (3, 5), (3, 31)]
+    oo, so = oracle_prefill_heads(inp, heads)
+    og = np.stack([to_f64(o[b, :, h]) for b, h in heads])
+    sg = np.stack([to_f64(st[b, h]) for b, h in heads])
+    to, ts = TOL["bf16"]
+    eo = assert_parity(og, oo, to, f"{name} o")
+    es = assert_parity(sg, so, ts, f"{name} S_T")
+    print(f"{name}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
