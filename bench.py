@@ -5,7 +5,7 @@
 Two timed phases, each W untimed steps then K timed steps bracketed by
 torch.cuda.synchronize():
   prefill  one kda_chunk_fwd over the K3-shaped layer: B=1, H=96, T=65536,
-           dk=dv=128, bf16 inputs, fp32 state, chunk 32, 10 % of tokens at
+           dk=dv=128, bf16 inputs, fp32 state, chunk 16, 10 % of tokens at
            g = -4.99 (the headline: `value` is its tokens/s);
   decode   one kda_decode_step over N=256 sequences x H=96 heads, dk=dv=128,
            bf16, ShortConv width 4 (reported under "decode").
@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=32)
+    ap.add_argument("--chunk", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
     args = ap.parse_args()

@@ -4,7 +4,7 @@ Every step of the computation runs in the library's HIP kernels; torch is used
 for device memory and for the current HIP stream.  If the library is missing
 the calls raise (there is no fallback).
 
-    o, S_T = chunk_fwd(q, k, v, g, beta, S0=None, chunk=32)
+    o, S_T = chunk_fwd(q, k, v, g, beta, S0=None, chunk=16)
     o      = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
 
 Shapes and dtypes follow include/kda.h: bf16 activations with an fp32 state,
@@ -90,7 +90,7 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def chunk_fwd(q, k, v, g, beta, S0=None, chunk=32, o=None, S_T=None, return_state=True):
+def chunk_fwd(q, k, v, g, beta, S0=None, chunk=16, o=None, S_T=None, return_state=True):
     """Chunkwise prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
     S0 [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv] fp32 or None).
     S_T may be passed as S0 itself for in-place streaming over segments."""

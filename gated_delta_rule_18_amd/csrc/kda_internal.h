@@ -10,6 +10,11 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const v
                             int B, int T, int H, int dk, int dv, bool fp32, int chunk,
                             hipStream_t stream);
 
+// chunk = 16: the warp-specialised kernel (kda_prefill_ws.hip)
+hipError_t launch_chunk16(const void *q, const void *k, const void *v, const void *g,
+                          const void *beta, const float *S0, void *o, float *S_T,
+                          int B, int T, int H, int dk, int dv, bool fp32, hipStream_t stream);
+
 hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
                               const float *conv_w, void *conv_cache, int oldest_slot,
                               const void *g, const void *beta, float *S, void *o,

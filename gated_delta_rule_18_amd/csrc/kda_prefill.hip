@@ -560,6 +560,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const v
                            S0, S_T, n);
         return hipGetLastError();
     }
+    if (chunk == 16)
+        return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, stream);
     if (fp32)
         return dispatch<float>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
     return dispatch<__bf16>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);

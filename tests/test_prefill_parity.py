@@ -67,23 +67,24 @@ def test_bound_stress_all_minus5(gpu, dtype):
         _check_full(spec, gpu, chunk, f"g=-5 {dtype}")
 
 
-def test_zero_state_variants_and_in_place(gpu):
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_zero_state_variants_and_in_place(gpu, chunk):
     spec = PrefillSpec(B=2, H=2, T=70, dk=128, dv=128, seed=21, s0_std=0.3)
     inp = prefill_inputs(spec, device=gpu)
     # S0 = None equals an explicit zero state
-    o1, s1 = _run(inp, 32, S0=None)
-    o2, s2 = _run(inp, 32, S0=torch.zeros_like(inp["S0"]))
+    o1, s1 = _run(inp, chunk, S0=None)
+    o2, s2 = _run(inp, chunk, S0=torch.zeros_like(inp["S0"]))
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     # S_T = None still writes o
     o3, s3 = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"],
-                               return_state=False)
+                               chunk=chunk, return_state=False)
     assert s3 is None
-    o4, s4 = _run(inp, 32)
+    o4, s4 = _run(inp, chunk)
     torch.cuda.synchronize()
     assert torch.equal(o3, o4)
     # in place: S_T is S0
     S = inp["S0"].clone()
-    o5, s5 = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S, S_T=S)
+    o5, s5 = binding.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S, chunk=chunk, S_T=S)
     torch.cuda.synchronize()
     assert s5 is S and torch.equal(S, s4) and torch.equal(o5, o4)
 
@@ -98,16 +99,17 @@ def test_empty_sequence(gpu):
     assert torch.count_nonzero(st) == 0
 
 
-def test_segments_equal_one_call(gpu):
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_segments_equal_one_call(gpu, chunk):
     """State passing: two chunk-aligned segments equal one call (same kernel order)."""
     spec = PrefillSpec(B=1, H=4, T=192, dk=128, dv=128, seed=5)
     inp = prefill_inputs(spec, device=gpu)
-    o, st = _run(inp, 32)
+    o, st = _run(inp, chunk)
     cut = 96
     a = {n: inp[n][:, :cut].contiguous() for n in ("q", "k", "v", "g", "beta")}
     b = {n: inp[n][:, cut:].contiguous() for n in ("q", "k", "v", "g", "beta")}
-    oa, sa = binding.chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], inp["S0"])
-    ob, sb = binding.chunk_fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], sa)
+    oa, sa = binding.chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], inp["S0"], chunk=chunk)
+    ob, sb = binding.chunk_fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], sa, chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([oa, ob], 1), o)
     assert torch.equal(sb, st)
@@ -120,16 +122,19 @@ def test_chunk_size_independence_and_determinism(gpu):
     o32b, s32b = _run(inp, 32)
     assert torch.equal(o32, o32b) and torch.equal(s32, s32b), "run-to-run bitwise"
     o16, s16 = _run(inp, 16)
+    o16b, s16b = _run(inp, 16)
+    assert torch.equal(o16, o16b) and torch.equal(s16, s16b), "run-to-run bitwise (chunk 16)"
     assert_parity(to_f64(o16), to_f64(o32), 2e-2, "chunk 16 vs 32 o")
     assert_parity(to_f64(s16), to_f64(s32), 1e-2, "chunk 16 vs 32 S")
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("name", ["prefill_b4h32", "L2", "L3"])
-def test_prefill_b4h32_sampled_heads(gpu, name):
+def test_prefill_b4h32_sampled_heads(gpu, name, chunk):
     """B4 H32 T4096 d128 bf16 at full size; the oracle checks 6 (b, h) pairs in full."""
     spec = WORKLOADS[name]
     inp = prefill_inputs(spec, device=gpu)
-    o, st = _run(inp, 32)
+    o, st = _run(inp, chunk)
     heads = [(0, 0), (0, 31), (1, 7), (2, 16), (3, 5), (3, 31)]
     oo, so = oracle_prefill_heads(inp, heads)
     og = np.stack([to_f64(o[b, :, h]) for b, h in heads])
@@ -137,4 +142,4 @@ def test_prefill_b4h32_sampled_heads(gpu, name):
     to, ts = TOL["bf16"]
     eo = assert_parity(og, oo, to, f"{name} o")
     es = assert_parity(sg, so, ts, f"{name} S_T")
-    print(f"{name}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
+    print(f"{name} chunk {chunk}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
