@@ -125,50 +125,106 @@ template <> struct Pair<__bf16> {
         r[1] = (__bf16)b;
         return __builtin_bit_cast(T, r);
     }
-    static __device__ __forceinline__ T zero() { return 0u; }
+    // low halves of x and y (element 0 of each pair), high halves
+    static __device__ __forceinline__ T los(T x, T y) { return (x & 0xffffu) | (y << 16); }
+    static __device__ __forceinline__ T his(T x, T y) { return (x >> 16) | (y & 0xffff0000u); }
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
 };
 template <> struct Pair<float> {
     typedef float2 T;
     static __device__ __forceinline__ float lo(T x) { return x.x; }
     static __device__ __forceinline__ float hi(T x) { return x.y; }
     static __device__ __forceinline__ T pack(float a, float b) { return make_float2(a, b); }
-    static __device__ __forceinline__ T zero() { return make_float2(0.f, 0.f); }
+    static __device__ __forceinline__ T los(T x, T y) { return make_float2(x.x, y.x); }
+    static __device__ __forceinline__ T his(T x, T y) { return make_float2(x.y, y.y); }
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+    }
 };
 
-// One chunk's raw inputs for one producer wave: lane l holds key channels
-// 2l, 2l+1 of q, k, g for the 16 tokens, value columns 2l, 2l+1 of the slice
-// (lanes < 32) and beta of token l (lanes < 16).
+// A scalar element as raw bits (converted where it is used, so that no
+// instruction right after the load has to wait for it).
+__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, __bf16 *)
+{
+    return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, float *)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+__device__ __forceinline__ float bits_to_f(unsigned x, __bf16 *) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bits_to_f(unsigned x, float *) { return __uint_as_float(x); }
+__device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, __bf16 *)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, float *)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+
+// Raw buffer over [base, base + bytes): loads past the end return 0 and stores
+// past the end are dropped, which masks a chunk's ragged tail without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+// One chunk in the producer's compute layout: lane l holds key channels 2l,
+// 2l+1 of q, k, g (and value columns 2l, 2l+1) for the 16 tokens.
 template <typename E>
 struct Raw {
     typename Pair<E>::T q[kC], k[kC], g[kC], v[kC];
-    E b;
+    float b;
+};
+
+// One chunk's raw inputs for one producer wave, as 16-byte vectors straight
+// from HBM (few, wide loads: the wave never has more outstanding loads than
+// its vmcnt counter can track).  q, k, g: load i of lane l is token
+// i * TPI + l / VPR, bytes 16 (l % VPR) .. of that token's head row; v the
+// same over the slice's 64 values; beta of token l for lanes < 16.  Tokens
+// past the end read 0.
+template <typename E, int DK>
+struct RawV {
+    static constexpr int ES = (int)sizeof(E);
+    static constexpr int VPR = DK * ES / 16, TPI = 64 / VPR, NL = kC / TPI;       // q, k, g
+    static constexpr int VPRV = kVS * ES / 16, TPIV = 64 / VPRV, NLV = kC / TPIV;  // v
+    uint4 q[NL], k[NL], g[NL], v[NLV];
+    unsigned b;          // beta of token (l & 15), raw bits
 };
 
 template <typename E, int DK>
-__device__ __forceinline__ void load_raw(Raw<E> &R, const E *qh, const E *kh, const E *gh,
-                                         const E *vh, const E *bh, long tok0, int valid, int H,
+__device__ __forceinline__ void load_raw(RawV<E, DK> &R, const E *q, const E *k, const E *g,
+                                         const E *v, const E *beta, long row0, int valid, int H,
                                          int DV, int slice, int lane)
 {
-    typedef Pair<E> PE;
-    typedef typename PE::T PT;
-    const bool kch = 2 * lane < DK, vch = lane < kVS / 2;
+    typedef RawV<E, DK> RV;
+    constexpr int ES = RV::ES;
+    // row0 = (b T + t0) H + h: this head's row of the chunk's first token
+    const int rsk = H * DK * ES, rsv = H * DV * ES;
+    const __amdgpu_buffer_rsrc_t rq = buffer(q + row0 * DK, (valid - 1) * rsk + DK * ES);
+    const __amdgpu_buffer_rsrc_t rk = buffer(k + row0 * DK, (valid - 1) * rsk + DK * ES);
+    const __amdgpu_buffer_rsrc_t rg = buffer(g + row0 * DK, (valid - 1) * rsk + DK * ES);
+    const __amdgpu_buffer_rsrc_t rv = buffer(v + row0 * DV + slice * kVS, (valid - 1) * rsv + kVS * ES);
+    const __amdgpu_buffer_rsrc_t rb = buffer(beta + row0, (valid - 1) * H * ES + ES);
+    const int vo = (lane / RV::VPR) * rsk + (lane % RV::VPR) * 16;
+    const int vov = (lane / RV::VPRV) * rsv + (lane % RV::VPRV) * 16;
 #pragma unroll
-    for (int r = 0; r < kC; ++r) {
-        R.q[r] = R.k[r] = R.g[r] = R.v[r] = PE::zero();
-        if (r < valid) {
-            const long row = (tok0 + r) * H;
-            if (kch) {
-                R.q[r] = *reinterpret_cast<const PT *>(qh + row * DK + 2 * lane);
-                R.k[r] = *reinterpret_cast<const PT *>(kh + row * DK + 2 * lane);
-                R.g[r] = *reinterpret_cast<const PT *>(gh + row * DK + 2 * lane);
-            }
-            if (vch)
-                R.v[r] = *reinterpret_cast<const PT *>(vh + row * DV + slice * kVS + 2 * lane);
-        }
+    for (int i = 0; i < RV::NL; ++i) {
+        R.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, vo, i * RV::TPI * rsk, 0));
+        R.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, vo, i * RV::TPI * rsk, 0));
+        R.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, vo, i * RV::TPI * rsk, 0));
     }
-    R.b = from_f<E>(0.f);
-    if (lane < valid && lane < kC)
-        R.b = bh[(tok0 + lane) * H];
+#pragma unroll
+    for (int i = 0; i < RV::NLV; ++i)
+        R.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vov, i * RV::TPIV * rsv, 0));
+    R.b = load_bits(rb, (lane & 15) * H * ES, (E *)nullptr);
 }
 
 template <typename E, int DK>
@@ -196,7 +252,10 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
     if (bh >= nbh)
         return;
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wavefront index, made provably uniform (buffer descriptors built from it
+    // must live in scalar registers)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
     const long tokb = (long)b * T;
     const int nchunks = (T + kC - 1) / kC;
@@ -207,6 +266,8 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 
     if (wave < 4) {
         // =============================== consumer ===============================
+        // the state chain is the critical path: let it win issue slots
+        __builtin_amdgcn_s_setprio(2);
         const int w = wave;
         const int col = slice * kVS + 16 * w + l16;      // this lane's value column
         f32x4 Sacc[NCT];                                  // S[16 ct + 4 g4 + j][col]
@@ -215,7 +276,8 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 Sacc[ct][j] = S0 ? S0[((long)bh * DK + 16 * ct + 4 * g4 + j) * DV + col] : 0.f;
-        E *oh = o + (long)h * DV + col;
+        const int rso = H * DV * L::ES;                   // bytes between token rows of o
+        const int ovo = (4 * g4) * rso + l16 * L::ES;     // this lane's first o element in a chunk
 
         for (int c = 0; c < nchunks; ++c) {
             const int s = c % NS;
@@ -267,14 +329,14 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             lds_fence();
             if (lane == 0)
                 st_flag(done + s * 4 + w, c + 1);
-            // o rows of this chunk
+            // o rows of this chunk; rows past T fall outside the buffer and are dropped
             const int t0 = c * kC;
+            const int valid = T - t0 < kC ? T - t0 : kC;
+            const __amdgpu_buffer_rsrc_t ro =
+                buffer(o + ((tokb + t0) * H + h) * (long)DV + slice * kVS + 16 * w, (valid - 1) * rso + 16 * L::ES);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * g4 + j;
-                if (t0 + r < T)
-                    oh[((tokb + t0 + r) * H) * (long)DV] = from_f<E>(Y[j] + Z[j]);
-            }
+            for (int j = 0; j < 4; ++j)
+                store_scalar(ro, ovo, j * rso, Y[j] + Z[j], (E *)nullptr);
         }
         if (S_T) {
 #pragma unroll
@@ -292,54 +354,81 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
     E *pKc = reinterpret_cast<E *>(pscr);
     float *pA = reinterpret_cast<float *>(pscr + L::pBytesE);
     float *pBeta = pA + L::pBeta;
-    const E *qh = q + (long)h * DK, *kh = k + (long)h * DK, *gh = g + (long)h * DK;
-    const E *vh = v + (long)h * DV, *bh_ = beta + h;
-    const bool kch = 2 * lane < DK, vch = lane < kVS / 2;
-    const float kLog2e = 1.4426950408889634f;
+    const long hrow = (long)b * T * H + h;       // row of token 0 of this head
 
-    // bf16: one chunk of register prefetch (issued a whole producer round
-    // ahead); fp32 test mode loads on demand (its registers are twice as big)
-    constexpr bool kPrefetch = sizeof(E) == 2;
-    Raw<E> nxt;
-    if (kPrefetch && pw < nchunks) {
-        const int t0 = pw * kC;
-        load_raw<E, DK>(nxt, qh, kh, gh, vh, bh_, tokb + t0, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
-    }
-    for (int c = pw; c < nchunks; c += 4) {
-        Raw<E> cur;
-        if (kPrefetch) {
-            cur = nxt;
-            if (c + 4 < nchunks) {
-                const int t1 = (c + 4) * kC;
-                load_raw<E, DK>(nxt, qh, kh, gh, vh, bh_, tokb + t1, T - t1 < kC ? T - t1 : kC, H, DV, slice, lane);
-            }
-        } else {
-            const int t0 = c * kC;
-            load_raw<E, DK>(cur, qh, kh, gh, vh, bh_, tokb + t0, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
-        }
+    auto load = [&](RawV<E, DK> &R, int c) {
+        const int t0 = c * kC;
+        load_raw<E, DK>(R, q, k, g, v, beta, hrow + (long)t0 * H, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
+    };
+
+    // One chunk from raw registers to a published slot; reloads the registers
+    // with this producer's next chunk (c + 4) as soon as they are staged.
+    auto produce = [&](RawV<E, DK> &raw, int c) {
+        typedef RawV<E, DK> RV;
         const int s = c % NS;
         if (c >= NS)
             wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
         E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
         float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
 
+        // ---- stage the raw rows in LDS: q -> Qt area, k -> Kt area, g -> the Kc
+        // scratch, v -> the Ke^T area (each is overwritten below only after the
+        // same lane has read its own elements back) -------------------------------
+        {
+            const int rr = lane / RV::VPR, cc = (lane % RV::VPR) * (16 / L::ES);
+#pragma unroll
+            for (int i = 0; i < RV::NL; ++i) {
+                const int r = i * RV::TPI + rr;
+                *reinterpret_cast<uint4 *>(sl + L::eQt + r * L::LDK + cc) = raw.q[i];
+                *reinterpret_cast<uint4 *>(sl + L::eKt + r * L::LDK + cc) = raw.k[i];
+                *reinterpret_cast<uint4 *>(pKc + r * L::LDK + cc) = raw.g[i];
+            }
+            const int rv = lane / RV::VPRV, cv = (lane % RV::VPRV) * (16 / L::ES);
+#pragma unroll
+            for (int i = 0; i < RV::NLV; ++i)
+                *reinterpret_cast<uint4 *>(sl + L::eKeT + (i * RV::TPIV + rv) * kVS + cv) = raw.v[i];
+        }
+        // beta is still in raw: park it in LDS before the registers are reused
+        pBeta[lane & 15] = bits_to_f(raw.b, (E *)nullptr);
+        lds_fence();
+        // the raw registers are free again: fetch this producer's next chunk now,
+        // a whole chunk of work ahead of its use
+        if (c + 4 < nchunks)
+            load(raw, c + 4);
+        // From here on lane l works on key channels 2l, 2l+1 (and value columns
+        // 2l, 2l+1) across the 16 tokens, reading the staged rows back.
+        typedef typename PE::T PT;
+        // ---- V^T rows and beta (value columns 2l, 2l+1 for lanes < 32) --------
+        // (all reads of a pass are issued before its writes: LDS latency overlaps
+        // instead of serialising on possible aliasing)
+        if (lane < kVS / 2) {
+            PT vr[kC];
+#pragma unroll
+            for (int r = 0; r < kC; ++r)
+                vr[r] = *reinterpret_cast<const PT *>(sl + L::eKeT + r * kVS + 2 * lane);
+            E *r0 = sl + L::eVT + (2 * lane) * L::LT;
+            E *r1 = r0 + L::LT;
+#pragma unroll
+            for (int r = 0; r < kC; r += 2) {
+                *reinterpret_cast<PT *>(r0 + r) = PE::los(vr[r], vr[r + 1]);
+                *reinterpret_cast<PT *>(r1 + r) = PE::his(vr[r], vr[r + 1]);
+            }
+        }
+
         // ---- decay factors by running products, then the operands ------------
-        if (kch) {
-            float a0[kC], a1[kC];
+        if (2 * lane < DK) {
+            PT gr[kC];
+#pragma unroll
+            for (int r = 0; r < kC; ++r)
+                gr[r] = *reinterpret_cast<const PT *>(pKc + r * L::LDK + 2 * lane);
+            float a0[kC], a1[kC];                         // alpha = e^g
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                a0[r] = __builtin_amdgcn_exp2f(PE::lo(cur.g[r]) * kLog2e);
-                a1[r] = __builtin_amdgcn_exp2f(PE::hi(cur.g[r]) * kLog2e);
+                a0[r] = __builtin_amdgcn_exp2f(PE::lo(gr[r]) * 1.4426950408889634f);
+                a1[r] = __builtin_amdgcn_exp2f(PE::hi(gr[r]) * 1.4426950408889634f);
             }
-            float P0[kC], P1[kC], Z0[kC], Z1[kC];       // prefix e^{G_r}, suffix e^{G_15 - G_r}
-            float p0 = 1.f, p1 = 1.f;
-#pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                p0 *= a0[r];
-                p1 *= a1[r];
-                P0[r] = p0;
-                P1[r] = p1;
-            }
+            // suffix products Z_r = e^{G_15 - G_r}; their total is Gam = e^{G_15}
+            float Z0[kC], Z1[kC];
             float z0 = 1.f, z1 = 1.f;
 #pragma unroll
             for (int r = kC - 1; r >= 0; --r) {
@@ -348,40 +437,39 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                 z0 *= a0[r];
                 z1 *= a1[r];
             }
-            const float ig0 = 1.f / p0, ig1 = 1.f / p1;  // 1 / Gam
-            *reinterpret_cast<float2 *>(gam + 2 * lane) = make_float2(p0, p1);
-            float ke0[kC], ke1[kC];
+            const float ig0 = __builtin_amdgcn_rcpf(z0), ig1 = __builtin_amdgcn_rcpf(z1);   // 1 / Gam
+            *reinterpret_cast<float2 *>(gam + 2 * lane) = make_float2(z0, z1);
+            PT kr[kC], qr[kC];
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                const float k0 = PE::lo(cur.k[r]), k1 = PE::hi(cur.k[r]);
-                const float q0 = PE::lo(cur.q[r]), q1 = PE::hi(cur.q[r]);
-                const float ip0 = Z0[r] * ig0, ip1 = Z1[r] * ig1;   // 1 / P_r
-                *reinterpret_cast<typename PE::T *>(sl + L::eKt + r * L::LDK + 2 * lane) = PE::pack(k0 * P0[r], k1 * P1[r]);
-                *reinterpret_cast<typename PE::T *>(sl + L::eQt + r * L::LDK + 2 * lane) = PE::pack(q0 * P0[r], q1 * P1[r]);
-                *reinterpret_cast<typename PE::T *>(pKc + r * L::LDK + 2 * lane) = PE::pack(k0 * ip0, k1 * ip1);
-                ke0[r] = k0 * Z0[r];          // Ke = k Gam / P = k * suffix product
-                ke1[r] = k1 * Z1[r];
+                kr[r] = *reinterpret_cast<const PT *>(sl + L::eKt + r * L::LDK + 2 * lane);
+                qr[r] = *reinterpret_cast<const PT *>(sl + L::eQt + r * L::LDK + 2 * lane);
             }
-            // channel-major rows: the 16 tokens of channel 2l, then of 2l+1
-            E *r0 = sl + L::eKeT + (2 * lane) * L::LT;
+            // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Ke = k Z, Kc = Ke / Gam = k / P
+            E *r0 = sl + L::eKeT + (2 * lane) * L::LT;   // channel-major rows of channels 2l, 2l+1
             E *r1 = r0 + L::LT;
+            float p0 = 1.f, p1 = 1.f, pe0 = 0.f, pe1 = 0.f;
 #pragma unroll
-            for (int r = 0; r < kC; r += 2) {
-                *reinterpret_cast<typename PE::T *>(r0 + r) = PE::pack(ke0[r], ke0[r + 1]);
-                *reinterpret_cast<typename PE::T *>(r1 + r) = PE::pack(ke1[r], ke1[r + 1]);
+            for (int r = 0; r < kC; ++r) {
+                p0 *= a0[r];
+                p1 *= a1[r];
+                PT *kt = reinterpret_cast<PT *>(sl + L::eKt + r * L::LDK + 2 * lane);
+                PT *qt = reinterpret_cast<PT *>(sl + L::eQt + r * L::LDK + 2 * lane);
+                PT *kc = reinterpret_cast<PT *>(pKc + r * L::LDK + 2 * lane);
+                const float k0 = PE::lo(kr[r]), k1 = PE::hi(kr[r]);
+                const float q0 = PE::lo(qr[r]), q1 = PE::hi(qr[r]);
+                const float e0 = k0 * Z0[r], e1 = k1 * Z1[r];
+                *kt = PE::pack(k0 * p0, k1 * p1);
+                *qt = PE::pack(q0 * p0, q1 * p1);
+                *kc = PE::pack(e0 * ig0, e1 * ig1);
+                if (r & 1) {
+                    *reinterpret_cast<PT *>(r0 + r - 1) = PE::pack(pe0, e0);
+                    *reinterpret_cast<PT *>(r1 + r - 1) = PE::pack(pe1, e1);
+                }
+                pe0 = e0;
+                pe1 = e1;
             }
         }
-        if (vch) {
-            E *r0 = sl + L::eVT + (2 * lane) * L::LT;
-            E *r1 = r0 + L::LT;
-#pragma unroll
-            for (int r = 0; r < kC; r += 2) {
-                *reinterpret_cast<typename PE::T *>(r0 + r) = PE::pack(PE::lo(cur.v[r]), PE::lo(cur.v[r + 1]));
-                *reinterpret_cast<typename PE::T *>(r1 + r) = PE::pack(PE::hi(cur.v[r]), PE::hi(cur.v[r + 1]));
-            }
-        }
-        if (lane < kC)
-            pBeta[lane] = to_f(cur.b);
         lds_fence();
 
         // ---- A and M on MFMA (contraction over the DK channels) ----------------
@@ -424,6 +512,9 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                             acc -= a4[e] * x[4 * i4 + e];
                 }
                 x[r] = acc;
+                // keep at most four rows of A in flight (register budget)
+                if ((r & 3) == 3)
+                    __builtin_amdgcn_sched_barrier(0);
             }
             const float bj = pBeta[j];
 #pragma unroll
@@ -436,7 +527,13 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         lds_fence();
         if (lane == 0)
             st_flag(ready + s, c + 1);
-    }
+    };
+
+    RawV<E, DK> raw;
+    if (pw < nchunks)
+        load(raw, pw);
+    for (int c = pw; c < nchunks; c += 4)
+        produce(raw, c);
 }
 
 template <typename E, int DK>
