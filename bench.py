@@ -49,6 +49,27 @@ def decode_bytes(N, H, dk, dv, W=4):
     return N * H * (8 * dk * dv + 2 * nch + 2 * (W - 1) * nch + 2 * nch + 2 * dk + 2 + 2 * dv)
 
 
+def measured_traffic(profile, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
+    kernel sources have changed since the counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, "gated_delta_rule_18_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        with open(os.path.join(ROOT, "profiles", profile)) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    if h.hexdigest()[:16] not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes:"):
+            return int(line.split(":")[1])
+    return None
+
+
 def _timed(fn, steps, warmup, torch):
     """W warmups, then K steps between synchronisations.  Returns (wall ms/step,
     mean kernel ms from events on the current stream)."""
@@ -107,6 +128,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run torch's device-to-device copy of MIB MiB, --steps times "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -119,6 +143,16 @@ def main():
     from gated_delta_rule_18_amd.inputs import DECODE, WORKLOADS, decode_state, decode_step_inputs, prefill_inputs
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n,
+                          "launches": args.steps}), flush=True)
+        return
     binding.lib()
 
     # ---------------- prefill --------------------------------------------------
@@ -167,7 +201,9 @@ def main():
             "tokens_per_s": ds.N / (d_wall * 1e-3),
             "gbps": d_gbps,
             "roofline": {"bound": "hbm", "achieved": d_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": d_gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "frac": d_gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("decode_n256_hbm_counters.txt",
+                                                     ["kda_decode.hip", "kda_device.h"]),
                          "bytes_per_launch": d_bytes},
         }
         del st, steps_in
@@ -192,7 +228,11 @@ def main():
         "tflops": p_tflops,
         "mfma_frac": p_tflops / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": p_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": p_gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": p_bytes},
+                     "frac": p_gbps / HBM_PEAK_GBPS,
+                     "traffic": (measured_traffic("prefill_k3_hbm_counters.txt",
+                                                  ["kda_prefill_ws.hip", "kda_device.h"])
+                                 if C == 16 else None),
+                     "bytes_per_launch": p_bytes},
         "decode": decode,
     }
     if cpu is not None:
