@@ -49,24 +49,37 @@ constexpr int kVS = 64;                // value columns per workgroup
 constexpr int kXCDs = 8;
 constexpr int kSpinLimit = 1 << 22;
 
+// LDS layout.  Every MFMA operand is stored as the register image the reading
+// wavefront loads (one contiguous 16- or 8-byte piece per lane), padded so that
+// both the producer's writes and the consumers' reads are free of bank
+// conflicts (64 banks of 4 bytes):
+//   image16 (Kt, Qt, Kc): K-step m (32 channels), lane (l16 = token, g4):
+//       element e of 8 at  m*MS + g4*GS + 8*l16 + e, GS = 136, MS = 4*GS; the
+//       8 channels of (m, g4) are {32m + 4g4 + e} (e < 4) and {32m + 16 + 4g4 + e-4}
+//       -- the contraction order the state accumulators impose (see consumer);
+//   image4 (Ke^T, V^T): 16-row tile t, lane (l16 = channel or value, g4 =
+//       token group): element e of 4 at  t*KS + 4*(l16 + 16 g4) + e, KS = 320;
+//   T, M: lane (l16 = row, g4): element e of 4 at 4*(l16 + 16 g4) + e = the
+//       entry (row l16, column 4 g4 + e).
 template <typename E, int DK>
 struct WsL {
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int NS = ES == 2 ? 8 : 3;        // LDS slots
-    static constexpr int LDK = DK + 16 / ES;          // padded row of [16][DK]
-    static constexpr int LT = 16;                     // row of [*][16]
+    static constexpr int NS = ES == 2 ? 7 : 3;        // LDS slots
+    static constexpr int GS = 136, MS = 4 * GS;       // image16 strides (elements)
+    static constexpr int KS = 320;                    // image4 tile stride (elements)
+    static constexpr int NKS = DK / 32, NCT = DK / 16;
+    static constexpr int I16 = NKS * MS;              // elements of one image16
     // slot, E-typed part (element offsets)
-    static constexpr int eKt = 0;                     // Kt   [16][LDK]  token-major
-    static constexpr int eQt = eKt + kC * LDK;        // Qt   [16][LDK]
-    static constexpr int eKeT = eQt + kC * LDK;       // Ke^T [DK][16]   channel-major
-    static constexpr int eVT = eKeT + DK * LT;        // V^T  [64][16]
-    static constexpr int eT = eVT + kVS * LT;         // T    [16][16]
-    static constexpr int eM = eT + kC * LT;           // M    [16][16]
-    static constexpr int slotE = eM + kC * LT;
+    static constexpr int eKt = 0;                     // Kt image16 (raw k staged here first)
+    static constexpr int eQt = eKt + I16;             // Qt image16 (raw q staged here first)
+    static constexpr int eKe = eQt + I16;             // Ke^T image4, NCT tiles (raw v staged here first)
+    static constexpr int eV = eKe + NCT * KS;         // V^T image4, 4 tiles
+    static constexpr int eT = eV + 4 * KS;            // T  [64 lanes][4]
+    static constexpr int eM = eT + 256;               // M  [64 lanes][4]
+    static constexpr int slotE = eM + 256;
     static constexpr int slotBytes = slotE * ES + DK * 4;   // + Gam fp32 [DK]
-    // producer scratch
-    static constexpr int pKc = 0;                     // Kc [16][LDK] token-major (E)
-    static constexpr int pBytesE = kC * LDK * ES;
+    // producer scratch: Kc image16 (raw g staged here first), A, beta
+    static constexpr int pBytesE = I16 * ES;
     static constexpr int LA = 20;                     // row of A (16-byte aligned)
     static constexpr int pA = 0;                      // A  [16][LA] fp32
     static constexpr int pBeta = 16 * LA;             // beta [16] fp32
@@ -78,6 +91,13 @@ struct WsL {
     static constexpr int nFlags = NS + NS * 4 + 1;    // ready[NS], done[NS][4], abort
     static constexpr int bytes = oFlags + nFlags * 4;
     static_assert(slotBytes % 16 == 0 && pBytesE % 16 == 0 && pBytes % 16 == 0, "alignment");
+    static_assert(kC * DK <= I16 && kC * kVS <= NCT * KS, "staging fits the images");
+    // image16 position of (token r, channel c)
+    static __device__ __forceinline__ int img16(int r, int c)
+    {
+        const int m = c >> 5, cp = c & 31, hf = cp >> 4, cq = cp & 15;
+        return m * MS + (cq >> 2) * GS + 8 * r + (cq & 3) + 4 * hf;
+    }
 };
 
 __device__ __forceinline__ void lds_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); }
@@ -167,6 +187,17 @@ __device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff,
 __device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, float *)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+
+// Four packs (8 elements) stored contiguously.
+__device__ __forceinline__ void st_quad(__bf16 *d, unsigned a, unsigned b, unsigned c, unsigned e)
+{
+    *reinterpret_cast<uint4 *>(d) = make_uint4(a, b, c, e);
+}
+__device__ __forceinline__ void st_quad(float *d, float2 a, float2 b, float2 c, float2 e)
+{
+    reinterpret_cast<float4 *>(d)[0] = make_float4(a.x, a.y, b.x, b.y);
+    reinterpret_cast<float4 *>(d)[1] = make_float4(c.x, c.y, e.x, e.y);
 }
 
 // Raw buffer over [base, base + bytes): loads past the end return 0 and stores
@@ -293,32 +324,30 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             const float *gam = reinterpret_cast<const float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
 
             f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-            const E *kt = sl + L::eKt + l16 * L::LDK + 4 * g4;
-            const E *qt = sl + L::eQt + l16 * L::LDK + 4 * g4;
+            const E *kt = sl + L::eKt + g4 * L::GS + 8 * l16;
+            const E *qt = sl + L::eQt + g4 * L::GS + 8 * l16;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                const V8 a = cat8(*reinterpret_cast<const V4 *>(kt + 32 * m),
-                                  *reinterpret_cast<const V4 *>(kt + 32 * m + 16));
-                const V8 aq = cat8(*reinterpret_cast<const V4 *>(qt + 32 * m),
-                                   *reinterpret_cast<const V4 *>(qt + 32 * m + 16));
+                const V8 a = *reinterpret_cast<const V8 *>(kt + m * L::MS);
+                const V8 aq = *reinterpret_cast<const V8 *>(qt + m * L::MS);
                 X = mma32(a, Bs[m], X);
                 Y = mma32(aq, Bs[m], Y);
             }
             // X <- V - Kt S   (rows 4 g4 + j = tokens, column l16)
-            const V4 vv = *reinterpret_cast<const V4 *>(sl + L::eVT + (16 * w + l16) * L::LT + 4 * g4);
+            const V4 vv = *reinterpret_cast<const V4 *>(sl + L::eV + w * L::KS + 4 * lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 X[j] = to_f(vv[j]) - X[j];
             // U = T X, then O = Y + M U   (contraction over tokens 4 g4 + e)
-            const V4 tr = *reinterpret_cast<const V4 *>(sl + L::eT + l16 * L::LT + 4 * g4);
+            const V4 tr = *reinterpret_cast<const V4 *>(sl + L::eT + 4 * lane);
             const f32x4 U = mma16(tr, cvt4<E>(X), f32x4{0.f, 0.f, 0.f, 0.f});
             const V4 bu = cvt4<E>(U);
-            const V4 mr = *reinterpret_cast<const V4 *>(sl + L::eM + l16 * L::LT + 4 * g4);
+            const V4 mr = *reinterpret_cast<const V4 *>(sl + L::eM + 4 * lane);
             const f32x4 Z = mma16(mr, bu, f32x4{0.f, 0.f, 0.f, 0.f});
             // S <- Gam S + Ke^T U
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const V4 kr = *reinterpret_cast<const V4 *>(sl + L::eKeT + (16 * ct + l16) * L::LT + 4 * g4);
+                const V4 kr = *reinterpret_cast<const V4 *>(sl + L::eKe + ct * L::KS + 4 * lane);
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 16 * ct + 4 * g4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -371,22 +400,21 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
         float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
 
-        // ---- stage the raw rows in LDS: q -> Qt area, k -> Kt area, g -> the Kc
-        // scratch, v -> the Ke^T area (each is overwritten below only after the
-        // same lane has read its own elements back) -------------------------------
+        // ---- stage the raw rows in LDS, unpadded row-major: q -> Qt area, k -> Kt
+        // area, g -> the Kc scratch, v -> the Ke^T area -----------------------------
         {
             const int rr = lane / RV::VPR, cc = (lane % RV::VPR) * (16 / L::ES);
 #pragma unroll
             for (int i = 0; i < RV::NL; ++i) {
                 const int r = i * RV::TPI + rr;
-                *reinterpret_cast<uint4 *>(sl + L::eQt + r * L::LDK + cc) = raw.q[i];
-                *reinterpret_cast<uint4 *>(sl + L::eKt + r * L::LDK + cc) = raw.k[i];
-                *reinterpret_cast<uint4 *>(pKc + r * L::LDK + cc) = raw.g[i];
+                *reinterpret_cast<uint4 *>(sl + L::eQt + r * DK + cc) = raw.q[i];
+                *reinterpret_cast<uint4 *>(sl + L::eKt + r * DK + cc) = raw.k[i];
+                *reinterpret_cast<uint4 *>(pKc + r * DK + cc) = raw.g[i];
             }
             const int rv = lane / RV::VPRV, cv = (lane % RV::VPRV) * (16 / L::ES);
 #pragma unroll
             for (int i = 0; i < RV::NLV; ++i)
-                *reinterpret_cast<uint4 *>(sl + L::eKeT + (i * RV::TPIV + rv) * kVS + cv) = raw.v[i];
+                *reinterpret_cast<uint4 *>(sl + L::eKe + (i * RV::TPIV + rv) * kVS + cv) = raw.v[i];
         }
         // beta is still in raw: park it in LDS before the registers are reused
         pBeta[lane & 15] = bits_to_f(raw.b, (E *)nullptr);
@@ -396,31 +424,38 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         if (c + 4 < nchunks)
             load(raw, c + 4);
         // From here on lane l works on key channels 2l, 2l+1 (and value columns
-        // 2l, 2l+1) across the 16 tokens, reading the staged rows back.
+        // 2l, 2l+1) across the 16 tokens.  Every staged element is read back
+        // before any image is written: the images overwrite the staging areas.
         typedef typename PE::T PT;
-        // ---- V^T rows and beta (value columns 2l, 2l+1 for lanes < 32) --------
-        // (all reads of a pass are issued before its writes: LDS latency overlaps
-        // instead of serialising on possible aliasing)
+        PT vr[kC], gr[kC], kr[kC], qr[kC];
         if (lane < kVS / 2) {
-            PT vr[kC];
 #pragma unroll
             for (int r = 0; r < kC; ++r)
-                vr[r] = *reinterpret_cast<const PT *>(sl + L::eKeT + r * kVS + 2 * lane);
-            E *r0 = sl + L::eVT + (2 * lane) * L::LT;
-            E *r1 = r0 + L::LT;
+                vr[r] = *reinterpret_cast<const PT *>(sl + L::eKe + r * kVS + 2 * lane);
+        }
+        if (2 * lane < DK) {
 #pragma unroll
-            for (int r = 0; r < kC; r += 2) {
-                *reinterpret_cast<PT *>(r0 + r) = PE::los(vr[r], vr[r + 1]);
-                *reinterpret_cast<PT *>(r1 + r) = PE::his(vr[r], vr[r + 1]);
+            for (int r = 0; r < kC; ++r) {
+                gr[r] = *reinterpret_cast<const PT *>(pKc + r * DK + 2 * lane);
+                kr[r] = *reinterpret_cast<const PT *>(sl + L::eKt + r * DK + 2 * lane);
+                qr[r] = *reinterpret_cast<const PT *>(sl + L::eQt + r * DK + 2 * lane);
             }
+        }
+        lds_fence();
+        // image4 position of channel / value 2l for token group 0 (group tg adds 64)
+        const int i4 = ((2 * lane) >> 4) * L::KS + 4 * ((2 * lane) & 15);
+
+        // ---- V^T image (value columns 2l, 2l+1 for lanes < 32) -----------------
+        if (lane < kVS / 2) {
+#pragma unroll
+            for (int tg = 0; tg < kC / 4; ++tg)
+                st_quad(sl + L::eV + i4 + 64 * tg, PE::los(vr[4 * tg], vr[4 * tg + 1]),
+                        PE::los(vr[4 * tg + 2], vr[4 * tg + 3]), PE::his(vr[4 * tg], vr[4 * tg + 1]),
+                        PE::his(vr[4 * tg + 2], vr[4 * tg + 3]));
         }
 
         // ---- decay factors by running products, then the operands ------------
         if (2 * lane < DK) {
-            PT gr[kC];
-#pragma unroll
-            for (int r = 0; r < kC; ++r)
-                gr[r] = *reinterpret_cast<const PT *>(pKc + r * L::LDK + 2 * lane);
             float a0[kC], a1[kC];                         // alpha = e^g
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
@@ -439,60 +474,49 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             }
             const float ig0 = __builtin_amdgcn_rcpf(z0), ig1 = __builtin_amdgcn_rcpf(z1);   // 1 / Gam
             *reinterpret_cast<float2 *>(gam + 2 * lane) = make_float2(z0, z1);
-            PT kr[kC], qr[kC];
-#pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                kr[r] = *reinterpret_cast<const PT *>(sl + L::eKt + r * L::LDK + 2 * lane);
-                qr[r] = *reinterpret_cast<const PT *>(sl + L::eQt + r * L::LDK + 2 * lane);
-            }
             // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Ke = k Z, Kc = Ke / Gam = k / P
-            E *r0 = sl + L::eKeT + (2 * lane) * L::LT;   // channel-major rows of channels 2l, 2l+1
-            E *r1 = r0 + L::LT;
-            float p0 = 1.f, p1 = 1.f, pe0 = 0.f, pe1 = 0.f;
+            const int io = L::img16(0, 2 * lane);         // token r adds 8 r
+            float p0 = 1.f, p1 = 1.f, e0s[4], e1s[4];
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
                 p0 *= a0[r];
                 p1 *= a1[r];
-                PT *kt = reinterpret_cast<PT *>(sl + L::eKt + r * L::LDK + 2 * lane);
-                PT *qt = reinterpret_cast<PT *>(sl + L::eQt + r * L::LDK + 2 * lane);
-                PT *kc = reinterpret_cast<PT *>(pKc + r * L::LDK + 2 * lane);
                 const float k0 = PE::lo(kr[r]), k1 = PE::hi(kr[r]);
                 const float q0 = PE::lo(qr[r]), q1 = PE::hi(qr[r]);
                 const float e0 = k0 * Z0[r], e1 = k1 * Z1[r];
-                *kt = PE::pack(k0 * p0, k1 * p1);
-                *qt = PE::pack(q0 * p0, q1 * p1);
-                *kc = PE::pack(e0 * ig0, e1 * ig1);
-                if (r & 1) {
-                    *reinterpret_cast<PT *>(r0 + r - 1) = PE::pack(pe0, e0);
-                    *reinterpret_cast<PT *>(r1 + r - 1) = PE::pack(pe1, e1);
-                }
-                pe0 = e0;
-                pe1 = e1;
+                *reinterpret_cast<PT *>(sl + L::eKt + io + 8 * r) = PE::pack(k0 * p0, k1 * p1);
+                *reinterpret_cast<PT *>(sl + L::eQt + io + 8 * r) = PE::pack(q0 * p0, q1 * p1);
+                *reinterpret_cast<PT *>(pKc + io + 8 * r) = PE::pack(e0 * ig0, e1 * ig1);
+                e0s[r & 3] = e0;
+                e1s[r & 3] = e1;
+                if ((r & 3) == 3)
+                    st_quad(sl + L::eKe + i4 + 64 * (r >> 2), PE::pack(e0s[0], e0s[1]), PE::pack(e0s[2], e0s[3]),
+                            PE::pack(e1s[0], e1s[1]), PE::pack(e1s[2], e1s[3]));
             }
         }
         lds_fence();
 
         // ---- A and M on MFMA (contraction over the DK channels) ----------------
         {
-            f32x4 Aacc = {0.f, 0.f, 0.f, 0.f}, Macc = {0.f, 0.f, 0.f, 0.f};
-            const E *kt = sl + L::eKt + l16 * L::LDK + 8 * g4;
-            const E *qt = sl + L::eQt + l16 * L::LDK + 8 * g4;
-            const E *kc = pKc + l16 * L::LDK + 8 * g4;
+            f32x4 Aacc = {0.f, 0.f, 0.f, 0.f}, Mtr = {0.f, 0.f, 0.f, 0.f};
+            const int ia = g4 * L::GS + 8 * l16;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                const V8 ak = cat8(*reinterpret_cast<const V4 *>(kt + 32 * m), *reinterpret_cast<const V4 *>(kt + 32 * m + 4));
-                const V8 aq = cat8(*reinterpret_cast<const V4 *>(qt + 32 * m), *reinterpret_cast<const V4 *>(qt + 32 * m + 4));
-                const V8 bc = cat8(*reinterpret_cast<const V4 *>(kc + 32 * m), *reinterpret_cast<const V4 *>(kc + 32 * m + 4));
-                Aacc = mma32(ak, bc, Aacc);
-                Macc = mma32(aq, bc, Macc);
+                const V8 ak = *reinterpret_cast<const V8 *>(sl + L::eKt + ia + m * L::MS);
+                const V8 aq = *reinterpret_cast<const V8 *>(sl + L::eQt + ia + m * L::MS);
+                const V8 bc = *reinterpret_cast<const V8 *>(pKc + ia + m * L::MS);
+                Aacc = mma32(ak, bc, Aacc);     // A: rows (Kt tokens) 4 g4 + j, column l16
+                Mtr = mma32(bc, aq, Mtr);       // M^T: rows (Kc tokens) 4 g4 + j, column l16
             }
-            // lane holds rows 4 g4 + j, column l16
+            // M^T's accumulator is already M's image: entry (row l16, column 4 g4 + j)
+            f32x4 Mm;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j, i = l16;
                 pA[r * L::LA + i] = i < r ? pBeta[r] * Aacc[j] : 0.f;
-                sl[L::eM + r * L::LT + i] = from_f<E>(i <= r ? Macc[j] : 0.f);
+                Mm[j] = r <= i ? Mtr[j] : 0.f;
             }
+            *reinterpret_cast<V4 *>(sl + L::eM + 4 * lane) = cvt4<E>(Mm);
         }
         lds_fence();
 
@@ -520,7 +544,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * g4 + e;
-                sl[L::eT + r * L::LT + j] = from_f<E>(x[r] * bj);
+                sl[L::eT + 4 * (r + 16 * (j >> 2)) + (j & 3)] = from_f<E>(x[r] * bj);
             }
         }
         // publish the slot
