@@ -28,12 +28,14 @@
 //                      dk x 64 fp32 state in MFMA accumulators for the whole
 //                      sequence and runs the state-dependent products of every
 //                      chunk in order; o goes straight to HBM;
-//   producers 4..7  -- producer p owns chunks p, p+4, p+8, ...: it loads them
-//                      (one chunk of prefetch in registers), builds the decayed
-//                      operands with in-register running products (lane = two
-//                      key channels, registers = the 16 tokens), forms A and M
-//                      on MFMA, inverts I + A by forward substitution and
-//                      publishes everything in a ring of NS LDS slots.
+//   producers 4..7  -- producer p owns chunks p, p+4, p+8, ...: it loads q, k,
+//                      g, v directly in its compute layout (lane = two key
+//                      channels, registers = the 16 tokens; two chunks in
+//                      flight), builds the decayed operands with in-register
+//                      running products, forms A and M on MFMA, inverts I + A by
+//                      forward substitution with A's entries read out of the
+//                      accumulators as wave-uniform operands, and publishes the
+//                      consumers' operands in a ring of NS LDS slots.
 // Producers and consumers hand slots over through per-slot LDS flags ("ready"
 // and per-consumer "done"); every wait is bounded and a WG-wide abort flag ends
 // all waits if one ever runs out (the result is then wrong, never a hang).
@@ -48,6 +50,8 @@ constexpr int kC = 16;                 // tokens per chunk
 constexpr int kVS = 64;                // value columns per workgroup
 constexpr int kXCDs = 8;
 constexpr int kSpinLimit = 1 << 22;
+// s_waitcnt operand: vector-memory count 0, the other counters unconstrained
+constexpr int kVmcntZero = 0x0F70;
 
 // LDS layout.  Every MFMA operand is stored as the register image the reading
 // wavefront loads (one contiguous 16- or 8-byte piece per lane), padded so that
@@ -64,34 +68,28 @@ constexpr int kSpinLimit = 1 << 22;
 template <typename E, int DK>
 struct WsL {
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int NS = ES == 2 ? 7 : 3;        // LDS slots
+    static constexpr int NS = ES == 2 ? 8 : 3;        // LDS slots
     static constexpr int GS = 136, MS = 4 * GS;       // image16 strides (elements)
     static constexpr int KS = 320;                    // image4 tile stride (elements)
     static constexpr int NKS = DK / 32, NCT = DK / 16;
     static constexpr int I16 = NKS * MS;              // elements of one image16
     // slot, E-typed part (element offsets)
-    static constexpr int eKt = 0;                     // Kt image16 (raw k staged here first)
-    static constexpr int eQt = eKt + I16;             // Qt image16 (raw q staged here first)
-    static constexpr int eKe = eQt + I16;             // Ke^T image4, NCT tiles (raw v staged here first)
+    static constexpr int eKt = 0;                     // Kt image16
+    static constexpr int eQt = eKt + I16;             // Qt image16
+    static constexpr int eKe = eQt + I16;             // Ke^T image4, NCT tiles
     static constexpr int eV = eKe + NCT * KS;         // V^T image4, 4 tiles
     static constexpr int eT = eV + 4 * KS;            // T  [64 lanes][4]
     static constexpr int eM = eT + 256;               // M  [64 lanes][4]
     static constexpr int slotE = eM + 256;
     static constexpr int slotBytes = slotE * ES + DK * 4;   // + Gam fp32 [DK]
-    // producer scratch: Kc image16 (raw g staged here first), A, beta
-    static constexpr int pBytesE = I16 * ES;
-    static constexpr int LA = 20;                     // row of A (16-byte aligned)
-    static constexpr int pA = 0;                      // A  [16][LA] fp32
-    static constexpr int pBeta = 16 * LA;             // beta [16] fp32
-    static constexpr int pBytes = pBytesE + (pBeta + 16) * 4;
+    static constexpr int pBytes = I16 * ES;           // producer scratch: Kc image16
     // byte offsets
     static constexpr int oSlots = 0;
     static constexpr int oProd = oSlots + NS * slotBytes;
     static constexpr int oFlags = oProd + 4 * pBytes;
     static constexpr int nFlags = NS + NS * 4 + 1;    // ready[NS], done[NS][4], abort
     static constexpr int bytes = oFlags + nFlags * 4;
-    static_assert(slotBytes % 16 == 0 && pBytesE % 16 == 0 && pBytes % 16 == 0, "alignment");
-    static_assert(kC * DK <= I16 && kC * kVS <= NCT * KS, "staging fits the images");
+    static_assert(slotBytes % 32 == 0 && pBytes % 32 == 0, "alignment");
     // image16 position of (token r, channel c)
     static __device__ __forceinline__ int img16(int r, int c)
     {
@@ -170,13 +168,13 @@ template <> struct Pair<float> {
 
 // A scalar element as raw bits (converted where it is used, so that no
 // instruction right after the load has to wait for it).
-__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, __bf16 *)
+__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, int soff, __bf16 *)
 {
-    return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+    return (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
-__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, float *)
+__device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, int soff, float *)
 {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 __device__ __forceinline__ float bits_to_f(unsigned x, __bf16 *) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bits_to_f(unsigned x, float *) { return __uint_as_float(x); }
@@ -200,6 +198,12 @@ __device__ __forceinline__ void st_quad(float *d, float2 a, float2 b, float2 c, 
     reinterpret_cast<float4 *>(d)[1] = make_float4(c.x, c.y, e.x, e.y);
 }
 
+// Bytes spanned by `rows` rows of `width` bytes, `stride` bytes apart (0 rows: 0).
+__device__ __forceinline__ int rows_bytes(int rows, int stride, int width)
+{
+    return rows > 0 ? (rows - 1) * stride + width : 0;
+}
+
 // Raw buffer over [base, base + bytes): loads past the end return 0 and stores
 // past the end are dropped, which masks a chunk's ragged tail without branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, int bytes)
@@ -207,55 +211,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, int b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// One chunk in the producer's compute layout: lane l holds key channels 2l,
-// 2l+1 of q, k, g (and value columns 2l, 2l+1) for the 16 tokens.
+// One chunk's raw inputs in the producer's compute layout, straight from HBM:
+// lane l holds key channels 2l, 2l+1 of g, k, q for each of the 16 tokens (one
+// coalesced pair load per token and tensor), value columns 2 (l % 32), +1 of
+// the slice for tokens 8 (l / 32) .. +7, and beta of token l & 15 as raw bits
+// (converted where used, so no instruction right after the loads waits):
+// 48 + 8 + 1 loads, within what the wave's outstanding-load counter tracks.
+// Tokens past the end read 0; a chunk past the end is an empty buffer, so the
+// loads are issued unconditionally (no branch for the wait-count analysis to
+// merge conservatively).
 template <typename E>
-struct Raw {
-    typename Pair<E>::T q[kC], k[kC], g[kC], v[kC];
-    float b;
-};
-
-// One chunk's raw inputs for one producer wave, as 16-byte vectors straight
-// from HBM (few, wide loads: the wave never has more outstanding loads than
-// its vmcnt counter can track).  q, k, g: load i of lane l is token
-// i * TPI + l / VPR, bytes 16 (l % VPR) .. of that token's head row; v the
-// same over the slice's 64 values; beta of token l for lanes < 16.  Tokens
-// past the end read 0.
-template <typename E, int DK>
-struct RawV {
-    static constexpr int ES = (int)sizeof(E);
-    static constexpr int VPR = DK * ES / 16, TPI = 64 / VPR, NL = kC / TPI;       // q, k, g
-    static constexpr int VPRV = kVS * ES / 16, TPIV = 64 / VPRV, NLV = kC / TPIV;  // v
-    uint4 q[NL], k[NL], g[NL], v[NLV];
-    unsigned b;          // beta of token (l & 15), raw bits
+struct RawC {
+    typename Pair<E>::T g[kC], k[kC], q[kC], v[kC / 2];
+    unsigned b;
 };
 
 template <typename E, int DK>
-__device__ __forceinline__ void load_raw(RawV<E, DK> &R, const E *q, const E *k, const E *g,
-                                         const E *v, const E *beta, long row0, int valid, int H,
-                                         int DV, int slice, int lane)
+__device__ __forceinline__ void load_chunk(RawC<E> &R, const E *q, const E *k, const E *g, const E *v,
+                                           const E *beta, long row0, int valid, int H, int DV, int slice,
+                                           int lane)
 {
-    typedef RawV<E, DK> RV;
-    constexpr int ES = RV::ES;
+    constexpr int ES = (int)sizeof(E);
     // row0 = (b T + t0) H + h: this head's row of the chunk's first token
-    const int rsk = H * DK * ES, rsv = H * DV * ES;
-    const __amdgpu_buffer_rsrc_t rq = buffer(q + row0 * DK, (valid - 1) * rsk + DK * ES);
-    const __amdgpu_buffer_rsrc_t rk = buffer(k + row0 * DK, (valid - 1) * rsk + DK * ES);
-    const __amdgpu_buffer_rsrc_t rg = buffer(g + row0 * DK, (valid - 1) * rsk + DK * ES);
-    const __amdgpu_buffer_rsrc_t rv = buffer(v + row0 * DV + slice * kVS, (valid - 1) * rsv + kVS * ES);
-    const __amdgpu_buffer_rsrc_t rb = buffer(beta + row0, (valid - 1) * H * ES + ES);
-    const int vo = (lane / RV::VPR) * rsk + (lane % RV::VPR) * 16;
-    const int vov = (lane / RV::VPRV) * rsv + (lane % RV::VPRV) * 16;
+    int rsk = H * DK * ES, rsv = H * DV * ES;
+    // recompute the per-token scalar offsets at every call instead of keeping
+    // them live across the whole loop (they would crowd out the SGPR file)
+    asm volatile("" : "+s"(rsk), "+s"(rsv));
+    const int nb = rows_bytes(valid, rsk, DK * ES);
+    const __amdgpu_buffer_rsrc_t rq = buffer(q + row0 * DK, nb);
+    const __amdgpu_buffer_rsrc_t rk = buffer(k + row0 * DK, nb);
+    const __amdgpu_buffer_rsrc_t rg = buffer(g + row0 * DK, nb);
+    const __amdgpu_buffer_rsrc_t rv = buffer(v + row0 * DV + slice * kVS, rows_bytes(valid, rsv, kVS * ES));
+    const __amdgpu_buffer_rsrc_t rb = buffer(beta + row0, rows_bytes(valid, H * ES, ES));
+    const int vo = lane * 2 * ES;
+    if (2 * lane < DK) {
 #pragma unroll
-    for (int i = 0; i < RV::NL; ++i) {
-        R.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, vo, i * RV::TPI * rsk, 0));
-        R.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, vo, i * RV::TPI * rsk, 0));
-        R.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, vo, i * RV::TPI * rsk, 0));
+        for (int r = 0; r < kC; ++r)
+            R.g[r] = Pair<E>::load(rg, vo, r * rsk);
+#pragma unroll
+        for (int r = 0; r < kC; ++r)
+            R.k[r] = Pair<E>::load(rk, vo, r * rsk);
+#pragma unroll
+        for (int r = 0; r < kC; ++r)
+            R.q[r] = Pair<E>::load(rq, vo, r * rsk);
     }
+    const int vov = (lane & 31) * 2 * ES + (lane >> 5) * (kC / 2) * rsv;
 #pragma unroll
-    for (int i = 0; i < RV::NLV; ++i)
-        R.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vov, i * RV::TPIV * rsv, 0));
-    R.b = load_bits(rb, (lane & 15) * H * ES, (E *)nullptr);
+    for (int i = 0; i < kC / 2; ++i)
+        R.v[i] = Pair<E>::load(rv, vov, i * rsv);
+    R.b = load_bits(rb, (lane & 15) * H * ES, 0, (E *)nullptr);
 }
 
 template <typename E, int DK>
@@ -307,8 +311,20 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 Sacc[ct][j] = S0 ? S0[((long)bh * DK + 16 * ct + 4 * g4 + j) * DV + col] : 0.f;
+        // drain the initial-state loads here: left pending into the loop, they
+        // make every chunk wait for all of its outstanding memory operations
+        // (the o stores included) before the state can be touched
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
         const int rso = H * DV * L::ES;                   // bytes between token rows of o
         const int ovo = (4 * g4) * rso + l16 * L::ES;     // this lane's first o element in a chunk
+        // buffer over this wave's 16 x 16 tile of o in chunk c; rows past T fall
+        // outside it and are dropped
+        auto tile = [&](const E *base, int c) {
+            const int t0 = c * kC;
+            const int valid = T - t0 < kC ? T - t0 : kC;
+            return buffer(base + ((tokb + t0) * H + h) * (long)DV + slice * kVS + 16 * w,
+                          rows_bytes(valid, rso, 16 * L::ES));
+        };
 
         for (int c = 0; c < nchunks; ++c) {
             const int s = c % NS;
@@ -358,11 +374,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             lds_fence();
             if (lane == 0)
                 st_flag(done + s * 4 + w, c + 1);
-            // o rows of this chunk; rows past T fall outside the buffer and are dropped
-            const int t0 = c * kC;
-            const int valid = T - t0 < kC ? T - t0 : kC;
-            const __amdgpu_buffer_rsrc_t ro =
-                buffer(o + ((tokb + t0) * H + h) * (long)DV + slice * kVS + 16 * w, (valid - 1) * rso + 16 * L::ES);
+            const __amdgpu_buffer_rsrc_t ro = tile(o, c);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 store_scalar(ro, ovo, j * rso, Y[j] + Z[j], (E *)nullptr);
@@ -379,88 +391,46 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 
     // ================================= producer =================================
     const int pw = wave - 4;
-    unsigned char *pscr = smem + L::oProd + pw * L::pBytes;
-    E *pKc = reinterpret_cast<E *>(pscr);
-    float *pA = reinterpret_cast<float *>(pscr + L::pBytesE);
-    float *pBeta = pA + L::pBeta;
+    E *pKc = reinterpret_cast<E *>(smem + L::oProd + pw * L::pBytes);
     const long hrow = (long)b * T * H + h;       // row of token 0 of this head
 
-    auto load = [&](RawV<E, DK> &R, int c) {
+    auto load = [&](RawC<E> &R, int c) {
         const int t0 = c * kC;
-        load_raw<E, DK>(R, q, k, g, v, beta, hrow + (long)t0 * H, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
+        load_chunk<E, DK>(R, q, k, g, v, beta, hrow + (long)t0 * H, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
     };
 
-    // One chunk from raw registers to a published slot; reloads the registers
-    // with this producer's next chunk (c + 4) as soon as they are staged.
-    auto produce = [&](RawV<E, DK> &raw, int c) {
-        typedef RawV<E, DK> RV;
+    // One chunk from raw registers to a published slot.
+    auto produce = [&](const RawC<E> &raw, int c) {
+        typedef typename PE::T PT;
         const int s = c % NS;
         if (c >= NS)
             wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
         E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
         float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
+        // lane coordinates re-derived per chunk: the masks and selects built from
+        // them below are cheap, and hoisting them all out of the loop would not
+        // fit the register files
+        int r16 = l16, rg4 = g4;
+        asm volatile("" : "+v"(r16), "+v"(rg4));
 
-        // ---- stage the raw rows in LDS, unpadded row-major: q -> Qt area, k -> Kt
-        // area, g -> the Kc scratch, v -> the Ke^T area -----------------------------
+        // ---- V^T image: lane (p, half) = (l % 32, l / 32) holds value columns
+        // 2p, 2p+1 for token groups 2 half, 2 half + 1 ------------------------------
         {
-            const int rr = lane / RV::VPR, cc = (lane % RV::VPR) * (16 / L::ES);
+            E *vt = sl + L::eV + ((2 * (lane & 31)) >> 4) * L::KS + 4 * ((2 * (lane & 31)) & 15) + 128 * (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < RV::NL; ++i) {
-                const int r = i * RV::TPI + rr;
-                *reinterpret_cast<uint4 *>(sl + L::eQt + r * DK + cc) = raw.q[i];
-                *reinterpret_cast<uint4 *>(sl + L::eKt + r * DK + cc) = raw.k[i];
-                *reinterpret_cast<uint4 *>(pKc + r * DK + cc) = raw.g[i];
-            }
-            const int rv = lane / RV::VPRV, cv = (lane % RV::VPRV) * (16 / L::ES);
-#pragma unroll
-            for (int i = 0; i < RV::NLV; ++i)
-                *reinterpret_cast<uint4 *>(sl + L::eKe + (i * RV::TPIV + rv) * kVS + cv) = raw.v[i];
-        }
-        // beta is still in raw: park it in LDS before the registers are reused
-        pBeta[lane & 15] = bits_to_f(raw.b, (E *)nullptr);
-        lds_fence();
-        // the raw registers are free again: fetch this producer's next chunk now,
-        // a whole chunk of work ahead of its use
-        if (c + 4 < nchunks)
-            load(raw, c + 4);
-        // From here on lane l works on key channels 2l, 2l+1 (and value columns
-        // 2l, 2l+1) across the 16 tokens.  Every staged element is read back
-        // before any image is written: the images overwrite the staging areas.
-        typedef typename PE::T PT;
-        PT vr[kC], gr[kC], kr[kC], qr[kC];
-        if (lane < kVS / 2) {
-#pragma unroll
-            for (int r = 0; r < kC; ++r)
-                vr[r] = *reinterpret_cast<const PT *>(sl + L::eKe + r * kVS + 2 * lane);
-        }
-        if (2 * lane < DK) {
-#pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                gr[r] = *reinterpret_cast<const PT *>(pKc + r * DK + 2 * lane);
-                kr[r] = *reinterpret_cast<const PT *>(sl + L::eKt + r * DK + 2 * lane);
-                qr[r] = *reinterpret_cast<const PT *>(sl + L::eQt + r * DK + 2 * lane);
-            }
-        }
-        lds_fence();
-        // image4 position of channel / value 2l for token group 0 (group tg adds 64)
-        const int i4 = ((2 * lane) >> 4) * L::KS + 4 * ((2 * lane) & 15);
-
-        // ---- V^T image (value columns 2l, 2l+1 for lanes < 32) -----------------
-        if (lane < kVS / 2) {
-#pragma unroll
-            for (int tg = 0; tg < kC / 4; ++tg)
-                st_quad(sl + L::eV + i4 + 64 * tg, PE::los(vr[4 * tg], vr[4 * tg + 1]),
-                        PE::los(vr[4 * tg + 2], vr[4 * tg + 3]), PE::his(vr[4 * tg], vr[4 * tg + 1]),
-                        PE::his(vr[4 * tg + 2], vr[4 * tg + 3]));
+            for (int u = 0; u < 2; ++u)
+                st_quad(vt + 64 * u, PE::los(raw.v[4 * u], raw.v[4 * u + 1]), PE::los(raw.v[4 * u + 2], raw.v[4 * u + 3]),
+                        PE::his(raw.v[4 * u], raw.v[4 * u + 1]), PE::his(raw.v[4 * u + 2], raw.v[4 * u + 3]));
         }
 
         // ---- decay factors by running products, then the operands ------------
+        // (lane l: key channels 2l, 2l+1 across the 16 tokens)
         if (2 * lane < DK) {
             float a0[kC], a1[kC];                         // alpha = e^g
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                a0[r] = __builtin_amdgcn_exp2f(PE::lo(gr[r]) * 1.4426950408889634f);
-                a1[r] = __builtin_amdgcn_exp2f(PE::hi(gr[r]) * 1.4426950408889634f);
+                a0[r] = __builtin_amdgcn_exp2f(PE::lo(raw.g[r]) * 1.4426950408889634f);
+                a1[r] = __builtin_amdgcn_exp2f(PE::hi(raw.g[r]) * 1.4426950408889634f);
             }
             // suffix products Z_r = e^{G_15 - G_r}; their total is Gam = e^{G_15}
             float Z0[kC], Z1[kC];
@@ -476,13 +446,14 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             *reinterpret_cast<float2 *>(gam + 2 * lane) = make_float2(z0, z1);
             // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Ke = k Z, Kc = Ke / Gam = k / P
             const int io = L::img16(0, 2 * lane);         // token r adds 8 r
+            E *ke = sl + L::eKe + ((2 * lane) >> 4) * L::KS + 4 * ((2 * lane) & 15);   // token group tg adds 64 tg
             float p0 = 1.f, p1 = 1.f, e0s[4], e1s[4];
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
                 p0 *= a0[r];
                 p1 *= a1[r];
-                const float k0 = PE::lo(kr[r]), k1 = PE::hi(kr[r]);
-                const float q0 = PE::lo(qr[r]), q1 = PE::hi(qr[r]);
+                const float k0 = PE::lo(raw.k[r]), k1 = PE::hi(raw.k[r]);
+                const float q0 = PE::lo(raw.q[r]), q1 = PE::hi(raw.q[r]);
                 const float e0 = k0 * Z0[r], e1 = k1 * Z1[r];
                 *reinterpret_cast<PT *>(sl + L::eKt + io + 8 * r) = PE::pack(k0 * p0, k1 * p1);
                 *reinterpret_cast<PT *>(sl + L::eQt + io + 8 * r) = PE::pack(q0 * p0, q1 * p1);
@@ -490,62 +461,69 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                 e0s[r & 3] = e0;
                 e1s[r & 3] = e1;
                 if ((r & 3) == 3)
-                    st_quad(sl + L::eKe + i4 + 64 * (r >> 2), PE::pack(e0s[0], e0s[1]), PE::pack(e0s[2], e0s[3]),
+                    st_quad(ke + 64 * (r >> 2), PE::pack(e0s[0], e0s[1]), PE::pack(e0s[2], e0s[3]),
                             PE::pack(e1s[0], e1s[1]), PE::pack(e1s[2], e1s[3]));
             }
         }
         lds_fence();
 
         // ---- A and M on MFMA (contraction over the DK channels) ----------------
+        f32x4 ATr = {0.f, 0.f, 0.f, 0.f}, Mtr = {0.f, 0.f, 0.f, 0.f};
         {
-            f32x4 Aacc = {0.f, 0.f, 0.f, 0.f}, Mtr = {0.f, 0.f, 0.f, 0.f};
             const int ia = g4 * L::GS + 8 * l16;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
                 const V8 ak = *reinterpret_cast<const V8 *>(sl + L::eKt + ia + m * L::MS);
                 const V8 aq = *reinterpret_cast<const V8 *>(sl + L::eQt + ia + m * L::MS);
                 const V8 bc = *reinterpret_cast<const V8 *>(pKc + ia + m * L::MS);
-                Aacc = mma32(ak, bc, Aacc);     // A: rows (Kt tokens) 4 g4 + j, column l16
-                Mtr = mma32(bc, aq, Mtr);       // M^T: rows (Kc tokens) 4 g4 + j, column l16
+                ATr = mma32(bc, ak, ATr);       // <Kc_i, Kt_r>: rows i = 4 g4 + j, column r = l16
+                Mtr = mma32(bc, aq, Mtr);       // <Kc_i, Qt_r>: rows i = 4 g4 + j, column r = l16
             }
-            // M^T's accumulator is already M's image: entry (row l16, column 4 g4 + j)
+            // M^T's accumulator is already M's image: entry (row l16, column 4 g4 + j),
+            // kept where column <= row
             f32x4 Mm;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * g4 + j, i = l16;
-                pA[r * L::LA + i] = i < r ? pBeta[r] * Aacc[j] : 0.f;
-                Mm[j] = r <= i ? Mtr[j] : 0.f;
-            }
+            for (int j = 0; j < 4; ++j)
+                Mm[j] = 4 * rg4 + j <= r16 ? Mtr[j] : 0.f;
             *reinterpret_cast<V4 *>(sl + L::eM + 4 * lane) = cvt4<E>(Mm);
         }
-        lds_fence();
 
-        // ---- T = (I + A)^{-1} Diag(beta): forward substitution, lane = column l16
+        // ---- T = (I + A)^{-1} Diag(beta), A[r][i] = beta_r <Kt_r, Kc_i> (i < r) ----
+        // A is strictly lower triangular, so A^16 = 0 and, exactly,
+        //   (I + A)^{-1} = sum_k (-A)^k = (I - A)(I + A^2)(I + A^4)(I + A^8).
+        // Evaluated on fp32 MFMA with every 16 x 16 matrix in the accumulator
+        // layout (lane (n, g) holds rows 4g .. 4g+3 of column n).  mul(Xt, Y)
+        // forms X Y from X^T and Y in that layout: the contraction index of step
+        // s in lane group g is 4g + s, which is element s of both operands.  A
+        // transposed product needs no data movement: (XY)^T = mul(Y, X^T) from
+        // the same registers.
         {
-            const int j = l16;
-            float x[kC];
+            auto mul = [](f32x4 xt, f32x4 y) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                float acc = (r == j) ? 1.f : 0.f;
+                for (int st = 0; st < 4; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[st], y[st], acc, 0, 0, 0);
+                return acc;
+            };
+            const float bl = bits_to_f(raw.b, (E *)nullptr);      // beta of token l16
+            f32x4 I4, AT;
 #pragma unroll
-                for (int i4 = 0; i4 < (r + 3) / 4; ++i4) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(pA + r * L::LA + 4 * i4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * i4 + e < r)
-                            acc -= a4[e] * x[4 * i4 + e];
-                }
-                x[r] = acc;
-                // keep at most four rows of A in flight (register budget)
-                if ((r & 3) == 3)
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) {
+                I4[j] = 4 * rg4 + j == r16 ? 1.f : 0.f;
+                // A^T[4g + j][l16] = A[l16][4g + j] = beta_l16 <Kt_l16, Kc_4g+j>, kept below the diagonal of A
+                AT[j] = 4 * rg4 + j < r16 ? bl * ATr[j] : 0.f;
             }
-            const float bj = pBeta[j];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g4 + e;
-                sl[L::eT + 4 * (r + 16 * (j >> 2)) + (j & 3)] = from_f<E>(x[r] * bj);
-            }
+            const f32x4 A1 = mul(AT, I4);                 // A
+            const f32x4 A2 = mul(AT, A1), A2T = mul(A1, AT);
+            const f32x4 A4 = mul(A2T, A2), A4T = mul(A2, A2T);
+            const f32x4 A8 = mul(A4T, A4);
+            const f32x4 W = I4 + A4 + A8 + mul(A4T, A8);  // (I + A^4)(I + A^8)
+            const f32x4 W2 = W + mul(A2T, W);             // (I + A^2) W
+            const f32x4 Li = W2 - mul(AT, W2);            // (I - A) W2 = (I + A)^{-1}
+            // T = Li Diag(beta): column l16 scales by beta_l16.  The consumers take
+            // T as an MFMA A operand, whose image is T^T in the accumulator layout.
+            const f32x4 TT = mul(Li * bl, I4);
+            *reinterpret_cast<V4 *>(sl + L::eT + 4 * lane) = cvt4<E>(TT);
         }
         // publish the slot
         lds_fence();
@@ -553,11 +531,18 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             st_flag(ready + s, c + 1);
     };
 
-    RawV<E, DK> raw;
-    if (pw < nchunks)
-        load(raw, pw);
-    for (int c = pw; c < nchunks; c += 4)
-        produce(raw, c);
+    // two chunks in flight per producer, alternating register sets: the loads
+    // for chunk c + 4 are issued before chunk c is processed
+    RawC<E> ra, rb;
+    load(ra, pw);
+    for (int c = pw; c < nchunks; c += 8) {
+        load(rb, c + 4);
+        produce(ra, c);
+        if (c + 4 >= nchunks)
+            break;
+        load(ra, c + 8);
+        produce(rb, c + 4);
+    }
 }
 
 template <typename E, int DK>
