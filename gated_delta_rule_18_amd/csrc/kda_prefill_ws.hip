@@ -29,9 +29,8 @@
 //                      sequence and runs the state-dependent products of every
 //                      chunk in order; o goes straight to HBM;
 //   producers 4..7  -- producer p owns chunks p, p+4, p+8, ...: it loads q, k,
-//                      g, v directly in its compute layout (lane = two key
-//                      channels, registers = the 16 tokens; two chunks in
-//                      flight), builds the decayed operands with in-register
+//                      g, v directly in its compute layout (lane = four key
+//                      channels x eight tokens; two chunks in flight), builds the decayed operands with in-register
 //                      running products, forms A and M on MFMA, inverts I + A by
 //                      forward substitution with A's entries read out of the
 //                      accumulators as wave-uniform operands, and publishes the
@@ -62,7 +61,9 @@ constexpr int kVmcntZero = 0x0F70;
 //       8 channels of (m, g4) are {32m + 4g4 + e} (e < 4) and {32m + 16 + 4g4 + e-4}
 //       -- the contraction order the state accumulators impose (see consumer);
 //   image4 (Ke^T, V^T): 16-row tile t, lane (l16 = channel or value, g4 =
-//       token group): element e of 4 at  t*KS + 4*(l16 + 16 g4) + e, KS = 320;
+//       token group): element e of 4 at  tile(t) + 4*(l16 + 16 g4) + e, with
+//       tile(t) = t*KS + 8*((t/2) % 2), KS = 320 (the shift of every other tile
+//       pair spreads the producer's 16-byte writes over all banks);
 //   T, M: lane (l16 = row, g4): element e of 4 at 4*(l16 + 16 g4) + e = the
 //       entry (row l16, column 4 g4 + e).
 template <typename E, int DK>
@@ -70,7 +71,7 @@ struct WsL {
     static constexpr int ES = (int)sizeof(E);
     static constexpr int NS = ES == 2 ? 8 : 3;        // LDS slots
     static constexpr int GS = 136, MS = 4 * GS;       // image16 strides (elements)
-    static constexpr int KS = 320;                    // image4 tile stride (elements)
+    static constexpr int KS = 320;                    // image4 tile stride (elements, >= 256 + 8)
     static constexpr int NKS = DK / 32, NCT = DK / 16;
     static constexpr int I16 = NKS * MS;              // elements of one image16
     // slot, E-typed part (element offsets)
@@ -90,6 +91,7 @@ struct WsL {
     static constexpr int nFlags = NS + NS * 4 + 1;    // ready[NS], done[NS][4], abort
     static constexpr int bytes = oFlags + nFlags * 4;
     static_assert(slotBytes % 32 == 0 && pBytes % 32 == 0, "alignment");
+    static __device__ __forceinline__ int tile(int t) { return t * KS + 8 * ((t >> 1) & 1); }
     // image16 position of (token r, channel c)
     static __device__ __forceinline__ int img16(int r, int c)
     {
@@ -166,6 +168,28 @@ template <> struct Pair<float> {
     }
 };
 
+// Four adjacent elements as two packs: a = elements 0, 1, b = elements 2, 3.
+template <typename E> struct Quad;
+template <> struct Quad<__bf16> {
+    unsigned a, b;
+    static __device__ __forceinline__ Quad load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        return Quad{x[0], x[1]};
+    }
+};
+template <> struct Quad<float> {
+    float2 a, b;
+    static __device__ __forceinline__ Quad load(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+    {
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        return Quad{make_float2(__uint_as_float(x[0]), __uint_as_float(x[1])),
+                    make_float2(__uint_as_float(x[2]), __uint_as_float(x[3]))};
+    }
+};
+
 // A scalar element as raw bits (converted where it is used, so that no
 // instruction right after the load has to wait for it).
 __device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff, int soff, __bf16 *)
@@ -198,6 +222,17 @@ __device__ __forceinline__ void st_quad(float *d, float2 a, float2 b, float2 c, 
     reinterpret_cast<float4 *>(d)[1] = make_float4(c.x, c.y, e.x, e.y);
 }
 
+// Two packs (4 elements) stored contiguously.
+__device__ __forceinline__ void st_pair2(__bf16 *d, unsigned a, unsigned b)
+{
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<v2u *>(d) = v2u{a, b};
+}
+__device__ __forceinline__ void st_pair2(float *d, float2 a, float2 b)
+{
+    *reinterpret_cast<float4 *>(d) = make_float4(a.x, a.y, b.x, b.y);
+}
+
 // Bytes spanned by `rows` rows of `width` bytes, `stride` bytes apart (0 rows: 0).
 __device__ __forceinline__ int rows_bytes(int rows, int stride, int width)
 {
@@ -211,18 +246,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, int b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
-// One chunk's raw inputs in the producer's compute layout, straight from HBM:
-// lane l holds key channels 2l, 2l+1 of g, k, q for each of the 16 tokens (one
-// coalesced pair load per token and tensor), value columns 2 (l % 32), +1 of
-// the slice for tokens 8 (l / 32) .. +7, and beta of token l & 15 as raw bits
-// (converted where used, so no instruction right after the loads waits):
-// 48 + 8 + 1 loads, within what the wave's outstanding-load counter tracks.
-// Tokens past the end read 0; a chunk past the end is an empty buffer, so the
-// loads are issued unconditionally (no branch for the wait-count analysis to
-// merge conservatively).
+// One chunk's raw inputs in the producer's compute layout, straight from HBM
+// (tokens past the end read 0).  Lane l = (cq, th) = (l % 32, l / 32) holds
+// key channels 4cq .. 4cq+3 of g, k, q for tokens 8th .. 8th+7 (one 8-byte
+// load per token and tensor); lane l = (vq, tq) = (l % 16, l / 16) holds value
+// columns 4vq .. 4vq+3 of the slice for tokens 4tq .. 4tq+3; every lane holds
+// beta of token l % 16 as raw bits (converted where used, so no instruction
+// right after the loads waits).  29 loads: two chunks in flight stay within
+// what the wave's outstanding-load counter tracks.  A chunk past the end is an
+// empty buffer, so the loads are issued unconditionally (no branch for the
+// wait-count analysis to merge conservatively).
 template <typename E>
 struct RawC {
-    typename Pair<E>::T g[kC], k[kC], q[kC], v[kC / 2];
+    Quad<E> g[8], k[8], q[8], v[4];
     unsigned b;
 };
 
@@ -243,22 +279,22 @@ __device__ __forceinline__ void load_chunk(RawC<E> &R, const E *q, const E *k, c
     const __amdgpu_buffer_rsrc_t rg = buffer(g + row0 * DK, nb);
     const __amdgpu_buffer_rsrc_t rv = buffer(v + row0 * DV + slice * kVS, rows_bytes(valid, rsv, kVS * ES));
     const __amdgpu_buffer_rsrc_t rb = buffer(beta + row0, rows_bytes(valid, H * ES, ES));
-    const int vo = lane * 2 * ES;
-    if (2 * lane < DK) {
+    if (4 * (lane & 31) < DK) {
+        const int vo = (lane & 31) * 4 * ES + (lane >> 5) * 8 * rsk;
 #pragma unroll
-        for (int r = 0; r < kC; ++r)
-            R.g[r] = Pair<E>::load(rg, vo, r * rsk);
+        for (int i = 0; i < 8; ++i)
+            R.g[i] = Quad<E>::load(rg, vo, i * rsk);
 #pragma unroll
-        for (int r = 0; r < kC; ++r)
-            R.k[r] = Pair<E>::load(rk, vo, r * rsk);
+        for (int i = 0; i < 8; ++i)
+            R.k[i] = Quad<E>::load(rk, vo, i * rsk);
 #pragma unroll
-        for (int r = 0; r < kC; ++r)
-            R.q[r] = Pair<E>::load(rq, vo, r * rsk);
+        for (int i = 0; i < 8; ++i)
+            R.q[i] = Quad<E>::load(rq, vo, i * rsk);
     }
-    const int vov = (lane & 31) * 2 * ES + (lane >> 5) * (kC / 2) * rsv;
+    const int vov = (lane & 15) * 4 * ES + (lane >> 4) * 4 * rsv;
 #pragma unroll
-    for (int i = 0; i < kC / 2; ++i)
-        R.v[i] = Pair<E>::load(rv, vov, i * rsv);
+    for (int i = 0; i < 4; ++i)
+        R.v[i] = Quad<E>::load(rv, vov, i * rsv);
     R.b = load_bits(rb, (lane & 15) * H * ES, 0, (E *)nullptr);
 }
 
@@ -350,7 +386,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                 Y = mma32(aq, Bs[m], Y);
             }
             // X <- V - Kt S   (rows 4 g4 + j = tokens, column l16)
-            const V4 vv = *reinterpret_cast<const V4 *>(sl + L::eV + w * L::KS + 4 * lane);
+            const V4 vv = *reinterpret_cast<const V4 *>(sl + L::eV + L::tile(w) + 4 * lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 X[j] = to_f(vv[j]) - X[j];
@@ -363,7 +399,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             // S <- Gam S + Ke^T U
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const V4 kr = *reinterpret_cast<const V4 *>(sl + L::eKe + ct * L::KS + 4 * lane);
+                const V4 kr = *reinterpret_cast<const V4 *>(sl + L::eKe + L::tile(ct) + 4 * lane);
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 16 * ct + 4 * g4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -413,62 +449,94 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         int r16 = l16, rg4 = g4;
         asm volatile("" : "+v"(r16), "+v"(rg4));
 
-        // ---- V^T image: lane (p, half) = (l % 32, l / 32) holds value columns
-        // 2p, 2p+1 for token groups 2 half, 2 half + 1 ------------------------------
+        // ---- V^T image: lane (vq, tq) writes value columns 4vq .. 4vq+3 for token
+        // group tq (two 8-element pieces: columns 4vq, +1 and 4vq+2, +3) --------
         {
-            E *vt = sl + L::eV + ((2 * (lane & 31)) >> 4) * L::KS + 4 * ((2 * (lane & 31)) & 15) + 128 * (lane >> 5);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                st_quad(vt + 64 * u, PE::los(raw.v[4 * u], raw.v[4 * u + 1]), PE::los(raw.v[4 * u + 2], raw.v[4 * u + 3]),
-                        PE::his(raw.v[4 * u], raw.v[4 * u + 1]), PE::his(raw.v[4 * u + 2], raw.v[4 * u + 3]));
+            const int vq = lane & 15, tq = lane >> 4;
+            E *vt = sl + L::eV + L::tile(vq >> 2) + 4 * (4 * (vq & 3) + 16 * tq);
+            st_quad(vt, PE::los(raw.v[0].a, raw.v[1].a), PE::los(raw.v[2].a, raw.v[3].a),
+                    PE::his(raw.v[0].a, raw.v[1].a), PE::his(raw.v[2].a, raw.v[3].a));
+            st_quad(vt + 8, PE::los(raw.v[0].b, raw.v[1].b), PE::los(raw.v[2].b, raw.v[3].b),
+                    PE::his(raw.v[0].b, raw.v[1].b), PE::his(raw.v[2].b, raw.v[3].b));
         }
 
         // ---- decay factors by running products, then the operands ------------
-        // (lane l: key channels 2l, 2l+1 across the 16 tokens)
-        if (2 * lane < DK) {
-            float a0[kC], a1[kC];                         // alpha = e^g
+        // Lane (cq, th): key channels 4cq + u (u < 4), tokens 8th + i (i < 8).
+        // The two halves of the chunk meet through the partner lane l ^ 32.
+        if (4 * (lane & 31) < DK) {
+            const int cq = lane & 31, th = lane >> 5;
+            float al[4][8];                               // alpha = e^g
 #pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                a0[r] = __builtin_amdgcn_exp2f(PE::lo(raw.g[r]) * 1.4426950408889634f);
-                a1[r] = __builtin_amdgcn_exp2f(PE::hi(raw.g[r]) * 1.4426950408889634f);
+            for (int i = 0; i < 8; ++i) {
+                al[0][i] = __builtin_amdgcn_exp2f(PE::lo(raw.g[i].a) * 1.4426950408889634f);
+                al[1][i] = __builtin_amdgcn_exp2f(PE::hi(raw.g[i].a) * 1.4426950408889634f);
+                al[2][i] = __builtin_amdgcn_exp2f(PE::lo(raw.g[i].b) * 1.4426950408889634f);
+                al[3][i] = __builtin_amdgcn_exp2f(PE::hi(raw.g[i].b) * 1.4426950408889634f);
             }
-            // suffix products Z_r = e^{G_15 - G_r}; their total is Gam = e^{G_15}
-            float Z0[kC], Z1[kC];
-            float z0 = 1.f, z1 = 1.f;
+            // local suffix products z_i = prod_{i' > i} alpha_i' over this half, and
+            // the half's total; the partner's total completes both directions:
+            //   first half:  P_r = local prefix,             Z_r = z_r * total(second)
+            //   second half: P_r = total(first) * local prefix, Z_r = z_r
+            float Z[4][8], tot[4], oth[4];
 #pragma unroll
-            for (int r = kC - 1; r >= 0; --r) {
-                Z0[r] = z0;
-                Z1[r] = z1;
-                z0 *= a0[r];
-                z1 *= a1[r];
+            for (int u = 0; u < 4; ++u) {
+                float z = 1.f;
+#pragma unroll
+                for (int i = 7; i >= 0; --i) {
+                    Z[u][i] = z;
+                    z *= al[u][i];
+                }
+                tot[u] = z;
+                oth[u] = __shfl_xor(z, 32, 64);
             }
-            const float ig0 = __builtin_amdgcn_rcpf(z0), ig1 = __builtin_amdgcn_rcpf(z1);   // 1 / Gam
-            *reinterpret_cast<float2 *>(gam + 2 * lane) = make_float2(z0, z1);
+            float p[4], ig[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float gm = tot[u] * oth[u];         // Gam = e^{G_15}
+                ig[u] = __builtin_amdgcn_rcpf(gm);
+                p[u] = th ? oth[u] : 1.f;
+                const float zm = th ? 1.f : oth[u];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    Z[u][i] *= zm;
+                tot[u] = gm;
+            }
+            if (th == 0)
+                *reinterpret_cast<f32x4 *>(gam + 4 * cq) = f32x4{tot[0], tot[1], tot[2], tot[3]};
             // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Ke = k Z, Kc = Ke / Gam = k / P
-            const int io = L::img16(0, 2 * lane);         // token r adds 8 r
-            E *ke = sl + L::eKe + ((2 * lane) >> 4) * L::KS + 4 * ((2 * lane) & 15);   // token group tg adds 64 tg
-            float p0 = 1.f, p1 = 1.f, e0s[4], e1s[4];
+            const int io = L::img16(8 * th, 4 * cq);      // token 8th + i adds 8 i
+            E *ke = sl + L::eKe + L::tile(cq >> 2) + 4 * (4 * (cq & 3) + 32 * th);   // token group 2th + j adds 64 j
+            float es[4][4];
 #pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                p0 *= a0[r];
-                p1 *= a1[r];
-                const float k0 = PE::lo(raw.k[r]), k1 = PE::hi(raw.k[r]);
-                const float q0 = PE::lo(raw.q[r]), q1 = PE::hi(raw.q[r]);
-                const float e0 = k0 * Z0[r], e1 = k1 * Z1[r];
-                *reinterpret_cast<PT *>(sl + L::eKt + io + 8 * r) = PE::pack(k0 * p0, k1 * p1);
-                *reinterpret_cast<PT *>(sl + L::eQt + io + 8 * r) = PE::pack(q0 * p0, q1 * p1);
-                *reinterpret_cast<PT *>(pKc + io + 8 * r) = PE::pack(e0 * ig0, e1 * ig1);
-                e0s[r & 3] = e0;
-                e1s[r & 3] = e1;
-                if ((r & 3) == 3)
-                    st_quad(ke + 64 * (r >> 2), PE::pack(e0s[0], e0s[1]), PE::pack(e0s[2], e0s[3]),
-                            PE::pack(e1s[0], e1s[1]), PE::pack(e1s[2], e1s[3]));
+            for (int i = 0; i < 8; ++i) {
+                float kk[4], qq[4];
+                kk[0] = PE::lo(raw.k[i].a), kk[1] = PE::hi(raw.k[i].a), kk[2] = PE::lo(raw.k[i].b), kk[3] = PE::hi(raw.k[i].b);
+                qq[0] = PE::lo(raw.q[i].a), qq[1] = PE::hi(raw.q[i].a), qq[2] = PE::lo(raw.q[i].b), qq[3] = PE::hi(raw.q[i].b);
+                float kt[4], qt[4], kc[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    p[u] *= al[u][i];
+                    kt[u] = kk[u] * p[u];
+                    qt[u] = qq[u] * p[u];
+                    es[u][i & 3] = kk[u] * Z[u][i];
+                    kc[u] = es[u][i & 3] * ig[u];
+                }
+                st_pair2(sl + L::eKt + io + 8 * i, PE::pack(kt[0], kt[1]), PE::pack(kt[2], kt[3]));
+                st_pair2(sl + L::eQt + io + 8 * i, PE::pack(qt[0], qt[1]), PE::pack(qt[2], qt[3]));
+                st_pair2(pKc + io + 8 * i, PE::pack(kc[0], kc[1]), PE::pack(kc[2], kc[3]));
+                if ((i & 3) == 3) {
+                    E *d = ke + 64 * (i >> 2);
+                    st_quad(d, PE::pack(es[0][0], es[0][1]), PE::pack(es[0][2], es[0][3]),
+                            PE::pack(es[1][0], es[1][1]), PE::pack(es[1][2], es[1][3]));
+                    st_quad(d + 8, PE::pack(es[2][0], es[2][1]), PE::pack(es[2][2], es[2][3]),
+                            PE::pack(es[3][0], es[3][1]), PE::pack(es[3][2], es[3][3]));
+                }
             }
         }
         lds_fence();
 
         // ---- A and M on MFMA (contraction over the DK channels) ----------------
-        f32x4 ATr = {0.f, 0.f, 0.f, 0.f}, Mtr = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Ar = {0.f, 0.f, 0.f, 0.f}, ATr = {0.f, 0.f, 0.f, 0.f}, Mtr = {0.f, 0.f, 0.f, 0.f};
         {
             const int ia = g4 * L::GS + 8 * l16;
 #pragma unroll
@@ -476,6 +544,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                 const V8 ak = *reinterpret_cast<const V8 *>(sl + L::eKt + ia + m * L::MS);
                 const V8 aq = *reinterpret_cast<const V8 *>(sl + L::eQt + ia + m * L::MS);
                 const V8 bc = *reinterpret_cast<const V8 *>(pKc + ia + m * L::MS);
+                Ar = mma32(ak, bc, Ar);         // <Kt_r, Kc_i>: rows r = 4 g4 + j, column i = l16
                 ATr = mma32(bc, ak, ATr);       // <Kc_i, Kt_r>: rows i = 4 g4 + j, column r = l16
                 Mtr = mma32(bc, aq, Mtr);       // <Kc_i, Qt_r>: rows i = 4 g4 + j, column r = l16
             }
@@ -494,9 +563,11 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         // Evaluated on fp32 MFMA with every 16 x 16 matrix in the accumulator
         // layout (lane (n, g) holds rows 4g .. 4g+3 of column n).  mul(Xt, Y)
         // forms X Y from X^T and Y in that layout: the contraction index of step
-        // s in lane group g is 4g + s, which is element s of both operands.  A
-        // transposed product needs no data movement: (XY)^T = mul(Y, X^T) from
-        // the same registers.
+        // s in lane group g is 4g + s, which is element s of both operands; so
+        // (XY)^T = mul(Y, X^T) comes from the same registers.  The consumers take
+        // T as an MFMA A operand, whose image is T^T in the accumulator layout:
+        //   T^T = Diag(beta) (I - A^T)(I + A2^T)(I + A4^T)(I + A8^T),
+        // built from A and A^T (both straight from the bf16 products above).
         {
             auto mul = [](f32x4 xt, f32x4 y) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -505,25 +576,28 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[st], y[st], acc, 0, 0, 0);
                 return acc;
             };
-            const float bl = bits_to_f(raw.b, (E *)nullptr);      // beta of token l16
-            f32x4 I4, AT;
+            // beta of token l16 (row l16 of A^T's columns) and of tokens 4g + j
+            // (this lane's rows), the latter fetched from lanes 4g + j
+            const float bl = bits_to_f(raw.b, (E *)nullptr);
+            f32x4 br;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                br[j] = bits_to_f((unsigned)__builtin_amdgcn_ds_bpermute(4 * (4 * rg4 + j), (int)raw.b), (E *)nullptr);
+            f32x4 I4, A, AT;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                I4[j] = 4 * rg4 + j == r16 ? 1.f : 0.f;
-                // A^T[4g + j][l16] = A[l16][4g + j] = beta_l16 <Kt_l16, Kc_4g+j>, kept below the diagonal of A
-                AT[j] = 4 * rg4 + j < r16 ? bl * ATr[j] : 0.f;
+                const int row = 4 * rg4 + j;
+                I4[j] = row == r16 ? 1.f : 0.f;
+                A[j] = row > r16 ? br[j] * Ar[j] : 0.f;      // A[row][l16]
+                AT[j] = row < r16 ? bl * ATr[j] : 0.f;       // A^T[row][l16] = A[l16][row]
             }
-            const f32x4 A1 = mul(AT, I4);                 // A
-            const f32x4 A2 = mul(AT, A1), A2T = mul(A1, AT);
+            const f32x4 A2 = mul(AT, A), A2T = mul(A, AT);
             const f32x4 A4 = mul(A2T, A2), A4T = mul(A2, A2T);
-            const f32x4 A8 = mul(A4T, A4);
-            const f32x4 W = I4 + A4 + A8 + mul(A4T, A8);  // (I + A^4)(I + A^8)
-            const f32x4 W2 = W + mul(A2T, W);             // (I + A^2) W
-            const f32x4 Li = W2 - mul(AT, W2);            // (I - A) W2 = (I + A)^{-1}
-            // T = Li Diag(beta): column l16 scales by beta_l16.  The consumers take
-            // T as an MFMA A operand, whose image is T^T in the accumulator layout.
-            const f32x4 TT = mul(Li * bl, I4);
-            *reinterpret_cast<V4 *>(sl + L::eT + 4 * lane) = cvt4<E>(TT);
+            const f32x4 A8T = mul(A4, A4T);
+            const f32x4 WT = I4 + A4T + A8T + mul(A4, A8T);   // ((I + A^4)(I + A^8))^T
+            const f32x4 W2T = WT + mul(A2, WT);                // (I + A2^T) W^T
+            const f32x4 LiT = W2T - mul(A, W2T);               // (I - A^T) W2^T = ((I + A)^{-1})^T
+            *reinterpret_cast<V4 *>(sl + L::eT + 4 * lane) = cvt4<E>(br * LiT);
         }
         // publish the slot
         lds_fence();
