@@ -233,6 +233,29 @@ __device__ __forceinline__ void st_pair2(float *d, float2 a, float2 b)
     *reinterpret_cast<float4 *>(d) = make_float4(a.x, a.y, b.x, b.y);
 }
 
+// Lane K of each 16-lane row of the wavefront, broadcast to the whole row
+// (DPP row broadcast; folded into the consuming instruction).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xf, 0xf, false));
+}
+
+// S[16 ct + 4 g + j][.] *= Gam[16 ct + 4 g + j] for every ct < N, with lane
+// 2 ct + j / 2 of row g holding Gam[16 ct + 4 g + j], j = 0..3, as gp.x (j even)
+// and gp.y (j odd).
+template <int N, int CT = 0>
+__device__ __forceinline__ void decay_rows(f32x4 *S, float2 gp)
+{
+    if constexpr (CT < N) {
+        S[CT][0] *= row_bcast<2 * CT>(gp.x);
+        S[CT][1] *= row_bcast<2 * CT>(gp.y);
+        S[CT][2] *= row_bcast<2 * CT + 1>(gp.x);
+        S[CT][3] *= row_bcast<2 * CT + 1>(gp.y);
+        decay_rows<N, CT + 1>(S, gp);
+    }
+}
+
 // Bytes spanned by `rows` rows of `width` bytes, `stride` bytes apart (0 rows: 0).
 __device__ __forceinline__ int rows_bytes(int rows, int stride, int width)
 {
@@ -362,54 +385,106 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                           rows_bytes(valid, rso, 16 * L::ES));
         };
 
-        for (int c = 0; c < nchunks; ++c) {
+        // Chunk c's operands, read from its slot into registers one chunk ahead:
+        // the state chain of chunk c then runs with no LDS wait in it, while the
+        // reads for chunk c + 1 overlap chunk c's state update.
+        // The A operands of the 16-deep products (T, M, Ke^T) sit in the low half
+        // of 8-element tuples whose high half stays zero for the whole loop (the
+        // zero is opaque to the compiler, so it is never rematerialised).
+        struct Ops {
+            V8 kt[NKS], qt[NKS];
+            V8 tr, mr, kr[NCT];
+            V4 vv;
+            float2 gp;        // Gam pair, see decay_rows
+        };
+        auto low = [](V4 x, V8 keep) { return __builtin_shufflevector(cat8(x, x), keep, 0, 1, 2, 3, 12, 13, 14, 15); };
+        // element offsets of this lane's 8-byte reads of Ke^T tiles, T and M in a
+        // slot, each held in its own register (opaque to the compiler), so no two
+        // reads are fused into one double read whose halves would then have to
+        // be copied into the operand tuples
+        int o4[NCT + 2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            o4[ct] = L::eKe + L::tile(ct) + 4 * lane;
+        o4[NCT] = L::eT + 4 * lane;
+        o4[NCT + 1] = L::eM + 4 * lane;
+#pragma unroll
+        for (int i = 0; i < NCT + 2; ++i)
+            asm volatile("" : "+v"(o4[i]));
+        auto fetch = [&](Ops &op, int c) {
             const int s = c % NS;
+            wait_flags(ready + s, 1, 1, c + 1, abort_flag);
+            const E *sl = reinterpret_cast<const E *>(smem + L::oSlots + s * L::slotBytes);
+            const float *gam = reinterpret_cast<const float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
+            const E *kt = sl + L::eKt + g4 * L::GS + 8 * l16;
+            const E *qt = sl + L::eQt + g4 * L::GS + 8 * l16;
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) {
+                op.kt[m] = *reinterpret_cast<const V8 *>(kt + m * L::MS);
+                op.qt[m] = *reinterpret_cast<const V8 *>(qt + m * L::MS);
+            }
+            op.vv = *reinterpret_cast<const V4 *>(sl + L::eV + L::tile(w) + 4 * lane);
+            op.tr = low(*reinterpret_cast<const V4 *>(sl + o4[NCT]), op.tr);
+            op.mr = low(*reinterpret_cast<const V4 *>(sl + o4[NCT + 1]), op.mr);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                op.kr[ct] = low(*reinterpret_cast<const V4 *>(sl + o4[ct]), op.kr[ct]);
+            op.gp = *reinterpret_cast<const float2 *>(gam + 16 * (l16 >> 1) + 4 * g4 + 2 * (l16 & 1));
+        };
+
+        Ops op;
+        {
+            V8 z = {};
+            asm volatile("" : "+v"(z));
+            op.tr = op.mr = z;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                op.kr[ct] = z;
+        }
+        if (nchunks > 0)
+            fetch(op, 0);
+        for (int c = 0; c < nchunks; ++c) {
             // S strip as B operands; contraction slice m holds channels
             // {32m + 4 g4 + e, 32m + 16 + 4 g4 + e}, e = 0..3
             V8 Bs[NKS];
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
                 Bs[m] = cat8(cvt4<E>(Sacc[2 * m]), cvt4<E>(Sacc[2 * m + 1]));
-
-            wait_flags(ready + s, 1, 1, c + 1, abort_flag);
-            const E *sl = reinterpret_cast<const E *>(smem + L::oSlots + s * L::slotBytes);
-            const float *gam = reinterpret_cast<const float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
-
-            f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-            const E *kt = sl + L::eKt + g4 * L::GS + 8 * l16;
-            const E *qt = sl + L::eQt + g4 * L::GS + 8 * l16;
+            // X = Kt S as two independent accumulation chains, Y = Qt S
+            f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0, Y = X0;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                const V8 a = *reinterpret_cast<const V8 *>(kt + m * L::MS);
-                const V8 aq = *reinterpret_cast<const V8 *>(qt + m * L::MS);
-                X = mma32(a, Bs[m], X);
-                Y = mma32(aq, Bs[m], Y);
+                if (m & 1)
+                    X1 = mma32(op.kt[m], Bs[m], X1);
+                else
+                    X0 = mma32(op.kt[m], Bs[m], X0);
+                Y = mma32(op.qt[m], Bs[m], Y);
             }
             // X <- V - Kt S   (rows 4 g4 + j = tokens, column l16)
-            const V4 vv = *reinterpret_cast<const V4 *>(sl + L::eV + L::tile(w) + 4 * lane);
+            f32x4 X;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                X[j] = to_f(vv[j]) - X[j];
-            // U = T X, then O = Y + M U   (contraction over tokens 4 g4 + e)
-            const V4 tr = *reinterpret_cast<const V4 *>(sl + L::eT + 4 * lane);
-            const f32x4 U = mma16(tr, cvt4<E>(X), f32x4{0.f, 0.f, 0.f, 0.f});
+                X[j] = to_f(op.vv[j]) - (X0[j] + X1[j]);
+            // U = T X, then O = Y + M U   (contraction over tokens 4 g4 + e; the
+            // B operands repeat their 4 elements in the high half, which the
+            // zero high half of the A operands cancels)
+            const V4 bx = cvt4<E>(X);
+            const f32x4 U = mma32(op.tr, cat8(bx, bx), f32x4{0.f, 0.f, 0.f, 0.f});
             const V4 bu = cvt4<E>(U);
-            const V4 mr = *reinterpret_cast<const V4 *>(sl + L::eM + 4 * lane);
-            const f32x4 Z = mma16(mr, bu, f32x4{0.f, 0.f, 0.f, 0.f});
+            const V8 bu8 = cat8(bu, bu);
+            const f32x4 Z = mma32(op.mr, bu8, f32x4{0.f, 0.f, 0.f, 0.f});
             // S <- Gam S + Ke^T U
+            decay_rows<NCT>(Sacc, op.gp);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const V4 kr = *reinterpret_cast<const V4 *>(sl + L::eKe + L::tile(ct) + 4 * lane);
-                const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 16 * ct + 4 * g4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Sacc[ct][j] *= gm[j];
-                Sacc[ct] = mma16(kr, bu, Sacc[ct]);
-            }
-            // every read of slot s has landed in registers: hand it back
+            for (int ct = 0; ct < NCT; ++ct)
+                Sacc[ct] = mma32(op.kr[ct], bu8, Sacc[ct]);
+            // every read of slot c is in registers (and consumed): hand it back,
+            // then fetch the next chunk while the state update runs
             lds_fence();
             if (lane == 0)
-                st_flag(done + s * 4 + w, c + 1);
+                st_flag(done + (c % NS) * 4 + w, c + 1);
+            if (c + 1 < nchunks)
+                fetch(op, c + 1);
             const __amdgpu_buffer_rsrc_t ro = tile(o, c);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
