@@ -14,13 +14,32 @@ chunk-relative cumulative log-decay G_r = sum_{s<=r} g_s,
     S_out  = Diag(exp(G_C)) S + (k*exp(G_C - G))^T U
 `ref` selects where each exp(G_r - G_i) is split into a row and a column factor:
     "direct"  -- the product is formed from the difference (no split),
-    "center"  -- split at the middle of the chunk, as the GPU kernel does (each
-                 factor then spans at most C/2 positions of decay).
+    "center"  -- split at the middle of the chunk, as the chunk-32 GPU kernel does
+                 (each factor then spans at most C/2 positions of decay),
+    "start"   -- split at the chunk start, as the chunk-16 GPU kernel does (row
+                 factor exp(G_r) <= 1, column factor exp(-G_i) <= e^{5 C}).
+`inverse` selects how (I + A)^{-1} is formed:
+    "solve"   -- a dense linear solve,
+    "product" -- the exact finite product (I - A)(I + A^2)(I + A^4)(I + A^8) for a
+                 strictly lower triangular A of order <= 16 (A^16 = 0), as the
+                 chunk-16 GPU kernel evaluates it.
 """
 import numpy as np
 
 
-def chunk_forward(q, k, v, g, beta, S0, C, ref="direct"):
+def nilpotent_inverse(A):
+    """(I + A)^{-1} for strictly lower triangular A of order n <= 16, as the product
+    (I - A)(I + A^2)(I + A^4)(I + A^8) = sum_{j<16} (-A)^j (A^16 = 0)."""
+    n = A.shape[0]
+    assert n <= 16 and not np.triu(A).any()
+    I = np.eye(n)
+    A2 = A @ A
+    A4 = A2 @ A2
+    A8 = A4 @ A4
+    return (I - A) @ (I + A2) @ (I + A4) @ (I + A8)
+
+
+def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve"):
     T, dk = q.shape
     dv = v.shape[1]
     S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
@@ -35,6 +54,11 @@ def chunk_forward(q, k, v, g, beta, S0, C, ref="direct"):
             E = np.exp(np.where(np.arange(n)[:, None, None] >= np.arange(n)[None, :, None], D, -np.inf))
             KK = np.einsum("rc,ic,ric->ri", kc, kc, E)
             QK = np.einsum("rc,ic,ric->ri", qc, kc, E)
+        elif ref == "start":
+            rowf = np.exp(G)
+            colf = np.exp(-G)
+            KK = (kc * rowf) @ (kc * colf).T
+            QK = (qc * rowf) @ (kc * colf).T
         elif ref == "center":
             h = min(C // 2, n)
             R = G[h - 1]
@@ -46,7 +70,12 @@ def chunk_forward(q, k, v, g, beta, S0, C, ref="direct"):
             raise ValueError(ref)
         A = np.tril(bc[:, None] * KK, -1)
         M = np.tril(QK)
-        Tm = np.linalg.solve(np.eye(n) + A, np.diag(bc))
+        if inverse == "solve":
+            Tm = np.linalg.solve(np.eye(n) + A, np.diag(bc))
+        elif inverse == "product":
+            Tm = nilpotent_inverse(A) @ np.diag(bc)
+        else:
+            raise ValueError(inverse)
         U = Tm @ (vc - (kc * np.exp(G)) @ S)
         o[sl] = (qc * np.exp(G)) @ S + M @ U
         S = np.exp(G[-1])[:, None] * S + (kc * np.exp(G[-1] - G)).T @ U
