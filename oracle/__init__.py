@@ -12,6 +12,9 @@ Functions
 ---------
 prefill(q, k, v, g, beta, S0=None, nthreads=None) -> (o, S_T)
     q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; S0 [B,H,dk,dv] or None.
+prefill_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, nthreads=None) -> (o, S_T, snaps)
+    as prefill, plus snaps [n_snaps,B,H,dk,dv]: snapshot s is the state after the
+    first (s + 1) * snap_every tokens.
 decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
             eps=1e-6, nthreads=None) -> o
     conv_cache and S are updated in place (they must be float64 C-contiguous
@@ -39,6 +42,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.kda_oracle_prefill.restype = ctypes.c_int
         lib.kda_oracle_prefill.argtypes = [_dp] * 8 + [ctypes.c_long] * 5 + [ctypes.c_int]
+        lib.kda_oracle_prefill_snapshots.restype = ctypes.c_int
+        lib.kda_oracle_prefill_snapshots.argtypes = [_dp] * 9 + [ctypes.c_long] * 7 + [ctypes.c_int]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = (
             [_dp] * 5 + [ctypes.c_long] + [_dp] * 4 + [ctypes.c_long] * 5 + [ctypes.c_double, ctypes.c_int])
@@ -75,6 +80,26 @@ def prefill(q, k, v, g, beta, S0=None, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_prefill failed ({rc})")
     return o, S_T
+
+
+def prefill_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, nthreads=None):
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("oracle.prefill_snapshots: inconsistent shapes")
+    S0a = None if S0 is None else _f64(S0)
+    if S0a is not None and S0a.shape != (B, H, dk, dv):
+        raise ValueError("oracle.prefill_snapshots: S0 shape")
+    o = np.empty((B, T, H, dv))
+    S_T = np.empty((B, H, dk, dv))
+    snaps = np.empty((n_snaps, B, H, dk, dv))
+    rc = _load().kda_oracle_prefill_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0a),
+                                              _ptr(o), _ptr(S_T), _ptr(snaps), int(snap_every), int(n_snaps),
+                                              B, T, H, dk, dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill_snapshots failed ({rc})")
+    return o, S_T, snaps
 
 
 def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,

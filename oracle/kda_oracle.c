@@ -33,9 +33,18 @@
  * tap 0 applied to the oldest token; Swish(u) = u * sigmoid(u); L2Norm(x) =
  * x / sqrt(sum x^2 + eps).
  *
+ * Prefill can also record the state at regular token counts: the note's
+ * section 9 (long-trajectory environments, the report's Figure 12 on prefix
+ * caching) keeps one KDA state per sequence and layer and snapshots it only at
+ * block boundaries (512 tokens), so that a cached prefix resumes prefill from
+ * the state at its end.  Snapshot s is the state after the first
+ * (s + 1) * snap_every tokens, i.e. exactly what a prefill over that prefix
+ * returns as its final state.
+ *
  * Layouts (all row-major, fp64, host memory):
  *   q, k, g : [B, T, H, dk]     v, o : [B, T, H, dv]     beta : [B, T, H]
  *   S0, S_T : [B, H, dk, dv]    (row = key channel, column = value channel)
+ *   snaps   : [n_snaps, B, H, dk, dv]
  * Independent (b, h) units are spread over `nthreads` POSIX threads; each
  * unit's loop is sequential.
  */
@@ -47,6 +56,8 @@
 typedef struct {
     const double *q, *k, *v, *g, *beta, *S0;
     double *o, *S_T;
+    double *snaps;
+    long snap_every, n_snaps;
     long B, T, H, dk, dv;
     int tid, nthreads;
     int status;
@@ -92,6 +103,11 @@ static void prefill_unit(const prefill_job *J, long b, long h, double *S, double
         for (long i = 0; i < dk; ++i)
             for (long j = 0; j < dv; ++j)
                 ot[j] += S[i * dv + j] * qt[i];
+        /* the state after t + 1 tokens, when that count closes a snapshot block */
+        if (J->snaps && (t + 1) % J->snap_every == 0 && (t + 1) / J->snap_every <= J->n_snaps) {
+            const long s = (t + 1) / J->snap_every - 1;
+            memcpy(J->snaps + ((s * J->B + b) * H + h) * dk * dv, S, sizeof(double) * dk * dv);
+        }
     }
     if (J->S_T)
         memcpy(J->S_T + (b * H + h) * dk * dv, S, sizeof(double) * dk * dv);
@@ -116,16 +132,23 @@ static void *prefill_worker(void *arg)
 }
 
 /*
- * Prefill over T tokens for B sequences and H heads.  S0 may be NULL (zero
- * initial state); S_T may be NULL (final state not returned).  S0 and S_T may
- * alias.  Returns 0, or -1 on a bad argument or failed allocation.
+ * Prefill over T tokens for B sequences and H heads, recording n_snaps states
+ * (snapshot s after (s + 1) * snap_every tokens; n_snaps * snap_every <= T).
+ * S0 may be NULL (zero initial state); S_T may be NULL (final state not
+ * returned); snaps may be NULL when n_snaps is 0.  S0 and S_T may alias.
+ * Returns 0, or -1 on a bad argument or failed allocation.
  */
-int kda_oracle_prefill(const double *q, const double *k, const double *v, const double *g,
-                       const double *beta, const double *S0, double *o, double *S_T,
-                       long B, long T, long H, long dk, long dv, int nthreads)
+int kda_oracle_prefill_snapshots(const double *q, const double *k, const double *v,
+                                 const double *g, const double *beta, const double *S0, double *o,
+                                 double *S_T, double *snaps, long snap_every, long n_snaps,
+                                 long B, long T, long H, long dk, long dv, int nthreads)
 {
     if (!q || !k || !v || !g || !beta || !o || B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return -1;
+    if (n_snaps < 0 || (n_snaps > 0 && (!snaps || snap_every <= 0 || n_snaps * snap_every > T)))
+        return -1;
+    if (n_snaps == 0)
+        snaps = NULL;
     if (nthreads < 1)
         nthreads = 1;
     if ((long)nthreads > B * H)
@@ -140,7 +163,7 @@ int kda_oracle_prefill(const double *q, const double *k, const double *v, const 
     }
     int rc = 0;
     for (int i = 0; i < nthreads; ++i) {
-        prefill_job J = {q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, i, nthreads, 0};
+        prefill_job J = {q, k, v, g, beta, S0, o, S_T, snaps, snap_every, n_snaps, B, T, H, dk, dv, i, nthreads, 0};
         jobs[i] = J;
     }
     for (int i = 1; i < nthreads; ++i)
@@ -161,6 +184,15 @@ int kda_oracle_prefill(const double *q, const double *k, const double *v, const 
     free(jobs);
     free(th);
     return rc;
+}
+
+/* Prefill without snapshots (see above). */
+int kda_oracle_prefill(const double *q, const double *k, const double *v, const double *g,
+                       const double *beta, const double *S0, double *o, double *S_T,
+                       long B, long T, long H, long dk, long dv, int nthreads)
+{
+    return kda_oracle_prefill_snapshots(q, k, v, g, beta, S0, o, S_T, NULL, 1, 0, B, T, H, dk, dv,
+                                        nthreads);
 }
 
 /* ---------------------------------------------------------------- decode -- */

@@ -283,3 +283,42 @@ def test_decode_identity_conv_and_unit_norm():
     np.testing.assert_array_equal(cache[:, :, 0, 2 * dk:], vp)
     assert np.allclose(np.linalg.norm(kn, axis=-1), 1.0, atol=1e-6)
     assert o.shape == (N, H, dv)
+
+
+# ---------------------------------------------------------------- snapshots --
+
+def test_snapshots_are_prefix_final_states():
+    """Snapshot s (the state after (s+1)*every tokens) is, independently, the final
+    state of a prefill over that prefix -- the state a cached prefix resumes from
+    (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 9, the
+    KDA-checkpoint / hash-block prefix cache figure)."""
+    rng = np.random.default_rng(31)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 2, 100, 3, 8, 4)
+    o, S_T, snaps = oracle.prefill_snapshots(q, k, v, g, beta, S0, 16, 6)
+    for s in range(6):
+        t = (s + 1) * 16
+        _, S_pre = oracle.prefill(q[:, :t], k[:, :t], v[:, :t], g[:, :t], beta[:, :t], S0)
+        assert np.array_equal(S_pre, snaps[s])
+    o2, S2 = oracle.prefill(q, k, v, g, beta, S0)
+    assert np.array_equal(o, o2) and np.array_equal(S_T, S2)
+
+
+def test_snapshot_at_the_end_is_the_final_state_and_resumes():
+    """With T a multiple of the interval the last snapshot is S_T, and a prefill of
+    the suffix started from a snapshot reproduces the tail of o and S_T."""
+    rng = np.random.default_rng(32)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 96, 2, 8, 4)
+    o, S_T, snaps = oracle.prefill_snapshots(q, k, v, g, beta, S0, 32, 3)
+    assert np.array_equal(snaps[2], S_T)
+    o_tail, S_tail = oracle.prefill(q[:, 32:], k[:, 32:], v[:, 32:], g[:, 32:], beta[:, 32:], snaps[0])
+    _close(o_tail, o[:, 32:], 1e-12)
+    _close(S_tail, S_T, 1e-12)
+
+
+def test_snapshot_arguments_rejected():
+    rng = np.random.default_rng(33)
+    q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 20, 1, 4, 4)
+    with pytest.raises(RuntimeError):
+        oracle.prefill_snapshots(q, k, v, g, beta, S0, 8, 3)   # 3 * 8 > 20
+    with pytest.raises(RuntimeError):
+        oracle.prefill_snapshots(q, k, v, g, beta, S0, 0, 1)
