@@ -9,6 +9,8 @@ torch.cuda.synchronize():
            g = -4.99 (the headline: `value` is its tokens/s);
   decode   one kda_decode_step over N=256 sequences x H=96 heads, dk=dv=128,
            bf16, ShortConv width 4 (reported under "decode").
+A third phase (reported under "snapshots") times kda_chunk_fwd_snapshots on the
+prefill workload with a state snapshot every 512 tokens (128 snapshots).
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
@@ -128,6 +130,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-snapshots", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -171,6 +174,30 @@ def main():
     p_flops = prefill_flops(B, T, H, dk, dv, C)
     p_gbps = p_bytes / (p_kern * 1e-3) / 1e9
     p_tflops = p_flops / (p_kern * 1e-3) / 1e12
+    snapshots = None
+    if not args.skip_snapshots:
+        every = 512
+        n_snaps = T // every
+        snaps = torch.empty((n_snaps, B, H, dk, dv), dtype=torch.float32, device=dev)
+
+        def snap_step(i=0):
+            binding.chunk_fwd_snapshots(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], every, n_snaps,
+                                        chunk=C, o=o, S_T=S_T, snaps=snaps)
+
+        s_wall, s_kern = _timed(snap_step, args.steps, args.warmup, torch)
+        s_bytes = p_bytes + n_snaps * B * H * dk * dv * 4
+        s_gbps = s_bytes / (s_kern * 1e-3) / 1e9
+        snapshots = {
+            "workload": f"k3_prefill with a state snapshot every {every} tokens ({n_snaps} snapshots, "
+                        f"{n_snaps * B * H * dk * dv * 4 / 1e9:.3f} GB written)",
+            "ms_per_step": s_wall,
+            "kernel_ms": s_kern,
+            "tokens_per_s": B * T / (s_wall * 1e-3),
+            "extra_ms_vs_prefill": s_kern - p_kern,
+            "roofline": {"bound": "hbm", "achieved": s_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": s_gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": s_bytes},
+        }
+        del snaps
     cpu = None if args.no_cpu else cpu_baseline(x, H)
     del x, o
 
@@ -234,6 +261,7 @@ def main():
                                  if C == 16 else None),
                      "bytes_per_launch": p_bytes},
         "decode": decode,
+        "snapshots": snapshots,
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -4,8 +4,9 @@ Every step of the computation runs in the library's HIP kernels; torch is used
 for device memory and for the current HIP stream.  If the library is missing
 the calls raise (there is no fallback).
 
-    o, S_T = chunk_fwd(q, k, v, g, beta, S0=None, chunk=16)
-    o      = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
+    o, S_T        = chunk_fwd(q, k, v, g, beta, S0=None, chunk=16)
+    o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=16)
+    o             = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
 
 Shapes and dtypes follow include/kda.h: bf16 activations with an fp32 state,
 or fp32 everywhere (test mode).
@@ -20,7 +21,7 @@ library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_strerror", "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_strerror", "kda_version")
 
 _lib = None
 
@@ -42,6 +43,8 @@ def lib():
         vp, i = ctypes.c_void_p, ctypes.c_int
         L.kda_chunk_fwd.restype = i
         L.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp]
+        L.kda_chunk_fwd_snapshots.restype = i
+        L.kda_chunk_fwd_snapshots.argtypes = [vp] * 9 + [i] * 9 + [vp]
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
         L.kda_strerror.restype = ctypes.c_char_p
@@ -94,6 +97,18 @@ def chunk_fwd(q, k, v, g, beta, S0=None, chunk=16, o=None, S_T=None, return_stat
     """Chunkwise prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
     S0 [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv] fp32 or None).
     S_T may be passed as S0 itself for in-place streaming over segments."""
+    o, S_T, _ = _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, None, 0, 0)
+    return o, S_T
+
+
+def chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=16, o=None, S_T=None,
+                        snaps=None, return_state=True):
+    """chunk_fwd that also returns snaps [n_snaps,B,H,dk,dv] fp32: snapshot s is the
+    state after the first (s+1)*snap_every tokens (snap_every a multiple of chunk)."""
+    return _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps)
+
+
+def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -111,10 +126,19 @@ def chunk_fwd(q, k, v, g, beta, S0=None, chunk=16, o=None, S_T=None, return_stat
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif S_T is not None:
         _want(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
-    rc = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
-                             _ptr(S_T), B, T, H, dk, dv, code, int(chunk), _stream(dev))
+    if n_snaps and snaps is None:
+        snaps = torch.empty((n_snaps, B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif snaps is not None:
+        _want(snaps, "snaps", (n_snaps, B, H, dk, dv), torch.float32, dev)
+    if n_snaps or snaps is not None:
+        rc = lib().kda_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                           _ptr(o), _ptr(S_T), _ptr(snaps), int(snap_every), int(n_snaps),
+                                           B, T, H, dk, dv, code, int(chunk), _stream(dev))
+    else:
+        rc = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                 _ptr(S_T), B, T, H, dk, dv, code, int(chunk), _stream(dev))
     _check(rc)
-    return o, S_T
+    return o, S_T, snaps
 
 
 def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o=None):

@@ -12,6 +12,53 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
 bool head_ok(int d) { return d == 64 || d == 128; }
 
+bool overlap(const void *a, long long na, const void *b, long long nb)
+{
+    const char *x = reinterpret_cast<const char *>(a), *y = reinterpret_cast<const char *>(b);
+    return a && b && x < y + nb && y < x + na;
+}
+
+int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+              const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv, int dtype,
+              int chunk, const kda::Snapshots &snap, void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (chunk != 16 && chunk != 32)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk) || !head_ok(dv))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40))
+        return KDA_ERR_INVALID;
+    const bool has_tokens = (long long)B * T * H > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !o))
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, g, o, S0, S_T, snap.out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDA_ERR_INVALID;
+    // S_T may be S0 itself; a partial overlap would let one head's write race
+    // with another head's read.
+    const long long state_bytes = (long long)B * H * dk * dv * 4;
+    if (S0 != S_T && overlap(S0, state_bytes, S_T, state_bytes))
+        return KDA_ERR_INVALID;
+    if (snap.count < 0)
+        return KDA_ERR_INVALID;
+    if (snap.count > 0) {
+        if (!snap.out || snap.every_chunks <= 0 || (long long)snap.count * snap.every_chunks * chunk > T)
+            return KDA_ERR_INVALID;
+        const long long snap_bytes = state_bytes * snap.count;
+        if (overlap(snap.out, snap_bytes, S0, state_bytes) || overlap(snap.out, snap_bytes, S_T, state_bytes))
+            return KDA_ERR_INVALID;
+    }
+    hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
+                                         dtype == KDA_FP32, chunk, snap,
+                                         reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 } // namespace
 
 extern "C" {
@@ -38,35 +85,26 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, co
                   const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv,
                   int dtype, int chunk, void *stream)
 {
-    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+    return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, kda::Snapshots{},
+                     stream);
+}
+
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *S0, void *o, float *S_T, float *snaps,
+                            int snap_every, int n_snaps, int B, int T, int H, int dk, int dv,
+                            int dtype, int chunk, void *stream)
+{
+    if (n_snaps < 0 || (n_snaps > 0 && (snap_every <= 0 || chunk <= 0 || snap_every % chunk != 0)))
         return KDA_ERR_INVALID;
-    if (dtype != KDA_BF16 && dtype != KDA_FP32)
-        return KDA_ERR_INVALID;
-    if (chunk != 16 && chunk != 32)
-        return KDA_ERR_INVALID;
-    if (!head_ok(dk) || !head_ok(dv))
-        return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40))
-        return KDA_ERR_INVALID;
-    const bool has_tokens = (long long)B * T * H > 0;
-    if (has_tokens && (!q || !k || !v || !g || !beta || !o))
-        return KDA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, g, o, S0, S_T};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p))
+    kda::Snapshots snap;
+    if (n_snaps > 0) {
+        if (!snaps)
             return KDA_ERR_INVALID;
-    // S_T may be S0 itself; a partial overlap would let one head's write race
-    // with another head's read.
-    if (S0 && S_T && S0 != S_T) {
-        const char *a = reinterpret_cast<const char *>(S0), *b = reinterpret_cast<const char *>(S_T);
-        const long long bytes = (long long)B * H * dk * dv * 4;
-        if (a < b + bytes && b < a + bytes)
-            return KDA_ERR_INVALID;
+        snap.out = snaps;
+        snap.every_chunks = snap_every / chunk;
+        snap.count = n_snaps;
     }
-    hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
-                                         dtype == KDA_FP32, chunk,
-                                         reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, snap, stream);
 }
 
 int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,

@@ -5,15 +5,24 @@
 
 namespace kda {
 
+// Intermediate states a prefill writes: snapshot s (s < count) is the state
+// after the first (s + 1) * every_chunks chunks, at out + s * B*H*dk*dv.
+struct Snapshots {
+    float *out = nullptr;
+    int every_chunks = 0;
+    int count = 0;
+};
+
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *S0, void *o, float *S_T,
                             int B, int T, int H, int dk, int dv, bool fp32, int chunk,
-                            hipStream_t stream);
+                            const Snapshots &snap, hipStream_t stream);
 
 // chunk = 16: the warp-specialised kernel (kda_prefill_ws.hip)
 hipError_t launch_chunk16(const void *q, const void *k, const void *v, const void *g,
                           const void *beta, const float *S0, void *o, float *S_T,
-                          int B, int T, int H, int dk, int dv, bool fp32, hipStream_t stream);
+                          int B, int T, int H, int dk, int dv, bool fp32, const Snapshots &snap,
+                          hipStream_t stream);
 
 hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
                               const float *conv_w, void *conv_cache, int oldest_slot,

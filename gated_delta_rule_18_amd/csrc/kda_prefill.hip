@@ -171,7 +171,7 @@ template <typename E, int DK, int C>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
-    float *S_T, int T, int H, int DV, int nbh, int nsl)
+    float *S_T, float *snaps, int snap_chunks, int n_snaps, int T, int H, int DV, int nbh, int nsl)
 {
     typedef Layout<E, DK, C> L;
     typedef typename Vec<E>::v4 V4;
@@ -456,6 +456,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                     Sacc[ct] = mma16(a, bu, Sacc[ct]);
                 }
             }
+            // the state after chunk ci, when ci + 1 closes a snapshot block
+            if (snaps && (ci + 1) % snap_chunks == 0 && (ci + 1) / snap_chunks <= n_snaps) {
+                float *dst = snaps + ((long)((ci + 1) / snap_chunks - 1) * nbh + bh) * DK * DV;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        dst[(long)(16 * ct + 4 * g4 + j) * DV + col] = Sacc[ct][j];
+            }
             // O tile -> LDS staging
 #pragma unroll
             for (int rt = 0; rt < NB; ++rt)
@@ -505,7 +514,7 @@ __global__ void copy_state_kernel(const float *S0, float *S_T, long n)
 template <typename E, int DK, int C>
 hipError_t launch(const void *q, const void *k, const void *v, const void *g, const void *beta,
                   const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
-                  hipStream_t stream)
+                  const Snapshots &snap, hipStream_t stream)
 {
     typedef Layout<E, DK, C> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
@@ -524,18 +533,19 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *g, co
     const int grid = ((nbh + kXCD - 1) / kXCD) * kXCD * nsl;
     hipLaunchKernelGGL((prefill_kernel<E, DK, C>), dim3(grid), dim3(kThreads), lds, stream,
                        (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
-                       (E *)o, S_T, T, H, dv, nbh, nsl);
+                       (E *)o, S_T, snap.count > 0 ? snap.out : nullptr, snap.every_chunks, snap.count,
+                       T, H, dv, nbh, nsl);
     return hipGetLastError();
 }
 
 template <typename E>
 hipError_t dispatch(int dk, int chunk, const void *q, const void *k, const void *v, const void *g,
                     const void *beta, const float *S0, void *o, float *S_T, int B, int T, int H,
-                    int dv, hipStream_t stream)
+                    int dv, const Snapshots &snap, hipStream_t stream)
 {
 #define KDA_PREFILL_CASE(D, CC)                                                         \
     if (dk == D && chunk == CC)                                                         \
-        return launch<E, D, CC>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+        return launch<E, D, CC>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
     KDA_PREFILL_CASE(128, 32)
     KDA_PREFILL_CASE(128, 16)
     KDA_PREFILL_CASE(64, 32)
@@ -548,7 +558,8 @@ hipError_t dispatch(int dk, int chunk, const void *q, const void *k, const void 
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *S0, void *o, float *S_T, int B, int T,
-                            int H, int dk, int dv, bool fp32, int chunk, hipStream_t stream)
+                            int H, int dk, int dv, bool fp32, int chunk, const Snapshots &snap,
+                            hipStream_t stream)
 {
     if ((long)B * H == 0)
         return hipSuccess;
@@ -561,10 +572,10 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const v
         return hipGetLastError();
     }
     if (chunk == 16)
-        return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, stream);
+        return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, snap, stream);
     if (fp32)
-        return dispatch<float>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
-    return dispatch<__bf16>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+        return dispatch<float>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
+    return dispatch<__bf16>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
 }
 
 } // namespace kda

@@ -325,7 +325,7 @@ template <typename E, int DK>
 __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
-    float *S_T, int T, int H, int DV, int nbh, int nsl)
+    float *S_T, float *snaps, int snap_chunks, int n_snaps, int T, int H, int DV, int nbh, int nsl)
 {
     typedef WsL<E, DK> L;
     typedef typename Vec<E>::v4 V4;
@@ -478,6 +478,15 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 Sacc[ct] = mma32(op.kr[ct], bu8, Sacc[ct]);
+            // the state after chunk c, when c + 1 closes a snapshot block
+            if (snaps && (c + 1) % snap_chunks == 0 && (c + 1) / snap_chunks <= n_snaps) {
+                float *dst = snaps + ((long)((c + 1) / snap_chunks - 1) * nbh + bh) * DK * DV;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        dst[(long)(16 * ct + 4 * g4 + j) * DV + col] = Sacc[ct][j];
+            }
             // every read of slot c is in registers (and consumed): hand it back,
             // then fetch the next chunk while the state update runs
             lds_fence();
@@ -697,7 +706,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 template <typename E, int DK>
 hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g, const void *beta,
                      const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
-                     hipStream_t stream)
+                     const Snapshots &snap, hipStream_t stream)
 {
     typedef WsL<E, DK> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
@@ -714,7 +723,8 @@ hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g,
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(kWsThreads), lds, stream,
                        (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
-                       (E *)o, S_T, T, H, dv, nbh, nsl);
+                       (E *)o, S_T, snap.count > 0 ? snap.out : nullptr, snap.every_chunks, snap.count,
+                       T, H, dv, nbh, nsl);
     return hipGetLastError();
 }
 
@@ -722,13 +732,13 @@ hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g,
 
 hipError_t launch_chunk16(const void *q, const void *k, const void *v, const void *g,
                           const void *beta, const float *S0, void *o, float *S_T, int B, int T,
-                          int H, int dk, int dv, bool fp32, hipStream_t stream)
+                          int H, int dk, int dv, bool fp32, const Snapshots &snap, hipStream_t stream)
 {
     if (fp32)
-        return dk == 128 ? launch_ws<float, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream)
-                         : launch_ws<float, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
-    return dk == 128 ? launch_ws<__bf16, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream)
-                     : launch_ws<__bf16, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, stream);
+        return dk == 128 ? launch_ws<float, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream)
+                         : launch_ws<float, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
+    return dk == 128 ? launch_ws<__bf16, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream)
+                     : launch_ws<__bf16, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
 }
 
 } // namespace kda

@@ -79,6 +79,32 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                   void *stream);
 
 /*
+ * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also writes intermediate states.
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 9, the figure on the KDA-checkpoint / MLA-hash-block prefix cache):
+ * a KDA layer keeps one recurrent state per sequence, so a cached prefix can
+ * only be resumed at token counts where that state was saved; the pages save
+ * it every 512 tokens.  Snapshot s is the state after the first
+ * (s + 1) * snap_every tokens -- exactly the S_T a kda_chunk_fwd over that
+ * prefix returns, and a valid S0 to continue from there.
+ *
+ * Arguments as kda_chunk_fwd, plus
+ *   snaps      : [n_snaps, B, H, dk, dv] fp32 (written); snaps + s*B*H*dk*dv is
+ *                snapshot s.  May be NULL when n_snaps == 0.  Must not overlap
+ *                S0 or S_T.
+ *   snap_every : tokens between snapshots, a positive multiple of `chunk`
+ *   n_snaps    : >= 0 with n_snaps * snap_every <= T
+ * Errors: KDA_ERR_INVALID for a violated condition above, else as kda_chunk_fwd.
+ * Cost: 4*dk*dv bytes written per head per snapshot on top of kda_chunk_fwd.
+ */
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *S0, void *o, float *S_T,
+                            float *snaps, int snap_every, int n_snaps,
+                            int B, int T, int H, int dk, int dv, int dtype, int chunk,
+                            void *stream);
+
+/*
  * kda_decode_step -- one generated token of one KDA layer for N sequences.
  *
  * Defines (same page, section 3.2): the decode interface

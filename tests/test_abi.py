@@ -64,6 +64,31 @@ def test_prefill_empty_batch_is_a_no_op():
     assert _prefill(H=0) == 0
 
 
+def _prefill_snap(**kw):
+    args = dict(q=A, k=A, v=A, g=A, beta=A, S0=A, o=A, S_T=A, snaps=A + (1 << 20), every=32, n=2,
+                B=1, T=64, H=2, dk=64, dv=64, dtype=0, chunk=16, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_chunk_fwd_snapshots(
+        vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]), vp(args["beta"]), vp(args["S0"]),
+        vp(args["o"]), vp(args["S_T"]), vp(args["snaps"]), args["every"], args["n"], args["B"], args["T"],
+        args["H"], args["dk"], args["dv"], args["dtype"], args["chunk"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), -1), (dict(snaps=None), -1), (dict(every=24), -1), (dict(every=0), -1),
+    (dict(n=3), -1), (dict(snaps=MIS), -1), (dict(snaps=A + 64), -1), (dict(chunk=64), -1),
+    (dict(every=64, chunk=32, n=2), -1), (dict(dk=96), -2),
+])
+def test_prefill_snapshots_rejects(kw, code):
+    assert _prefill_snap(**kw) == code
+
+
+def test_prefill_snapshots_empty_batch_is_a_no_op():
+    assert _prefill_snap(B=0, T=0, n=0, snaps=None, q=None, k=None, v=None, g=None, beta=None, o=None) == 0
+    assert _prefill_snap(H=0) == 0
+
+
 def _decode(**kw):
     args = dict(qp=A, kp=A, vp=A, w=A, cache=A, pos=0, g=A, beta=A, S=A, o=A, N=2, H=3, dk=64,
                 dv=64, width=4, dtype=0, stream=None)

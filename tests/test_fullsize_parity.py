@@ -17,15 +17,19 @@ HEADS = (0, 47, 95)
 COLS = np.arange(0, 128, 8)          # 16 of the 128 value columns
 
 
-def _oracle_segment(inp, S0_cols, heads=HEADS, cols=COLS):
+def _oracle_segment(inp, S0_cols, heads=HEADS, cols=COLS, snap_every=0, n_snaps=0):
     """Oracle on (head, column-subset) for one segment, the sampled heads run as a batch
-    (one thread each); S0_cols [n, dk, len(cols)] or None.  Returns o [n, T, c], S [n, dk, c]."""
+    (one thread each); S0_cols [n, dk, len(cols)] or None.  Returns o [n, T, c], S [n, dk, c]
+    (and snapshots [n_snaps, n, dk, c] when asked)."""
     hs = list(heads)
     sl = lambda t: np.ascontiguousarray(np.transpose(to_f64(t[0, :, hs]), (1, 0, 2))[:, :, None, :])
     q, k, g = sl(inp["q"]), sl(inp["k"]), sl(inp["g"])
     v = np.ascontiguousarray(sl(inp["v"])[..., cols])
     beta = np.ascontiguousarray(to_f64(inp["beta"][0, :, hs]).T[:, :, None])
     s0 = None if S0_cols is None else np.ascontiguousarray(S0_cols[:, None])
+    if n_snaps:
+        o, S, sn = oracle.prefill_snapshots(q, k, v, g, beta, s0, snap_every, n_snaps)
+        return o[:, :, 0], S[:, 0], sn[:, :, 0]
     o, S = oracle.prefill(q, k, v, g, beta, s0)
     return o[:, :, 0], S[:, 0]
 
@@ -47,6 +51,27 @@ def test_k3_prefill_full_size_sampled():
     # every head, every column: finite
     assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
     print(f"k3_prefill: err_o {eo:.2e} err_S {es:.2e}", flush=True)
+
+
+def test_k3_prefill_snapshots_sampled():
+    """The K3 shape with a state snapshot every 4096 tokens (16 snapshots): sampled heads
+    and columns of every snapshot against the oracle's states at those token counts."""
+    dev = torch.device("cuda:0")
+    spec = WORKLOADS["k3_prefill"]
+    inp = prefill_inputs(spec, device=dev)
+    every, n = 4096, spec.T // 4096
+    o, S_T, snaps = binding.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                                inp["S0"], every, n, chunk=16)
+    torch.cuda.synchronize()
+    S0c = np.stack([to_f64(inp["S0"][0, h])[:, COLS] for h in HEADS])
+    oo, so, sn = _oracle_segment(inp, S0c, snap_every=every, n_snaps=n)
+    ts = TOL["bf16"][1]
+    worst = 0.0
+    for s in range(n):
+        got = np.stack([to_f64(snaps[s, 0, h])[:, COLS] for h in HEADS])
+        worst = max(worst, assert_parity(got, sn[s], ts, f"k3 snapshot {s}"))
+    assert torch.isfinite(snaps).all()
+    print(f"k3 snapshots: {n} x every {every}, worst err_S {worst:.2e}", flush=True)
 
 
 @pytest.mark.slow

@@ -143,3 +143,58 @@ def test_prefill_b4h32_sampled_heads(gpu, name, chunk):
     eo = assert_parity(og, oo, to, f"{name} o")
     es = assert_parity(sg, so, ts, f"{name} S_T")
     print(f"{name} chunk {chunk}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------- snapshots --
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("chunk,every,dk,dv", [(16, 16, 128, 128), (16, 48, 64, 128), (32, 64, 128, 64),
+                                              (32, 32, 64, 64)])
+def test_snapshots_match_oracle(gpu, dtype, chunk, every, dk, dv):
+    """kda_chunk_fwd_snapshots: snapshot s against the oracle's state after (s+1)*every
+    tokens; o and S_T as kda_chunk_fwd (ragged T)."""
+    spec = PrefillSpec(B=2, H=3, T=203, dk=dk, dv=dv, dtype=dtype, seed=300 + every + dk, s0_std=0.3)
+    inp = prefill_inputs(spec, device=gpu)
+    n = spec.T // every
+    o, st, snaps = binding.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                               inp["S0"], every, n, chunk=chunk)
+    torch.cuda.synchronize()
+    oo, so, sn = oracle.prefill_snapshots(*(to_f64(inp[x]) for x in ("q", "k", "v", "g", "beta")),
+                                          to_f64(inp["S0"]), every, n)
+    to, ts = TOL[dtype]
+    assert_parity(to_f64(o), oo, to, "o")
+    assert_parity(to_f64(st), so, ts, "S_T")
+    worst = max(assert_parity(to_f64(snaps[s]), sn[s], ts, f"snapshot {s}") for s in range(n))
+    print(f"snapshots {dtype} chunk {chunk} every {every}: {n} snaps, worst err {worst:.2e}", flush=True)
+    # o and S_T are unchanged by taking snapshots (same kernel arithmetic, bitwise)
+    o2, st2 = _run(inp, chunk)
+    assert torch.equal(o, o2) and torch.equal(st, st2)
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_snapshot_is_the_prefix_final_state(gpu, chunk):
+    """A snapshot is bitwise the S_T of the same kernel run over that prefix, and a
+    prefill of the suffix started from it continues the sequence."""
+    spec = PrefillSpec(B=1, H=4, T=256, dk=128, dv=128, seed=41, s0_std=0.2)
+    inp = prefill_inputs(spec, device=gpu)
+    o, st, snaps = binding.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                               inp["S0"], 64, 4, chunk=chunk)
+    pre = {n: inp[n][:, :128].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    _, st_pre = binding.chunk_fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], inp["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(st_pre, snaps[1])
+    assert torch.equal(snaps[3], st)
+    suf = {n: inp[n][:, 128:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    o_suf, st_suf = binding.chunk_fwd(suf["q"], suf["k"], suf["v"], suf["g"], suf["beta"], snaps[1].contiguous(),
+                                      chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o_suf, o[:, 128:]) and torch.equal(st_suf, st)
+
+
+def test_snapshots_none_requested_equals_plain_prefill(gpu):
+    spec = PrefillSpec(B=1, H=2, T=80, dk=128, dv=128, seed=42)
+    inp = prefill_inputs(spec, device=gpu)
+    o, st, snaps = binding.chunk_fwd_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                               inp["S0"], 16, 0, chunk=16)
+    o2, st2 = _run(inp, 16)
+    assert snaps is None and torch.equal(o, o2) and torch.equal(st, st2)
