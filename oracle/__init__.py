@@ -15,6 +15,12 @@ prefill(q, k, v, g, beta, S0=None, nthreads=None) -> (o, S_T)
 prefill_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, nthreads=None) -> (o, S_T, snaps)
     as prefill, plus snaps [n_snaps,B,H,dk,dv]: snapshot s is the state after the
     first (s + 1) * snap_every tokens.
+prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit,
+             eps=1e-6, nthreads=None) -> (q, k, v, g, beta, conv_final)
+    q_pre, k_pre, z [B,T,H,dk]; v_pre [B,T,H,dv]; beta_logit [B,T,H];
+    conv_w [H,2dk+dv,width]; A [H]; conv_init [B,H,width-1,2dk+dv] (oldest
+    first) or None for a zero history.  conv_final holds the last width-1
+    pre-activations, oldest first.
 decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
             eps=1e-6, nthreads=None) -> o
     conv_cache and S are updated in place (they must be float64 C-contiguous
@@ -44,6 +50,9 @@ def _load():
         lib.kda_oracle_prefill.argtypes = [_dp] * 8 + [ctypes.c_long] * 5 + [ctypes.c_int]
         lib.kda_oracle_prefill_snapshots.restype = ctypes.c_int
         lib.kda_oracle_prefill_snapshots.argtypes = [_dp] * 9 + [ctypes.c_long] * 7 + [ctypes.c_int]
+        lib.kda_oracle_prefill_prep.restype = ctypes.c_int
+        lib.kda_oracle_prefill_prep.argtypes = (
+            [_dp] * 14 + [ctypes.c_long] * 6 + [ctypes.c_double, ctypes.c_int])
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = (
             [_dp] * 5 + [ctypes.c_long] + [_dp] * 4 + [ctypes.c_long] * 5 + [ctypes.c_double, ctypes.c_int])
@@ -100,6 +109,32 @@ def prefill_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, nthreads=None):
     if rc != 0:
         raise RuntimeError(f"kda_oracle_prefill_snapshots failed ({rc})")
     return o, S_T, snaps
+
+
+def prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit,
+                 eps=L2NORM_EPS, nthreads=None):
+    q_pre, k_pre, v_pre, conv_w, z, A, beta_logit = (
+        _f64(x) for x in (q_pre, k_pre, v_pre, conv_w, z, A, beta_logit))
+    B, T, H, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    width = conv_w.shape[-1]
+    nch = 2 * dk + dv
+    init = None if conv_init is None else _f64(conv_init)
+    if (k_pre.shape != q_pre.shape or z.shape != q_pre.shape or v_pre.shape != (B, T, H, dv)
+            or beta_logit.shape != (B, T, H) or conv_w.shape != (H, nch, width) or A.shape != (H,)
+            or (init is not None and init.shape != (B, H, width - 1, nch))):
+        raise ValueError("oracle.prefill_prep: inconsistent shapes")
+    q, k, g = (np.empty((B, T, H, dk)) for _ in range(3))
+    v = np.empty((B, T, H, dv))
+    beta = np.empty((B, T, H))
+    conv_final = np.empty((B, H, width - 1, nch))
+    rc = _load().kda_oracle_prefill_prep(
+        _ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(init), _ptr(z), _ptr(A),
+        _ptr(beta_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_final),
+        B, T, H, dk, dv, width, float(eps), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prefill_prep failed ({rc})")
+    return q, k, v, g, beta, conv_final
 
 
 def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,

@@ -33,6 +33,13 @@
  * tap 0 applied to the oldest token; Swish(u) = u * sigmoid(u); L2Norm(x) =
  * x / sqrt(sum x^2 + eps).
  *
+ * Prefill preprocessing applies the same input branches to a whole sequence of
+ * projected pre-activations (the conv window reaching back into a caller-given
+ * history of width-1 tokens before the first one) and adds the two scalar maps
+ * of the note: beta_t = Sigmoid(beta logit) (section 3.2) and the lower-bounded
+ * decay of section 3.3, g_t = g_min * Sigmoid(e^{A^h} z_t) with g_min = -5 and
+ * A^h one number per head.
+ *
  * Prefill can also record the state at regular token counts: the note's
  * section 9 (long-trajectory environments, the report's Figure 12 on prefix
  * caching) keeps one KDA state per sequence and layer and snapshots it only at
@@ -344,6 +351,147 @@ int kda_oracle_decode_step(const double *q_pre, const double *k_pre, const doubl
     for (int i = 0; i < nthreads; ++i)
         if (jobs[i].status)
             rc = -1;
+    free(jobs);
+    free(th);
+    return rc;
+}
+
+/* ------------------------------------------------------ prefill preprocessing -- */
+
+typedef struct {
+    const double *q_pre, *k_pre, *v_pre, *conv_w, *conv_init, *z, *A, *beta_logit;
+    double *q, *k, *v, *g, *beta, *conv_final;
+    long B, T, H, dk, dv, width;
+    double eps;
+    int tid, nthreads;
+} prep_job;
+
+static double sigmoid(double u) { return 1.0 / (1.0 + exp(-u)); }
+
+/* Pre-activation of channel c (order q | k | v) at token t of unit (b, h); t < 0
+ * reaches into the history: conv_init[b, h, (width-1) + t, c], or 0 without one. */
+static double pre_at(const prep_job *J, long b, long h, long t, long c)
+{
+    const long dk = J->dk, dv = J->dv, H = J->H, nch = 2 * dk + dv;
+    if (t < 0) {
+        if (!J->conv_init)
+            return 0.0;
+        return J->conv_init[((b * H + h) * (J->width - 1) + (J->width - 1) + t) * nch + c];
+    }
+    const long tok = (b * J->T + t) * H + h;
+    if (c < dk)
+        return J->q_pre[tok * dk + c];
+    if (c < 2 * dk)
+        return J->k_pre[tok * dk + c - dk];
+    return J->v_pre[tok * dv + c - 2 * dk];
+}
+
+/* One (b, h) unit, token by token (note, sections 3.2 and 3.3). */
+static void prep_unit(const prep_job *J, long b, long h, double *act)
+{
+    const long dk = J->dk, dv = J->dv, H = J->H, W = J->width, nch = 2 * dk + dv;
+    const double *w = J->conv_w + h * nch * W;
+    const double eA = exp(J->A[h]);
+    for (long t = 0; t < J->T; ++t) {
+        const long tok = (b * J->T + t) * H + h;
+        /* ShortConv over the window t-W+1 .. t (tap 0 = oldest), then Swish */
+        for (long c = 0; c < nch; ++c) {
+            double u = 0.0;
+            for (long j = 0; j < W; ++j)
+                u += w[c * W + j] * pre_at(J, b, h, t - (W - 1) + j, c);
+            act[c] = swish(u);
+        }
+        /* L2Norm of the q part and of the k part */
+        double sq = 0.0, sk = 0.0;
+        for (long c = 0; c < dk; ++c) {
+            sq += act[c] * act[c];
+            sk += act[dk + c] * act[dk + c];
+        }
+        const double rq = 1.0 / sqrt(sq + J->eps), rk = 1.0 / sqrt(sk + J->eps);
+        for (long c = 0; c < dk; ++c) {
+            J->q[tok * dk + c] = act[c] * rq;
+            J->k[tok * dk + c] = act[dk + c] * rk;
+        }
+        for (long c = 0; c < dv; ++c)
+            J->v[tok * dv + c] = act[2 * dk + c];
+        /* the two scalar maps */
+        J->beta[tok] = sigmoid(J->beta_logit[tok]);
+        for (long c = 0; c < dk; ++c)
+            J->g[tok * dk + c] = -5.0 * sigmoid(eA * J->z[tok * dk + c]);
+    }
+    /* the history the next call continues from: the last width-1 pre-activations */
+    if (J->conv_final)
+        for (long j = 0; j < W - 1; ++j)
+            for (long c = 0; c < nch; ++c)
+                J->conv_final[((b * H + h) * (W - 1) + j) * nch + c] =
+                    pre_at(J, b, h, J->T - (W - 1) + j, c);
+}
+
+static void *prep_worker(void *arg)
+{
+    prep_job *J = (prep_job *)arg;
+    double *act = (double *)malloc(sizeof(double) * (size_t)(2 * J->dk + J->dv));
+    if (act)
+        for (long u = J->tid; u < J->B * J->H; u += J->nthreads)
+            prep_unit(J, u / J->H, u % J->H, act);
+    free(act);
+    return act ? NULL : (void *)1;
+}
+
+/*
+ * Prefill preprocessing of B sequences of T tokens and H heads.
+ *   q_pre, k_pre, z [B,T,H,dk]; v_pre [B,T,H,dv]; beta_logit [B,T,H]
+ *   conv_w [H, 2dk+dv, width] (tap 0 = oldest); A [H]
+ *   conv_init [B,H,width-1,2dk+dv] oldest first, or NULL for a zero history
+ * Writes q, k, g [B,T,H,dk], v [B,T,H,dv], beta [B,T,H] and, when conv_final is
+ * not NULL, conv_final [B,H,width-1,2dk+dv]: the last width-1 pre-activations,
+ * oldest first (reaching into conv_init when T < width-1).  conv_final must not
+ * overlap conv_init.  Returns 0, or -1 on a bad argument or failed allocation.
+ */
+int kda_oracle_prefill_prep(const double *q_pre, const double *k_pre, const double *v_pre,
+                            const double *conv_w, const double *conv_init, const double *z,
+                            const double *A, const double *beta_logit,
+                            double *q, double *k, double *v, double *g, double *beta,
+                            double *conv_final, long B, long T, long H, long dk, long dv,
+                            long width, double eps, int nthreads)
+{
+    if (!q_pre || !k_pre || !v_pre || !conv_w || !z || !A || !beta_logit || !q || !k || !v ||
+        !g || !beta || B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || width < 2)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if ((long)nthreads > B * H)
+        nthreads = (int)(B * H > 0 ? B * H : 1);
+    prep_job *jobs = (prep_job *)calloc((size_t)nthreads, sizeof(prep_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        prep_job J = {q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit,
+                      q, k, v, g, beta, conv_final, B, T, H, dk, dv, width, eps, i, nthreads};
+        jobs[i] = J;
+    }
+    /* a worker whose thread could not start runs on the calling thread */
+    char *started = (char *)calloc((size_t)nthreads, 1);
+    if (started)
+        for (int i = 1; i < nthreads; ++i)
+            started[i] = pthread_create(&th[i], NULL, prep_worker, &jobs[i]) == 0;
+    if (prep_worker(&jobs[0]))
+        rc = -1;
+    for (int i = 1; i < nthreads; ++i) {
+        void *ret = NULL;
+        if (started && started[i])
+            pthread_join(th[i], &ret);
+        else
+            ret = prep_worker(&jobs[i]);
+        if (ret)
+            rc = -1;
+    }
+    free(started);
     free(jobs);
     free(th);
     return rc;

@@ -322,3 +322,139 @@ def test_snapshot_arguments_rejected():
         oracle.prefill_snapshots(q, k, v, g, beta, S0, 8, 3)   # 3 * 8 > 20
     with pytest.raises(RuntimeError):
         oracle.prefill_snapshots(q, k, v, g, beta, S0, 0, 1)
+
+
+# -------------------------------------------------------- prefill preprocessing --
+
+def _prep_inputs(rng, B, T, H, dk, dv, W=4, history=True):
+    nch = 2 * dk + dv
+    qp = rng.standard_normal((B, T, H, dk))
+    kp = rng.standard_normal((B, T, H, dk))
+    vp = rng.standard_normal((B, T, H, dv))
+    w = 0.5 * rng.standard_normal((H, nch, W))
+    init = rng.standard_normal((B, H, W - 1, nch)) if history else None
+    z = 2.0 * rng.standard_normal((B, T, H, dk))
+    A = rng.standard_normal(H)
+    bl = 2.0 * rng.standard_normal((B, T, H))
+    return qp, kp, vp, w, init, z, A, bl
+
+
+def test_gate_and_beta_worked_values():
+    """Hand-derived values where Sigmoid lands on an exact ratio (note, sections 3.2 and 3.3)."""
+    with open(os.path.join(GOLDEN, "gate_beta_worked.json")) as f:
+        gd = json.load(f)
+    n = len(gd["gate"])
+    H, dk, dv = n, 4, 2
+    rng = np.random.default_rng(31)
+    qp, kp, vp, w, init, _, _, _ = _prep_inputs(rng, 1, 1, H, dk, dv)
+    A = np.array([math.log(e["eA"]) for e in gd["gate"]])
+    z = np.empty((1, 1, H, dk))
+    for h, e in enumerate(gd["gate"]):
+        z[0, 0, h, :] = e["z_factor"] * math.log(e["z_ln_arg"])
+    bl = np.array([[[e["logit_factor"] * math.log(e["logit_ln_arg"])
+                     for e in (gd["beta"] * H)[:H]]]])
+    _, _, _, g, beta, _ = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    for h, e in enumerate(gd["gate"]):
+        np.testing.assert_allclose(g[0, 0, h], e["g"], rtol=0, atol=1e-14)
+    for h in range(H):
+        np.testing.assert_allclose(beta[0, 0, h], (gd["beta"] * H)[h]["beta"], rtol=0, atol=1e-15)
+
+
+def test_gate_range_and_monotonicity():
+    """g lies in (-5, 0), falls as z grows (for any A), and z = 0 gives -5/2 for every A."""
+    rng = np.random.default_rng(32)
+    H, dk, dv = 3, 64, 2
+    qp, kp, vp, w, init, _, _, bl = _prep_inputs(rng, 1, 1, H, dk, dv)
+    A = np.array([-2.0, 0.0, 1.5])
+    zs = np.linspace(-8, 8, dk)
+    z = np.broadcast_to(zs, (1, 1, H, dk)).copy()
+    z[0, 0, :, dk // 2] = 0.0
+    _, _, _, g, _, _ = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    g = g[0, 0]
+    assert np.all(g > -5.0) and np.all(g < 0.0)
+    np.testing.assert_allclose(g[:, dk // 2], -2.5, rtol=0, atol=1e-15)
+    order = np.argsort(z[0, 0, 0], kind="stable")
+    assert np.all(np.diff(g[:, order], axis=1) <= 0)
+    # a larger A sharpens the map: further from -5/2 at the same z != 0
+    far = np.abs(g + 2.5)
+    nz = z[0, 0, 0] != 0
+    assert np.all(far[2, nz] > far[1, nz]) and np.all(far[1, nz] > far[0, nz])
+
+
+@pytest.mark.parametrize("history", [True, False])
+def test_prep_matches_library_routines(history):
+    """Conv by np.convolve, Swish by torch's silu, L2Norm by np.linalg.norm, sigmoids by
+    scipy's expit (note, section 3.2 input branches; section 3.3 gate)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(33)
+    B, T, H, dk, dv, W = 2, 9, 3, 8, 6, 4
+    qp, kp, vp, w, init, z, A, bl = _prep_inputs(rng, B, T, H, dk, dv, W, history)
+    q, k, v, g, beta, fin = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    nch = 2 * dk + dv
+    x = np.concatenate([qp, kp, vp], axis=-1)                       # [B, T, H, nch]
+    hist = np.zeros((B, H, W - 1, nch)) if init is None else init
+    seq = np.concatenate([np.transpose(hist, (0, 2, 1, 3)), x], axis=1)  # [B, W-1+T, H, nch]
+    u = np.empty_like(x)
+    for b in range(B):
+        for h in range(H):
+            for c in range(nch):
+                u[b, :, h, c] = np.convolve(seq[b, :, h, c], w[h, c, ::-1], mode="valid")
+    s = torch.nn.functional.silu(torch.from_numpy(u)).numpy()
+    eq = s[..., :dk] / np.sqrt(np.linalg.norm(s[..., :dk], axis=-1, keepdims=True) ** 2 + oracle.L2NORM_EPS)
+    ek = s[..., dk:2 * dk] / np.sqrt(np.linalg.norm(s[..., dk:2 * dk], axis=-1, keepdims=True) ** 2
+                                     + oracle.L2NORM_EPS)
+    _close(q, eq, 1e-13)
+    _close(k, ek, 1e-13)
+    _close(v, s[..., 2 * dk:], 1e-13)
+    _close(beta, expit(bl), 1e-15)
+    _close(g, -5.0 * expit(np.exp(A)[None, None, :, None] * z), 1e-14)
+    np.testing.assert_array_equal(fin, np.transpose(seq[:, -(W - 1):], (0, 2, 1, 3)))
+
+
+def test_prep_split_resumes_through_conv_final():
+    """Preprocessing T tokens at once equals two calls joined by conv_final -> conv_init,
+    also when the second call is shorter than the conv history."""
+    rng = np.random.default_rng(34)
+    B, T, H, dk, dv = 2, 11, 2, 8, 4
+    qp, kp, vp, w, init, z, A, bl = _prep_inputs(rng, B, T, H, dk, dv)
+    full = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    for t1 in (0, 1, 5, 9, 10):
+        cut = lambda a, sl: np.ascontiguousarray(a[:, sl])
+        first = oracle.prefill_prep(cut(qp, slice(0, t1)), cut(kp, slice(0, t1)), cut(vp, slice(0, t1)),
+                                    w, init, cut(z, slice(0, t1)), A, cut(bl, slice(0, t1)))
+        second = oracle.prefill_prep(cut(qp, slice(t1, T)), cut(kp, slice(t1, T)), cut(vp, slice(t1, T)),
+                                     w, first[5], cut(z, slice(t1, T)), A, cut(bl, slice(t1, T)))
+        for i in range(5):
+            np.testing.assert_array_equal(np.concatenate([first[i], second[i]], axis=1), full[i])
+        np.testing.assert_array_equal(second[5], full[5])
+
+
+def test_prep_then_prefill_equals_decode_steps():
+    """The decode oracle (pinned separately against library routines) stepped token by token
+    from the same conv history reproduces prep + prefill: outputs, state and conv history."""
+    rng = np.random.default_rng(35)
+    B, T, H, dk, dv, W = 2, 7, 3, 8, 6, 4
+    qp, kp, vp, w, init, z, A, bl = _prep_inputs(rng, B, T, H, dk, dv, W)
+    q, k, v, g, beta, fin = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    S0 = 0.1 * rng.standard_normal((B, H, dk, dv))
+    o, S_T = oracle.prefill(q, k, v, g, beta, S0)
+    cache = init.copy()          # ring at position 0: slot 0 holds the oldest token
+    S = S0.copy()
+    for t in range(T):
+        ot = oracle.decode_step(qp[:, t], kp[:, t], vp[:, t], w, cache, t, g[:, t], beta[:, t], S)
+        _close(ot, o[:, t], 1e-12)
+    _close(S, S_T, 1e-12)
+    # after T steps the ring's oldest slot is T mod (W-1)
+    np.testing.assert_array_equal(np.roll(cache, -(T % (W - 1)), axis=2), fin)
+
+
+def test_prep_empty_and_rejects():
+    rng = np.random.default_rng(36)
+    qp, kp, vp, w, init, z, A, bl = _prep_inputs(rng, 2, 0, 2, 4, 4)
+    q, k, v, g, beta, fin = oracle.prefill_prep(qp, kp, vp, w, init, z, A, bl)
+    assert q.shape == (2, 0, 2, 4) and beta.shape == (2, 0, 2)
+    np.testing.assert_array_equal(fin, init)
+    with pytest.raises(ValueError):
+        oracle.prefill_prep(qp, kp, vp, w, init, z, A[:1], bl)
+    with pytest.raises(ValueError):
+        oracle.prefill_prep(qp, kp, vp, w, init[:, :, :2], z, A, bl)
