@@ -10,7 +10,9 @@ torch.cuda.synchronize():
   decode   one kda_decode_step over N=256 sequences x H=96 heads, dk=dv=128,
            bf16, ShortConv width 4 (reported under "decode").
 A third phase (reported under "snapshots") times kda_chunk_fwd_snapshots on the
-prefill workload with a state snapshot every 512 tokens (128 snapshots).
+prefill workload with a state snapshot every 512 tokens (128 snapshots), and a
+fourth (reported under "prep") kda_prefill_prep on the same B=1, H=96, T=65536
+shape: projected pre-activations to q, k, v, g, beta.
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
@@ -49,6 +51,16 @@ def decode_bytes(N, H, dk, dv, W=4):
     g 2dk, beta 2, o 2dv."""
     nch = 2 * dk + dv
     return N * H * (8 * dk * dv + 2 * nch + 2 * (W - 1) * nch + 2 * nch + 2 * dk + 2 + 2 * dv)
+
+
+def prep_bytes(B, T, H, dk, dv, W=4):
+    """Algorithmic HBM bytes of one kda_prefill_prep call (bf16): per token-head the
+    pre-activations 2(2dk+dv), z 2dk and the beta logit 2 in, q, k, v, g and beta out
+    (the same sizes); per head the fp32 taps 4(2dk+dv)W and the conv history in and out
+    2 * 2(W-1)(2dk+dv)."""
+    nch = 2 * dk + dv
+    per_token_head = 2 * (2 * nch + 2 * dk + 2)
+    return B * T * H * per_token_head + H * 4 * nch * W + B * H * 4 * (W - 1) * nch
 
 
 def measured_traffic(profile, sources):
@@ -90,7 +102,7 @@ def _timed(fn, steps, warmup, torch):
     return wall, kern
 
 
-def cpu_baseline(x, H_total, heads=32, tokens=65536):
+def cpu_baseline(x, H_total, heads=96, tokens=65536):
     """Time the fp64 oracle (as it stands) on a bounded sample of the prefill workload:
     the first `heads` heads of the generated K3-shaped inputs over `tokens` tokens."""
     import oracle
@@ -131,6 +143,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-snapshots", action="store_true")
+    ap.add_argument("--skip-prep", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -143,7 +156,8 @@ def main():
     import torch
 
     from gated_delta_rule_18_amd import binding
-    from gated_delta_rule_18_amd.inputs import DECODE, WORKLOADS, decode_state, decode_step_inputs, prefill_inputs
+    from gated_delta_rule_18_amd.inputs import (DECODE, PREP_K3, WORKLOADS, decode_state, decode_step_inputs,
+                                                prefill_inputs, prep_inputs)
 
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
@@ -235,6 +249,36 @@ def main():
         }
         del st, steps_in
 
+    # ---------------- prefill preprocessing --------------------------------------
+    prep = None
+    if not args.skip_prep:
+        ps = PREP_K3
+        xp = prep_inputs(ps, device=dev)
+        outs = tuple(torch.empty(sh, dtype=torch.bfloat16, device=dev)
+                     for sh in ((ps.B, ps.T, ps.H, ps.dk), (ps.B, ps.T, ps.H, ps.dk), (ps.B, ps.T, ps.H, ps.dv),
+                                (ps.B, ps.T, ps.H, ps.dk), (ps.B, ps.T, ps.H)))
+        fin = torch.empty_like(xp["conv_init"])
+        torch.cuda.synchronize()
+
+        def prep_step(i=0):
+            binding.prefill_prep(xp["q_pre"], xp["k_pre"], xp["v_pre"], xp["conv_w"], xp["conv_init"], xp["z"],
+                                 xp["A"], xp["beta_logit"], out=outs, conv_final=fin)
+
+        r_wall, r_kern = _timed(prep_step, args.steps, args.warmup, torch)
+        r_bytes = prep_bytes(ps.B, ps.T, ps.H, ps.dk, ps.dv, ps.width)
+        r_gbps = r_bytes / (r_kern * 1e-3) / 1e9
+        prep = {
+            "workload": f"prefill preprocessing B{ps.B} H{ps.H} T{ps.T} dk=dv={ps.dk} bf16 ShortConv{ps.width}",
+            "ms_per_step": r_wall,
+            "kernel_ms": r_kern,
+            "tokens_per_s": ps.B * ps.T / (r_wall * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": r_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": r_gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("prep_k3_hbm_counters.txt", ["kda_prep.hip", "kda_device.h"]),
+                         "bytes_per_launch": r_bytes},
+        }
+        del xp, outs, fin
+
     line = {
         "metric": "KDA prefill tokens/s & TFLOP/s (% MFMA peak); decode-step HBM GB/s (% peak)",
         "value": B * T / (p_wall * 1e-3),
@@ -262,6 +306,7 @@ def main():
                      "bytes_per_launch": p_bytes},
         "decode": decode,
         "snapshots": snapshots,
+        "prep": prep,
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -7,6 +7,8 @@ the calls raise (there is no fallback).
     o, S_T        = chunk_fwd(q, k, v, g, beta, S0=None, chunk=16)
     o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=16)
     o             = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
+    q, k, v, g, beta, conv_final = prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A,
+                                                beta_logit)
 
 Shapes and dtypes follow include/kda.h: bf16 activations with an fp32 state,
 or fp32 everywhere (test mode).
@@ -21,7 +23,8 @@ library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_strerror", "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_prefill_prep",
+           "kda_strerror", "kda_version")
 
 _lib = None
 
@@ -47,6 +50,8 @@ def lib():
         L.kda_chunk_fwd_snapshots.argtypes = [vp] * 9 + [i] * 9 + [vp]
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
+        L.kda_prefill_prep.restype = i
+        L.kda_prefill_prep.argtypes = [vp] * 14 + [i] * 7 + [vp]
         L.kda_strerror.restype = ctypes.c_char_p
         L.kda_strerror.argtypes = [i]
         L.kda_version.restype = i
@@ -166,3 +171,41 @@ def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o
                                W, code, _stream(dev))
     _check(rc)
     return o
+
+
+def prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, out=None,
+                 conv_final=None, return_final=True):
+    """Prefill preprocessing.  q_pre, k_pre, z [B,T,H,dk]; v_pre [B,T,H,dv]; beta_logit [B,T,H];
+    conv_w fp32 [H,2dk+dv,W]; conv_init [B,H,W-1,2dk+dv] or None (zero history); A fp32 [H].
+    Returns (q, k, v, g, beta, conv_final); conv_final may be passed as conv_init itself.
+    `out` may supply preallocated (q, k, v, g, beta)."""
+    B, T, H, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    W = conv_w.shape[-1]
+    nch = 2 * dk + dv
+    dev, dt = q_pre.device, q_pre.dtype
+    code = _dtype_code(q_pre)
+    for name, t, shp in (("q_pre", q_pre, (B, T, H, dk)), ("k_pre", k_pre, (B, T, H, dk)),
+                         ("z", z, (B, T, H, dk)), ("v_pre", v_pre, (B, T, H, dv)),
+                         ("beta_logit", beta_logit, (B, T, H))):
+        _want(t, name, shp, dt, dev)
+    _want(conv_w, "conv_w", (H, nch, W), torch.float32, dev)
+    _want(A, "A", (H,), torch.float32, dev)
+    if conv_init is not None:
+        _want(conv_init, "conv_init", (B, H, W - 1, nch), dt, dev)
+    shapes = ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk), (B, T, H))
+    if out is None:
+        out = tuple(torch.empty(s, dtype=dt, device=dev) for s in shapes)
+    else:
+        for name, t, s in zip(("q", "k", "v", "g", "beta"), out, shapes):
+            _want(t, name, s, dt, dev)
+    if conv_final is None and return_final:
+        conv_final = torch.empty((B, H, W - 1, nch), dtype=dt, device=dev)
+    elif conv_final is not None:
+        _want(conv_final, "conv_final", (B, H, W - 1, nch), dt, dev)
+    q, k, v, g, beta = out
+    rc = lib().kda_prefill_prep(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(conv_init),
+                                _ptr(z), _ptr(A), _ptr(beta_logit), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(conv_final), B, T, H, dk, dv, W, code, _stream(dev))
+    _check(rc)
+    return q, k, v, g, beta, conv_final

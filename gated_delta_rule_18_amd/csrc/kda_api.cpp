@@ -135,4 +135,51 @@ int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, con
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                     const void *conv_init, const void *z, const float *A, const void *beta_logit,
+                     void *q, void *k, void *v, void *g, void *beta, void *conv_final, int B, int T,
+                     int H, int dk, int dv, int width, int dtype, void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (width != 4)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk) || !head_ok(dv))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40) || B > 65535 || H > 65535)
+        return KDA_ERR_INVALID;
+    if ((long long)B * H == 0)
+        return KDA_OK;
+    if (!conv_w || !A)
+        return KDA_ERR_INVALID;
+    const bool has_tokens = T > 0;
+    if (has_tokens && (!q_pre || !k_pre || !v_pre || !z || !beta_logit || !q || !k || !v || !g || !beta))
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q_pre, k_pre, v_pre, conv_w, conv_init, z, q, k, v, g, conv_final};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDA_ERR_INVALID;
+    const long long es = dtype == KDA_FP32 ? 4 : 2;
+    const long long nk = (long long)B * T * H * dk * es, nv = (long long)B * T * H * dv * es;
+    const long long nb = (long long)B * T * H * es, nc = (long long)B * H * (width - 1) * (2 * dk + dv) * es;
+    const void *in[] = {q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit};
+    const long long in_n[] = {nk, nk, nv, (long long)H * (2 * dk + dv) * width * 4, nc, nk, (long long)H * 4, nb};
+    const void *out[] = {q, k, v, g, beta, conv_final};
+    const long long out_n[] = {nk, nk, nv, nk, nb, nc};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 8; ++j)
+            if (!(i == 5 && j == 4 && out[i] == in[j]) && overlap(out[i], out_n[i], in[j], in_n[j]))
+                return KDA_ERR_INVALID;
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out_n[i], out[j], out_n[j]))
+                return KDA_ERR_INVALID;
+    }
+    hipError_t e = kda::launch_prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit,
+                                            q, k, v, g, beta, conv_final, B, T, H, dk, dv,
+                                            dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 } // extern "C"

@@ -29,4 +29,10 @@ hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *
                               const void *g, const void *beta, float *S, void *o,
                               int N, int H, int dk, int dv, bool fp32, hipStream_t stream);
 
+hipError_t launch_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
+                               const float *conv_w, const void *conv_init, const void *z,
+                               const float *A, const void *beta_logit, void *q, void *k, void *v,
+                               void *g, void *beta, void *conv_final, int B, int T, int H, int dk,
+                               int dv, bool fp32, hipStream_t stream);
+
 } // namespace kda

@@ -13,6 +13,7 @@ Workloads (shapes as named; every value is synthetic):
   k3_prefill     B=1  H=96 T=65536  d=128  bf16  + 10% of tokens g=-4.99   seed 2
   stream_1m      16 segments of k3_prefill's shape, state carried          seed 3000+s
   decode         N=256 H=96 d=128, 64 steps, bf16                          seed 4000+step
+  k3_prep        B=1  H=96 T=65536  d=128  bf16  prefill preprocessing     seed 5
 Long-memory variants (make the state matter across chunks):
   L1  tiny_fp32 shape, g = -5 sigmoid(N(0,1) - 7), upper half of the key channels g = 0
   L2  prefill_b4h32 shape with the L1 gate distribution
@@ -20,7 +21,8 @@ Long-memory variants (make the state matter across chunks):
 
 Draw order per call: q, k, v, beta logits, g logits, S0, then the bound mask
 (k3_prefill only).  Decode state: conv weights, conv cache, S.  Decode step:
-q_pre, k_pre, v_pre, beta logits, g logits.
+q_pre, k_pre, v_pre, beta logits, g logits.  Prefill preprocessing: conv weights,
+A, conv history, then q_pre, k_pre, v_pre, z, beta logits.
 """
 from dataclasses import dataclass, field
 
@@ -61,6 +63,19 @@ class DecodeSpec:
     gate: str = "standard"
 
 
+@dataclass(frozen=True)
+class PrepSpec:
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    width: int = 4
+    dtype: str = "bf16"
+    seed: int = 5
+    history: bool = True         # False -> conv_init is None (zero history)
+
+
 WORKLOADS = {
     "tiny_fp32": PrefillSpec(B=1, H=2, T=256, dk=64, dv=64, dtype="fp32", seed=0, s0_std=0.0, chunk=16),
     "prefill_b4h32": PrefillSpec(B=4, H=32, T=4096, dk=128, dv=128, seed=1),
@@ -71,6 +86,7 @@ WORKLOADS = {
     "L3": PrefillSpec(B=4, H=32, T=4096, dk=128, dv=128, seed=13, s0_std=1.0, gate="const",
                       g_const=-1e-3, beta_zero=True),
 }
+PREP_K3 = PrepSpec(B=1, T=65536, H=96, dk=128, dv=128, seed=5)
 STREAM_1M = dict(base=WORKLOADS["k3_prefill"], segments=16, seed_base=3000)
 DECODE = DecodeSpec(N=256, H=96, dk=128, dv=128)
 
@@ -166,6 +182,26 @@ def decode_step_inputs(spec: DecodeSpec, step: int, device="cpu", N=None):
         raise ValueError(spec.gate)
     return dict(q_pre=q.to(dt).contiguous(), k_pre=k.to(dt).contiguous(), v_pre=v.to(dt).contiguous(),
                 g=g.to(dt).contiguous(), beta=beta.to(dt).contiguous())
+
+
+def prep_inputs(spec: PrepSpec, device="cpu", seed=None, T=None):
+    """Prefill-preprocessing inputs: conv_w fp32 [H, 2dk+dv, width] ~ 0.5 N(0,1);
+    A fp32 [H] ~ N(0,1); conv_init [B, H, width-1, 2dk+dv] ~ N(0,1) (or None);
+    q_pre, k_pre, z [B,T,H,dk], v_pre [B,T,H,dv], beta_logit [B,T,H] ~ N(0,1)."""
+    seed = spec.seed if seed is None else seed
+    T = spec.T if T is None else T
+    B, H, dk, dv, W = spec.B, spec.H, spec.dk, spec.dv, spec.width
+    nch = 2 * dk + dv
+    dt = torch_dtype(spec.dtype)
+    gen = _gen(device, seed)
+    conv_w = 0.5 * _randn((H, nch, W), gen, device)
+    A = _randn((H,), gen, device)
+    init = _randn((B, H, W - 1, nch), gen, device).to(dt).contiguous() if spec.history else None
+    x = {n: _randn(shp, gen, device).to(dt).contiguous()
+         for n, shp in (("q_pre", (B, T, H, dk)), ("k_pre", (B, T, H, dk)), ("v_pre", (B, T, H, dv)),
+                        ("z", (B, T, H, dk)), ("beta_logit", (B, T, H)))}
+    x.update(conv_w=conv_w.contiguous(), A=A.contiguous(), conv_init=init)
+    return x
 
 
 def to_f64(t):

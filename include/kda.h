@@ -136,6 +136,47 @@ int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
                     int N, int H, int dk, int dv, int width, int dtype,
                     void *stream);
 
+/*
+ * kda_prefill_prep -- prefill preprocessing: projected pre-activations to the
+ * q, k, v, g, beta that kda_chunk_fwd consumes.
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.2, input-branch equations, applied to every token of a sequence;
+ * section 3.3, lower-bounded decay equation):
+ *   q_t = L2Norm(Swish(ShortConv(q_pre)_t)),  k_t likewise,
+ *   v_t = Swish(ShortConv(v_pre)_t),
+ *   beta_t = Sigmoid(beta_logit_t),
+ *   g_t = -5 * Sigmoid(e^{A[h]} * z_t)       (so g lies in (-5, 0) by construction)
+ * with the ShortConv, Swish and L2Norm readings of kda_decode_step.  The conv
+ * window of the first tokens reaches into `conv_init`, the 3 pre-activations
+ * before token 0; the call returns in `conv_final` the last 3, so a following
+ * prefill segment (conv_init = conv_final) or a decode loop (conv_cache =
+ * conv_final with conv_pos = 0) continues the sequence.
+ *
+ *   q_pre, k_pre, z : [B, T, H, dk]  (dtype)   projections; z feeds the gate
+ *   v_pre           : [B, T, H, dv]  (dtype)
+ *   conv_w          : [H, 2dk+dv, width] fp32  taps, channel order q | k | v, tap 0 = oldest
+ *   conv_init       : [B, H, width-1, 2dk+dv] (dtype), oldest first; NULL = zero history
+ *   A               : [H] fp32                 per-head gate scale exponent A^h
+ *   beta_logit      : [B, T, H]      (dtype)
+ *   q, k, g         : [B, T, H, dk]  (dtype)   written
+ *   v               : [B, T, H, dv]  (dtype)   written
+ *   beta            : [B, T, H]      (dtype)   written
+ *   conv_final      : [B, H, width-1, 2dk+dv] (dtype), written, oldest first; NULL = not
+ *                     returned.  May equal conv_init (in-place streaming); no other
+ *                     output may overlap an input.
+ *   width           : 4;  dk, dv : 64 or 128
+ * Errors: KDA_ERR_INVALID (null required pointer, bad size/width/dtype,
+ * misaligned buffer, overlapping buffers), KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH.
+ * conv_w and A are required whenever B*H > 0; the sequence tensors when B*T*H > 0.
+ */
+int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
+                     const float *conv_w, const void *conv_init, const void *z,
+                     const float *A, const void *beta_logit,
+                     void *q, void *k, void *v, void *g, void *beta, void *conv_final,
+                     int B, int T, int H, int dk, int dv, int width, int dtype,
+                     void *stream);
+
 /* Human-readable text for a kda_status code (static storage, never NULL). */
 const char *kda_strerror(int status);
 

@@ -112,6 +112,37 @@ def test_decode_empty_is_a_no_op():
     assert _decode(N=0, S=None) == 0
 
 
+def _prep(**kw):
+    big = 1 << 24      # separate fake regions for every output: no overlap unless asked for
+    args = dict(qp=A, kp=A, vp=A, w=A, init=A, z=A, Ah=A, bl=A, q=A + big, k=A + 2 * big,
+                v=A + 3 * big, g=A + 4 * big, beta=A + 5 * big, fin=A + 6 * big, B=1, T=8, H=2,
+                dk=64, dv=64, width=4, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    n = ("qp", "kp", "vp", "w", "init", "z", "Ah", "bl", "q", "k", "v", "g", "beta", "fin")
+    return binding.lib().kda_prefill_prep(*(vp(args[a]) for a in n), args["B"], args["T"], args["H"],
+                                          args["dk"], args["dv"], args["width"], args["dtype"],
+                                          args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(width=3), -1), (dict(dtype=5), -1), (dict(T=-1), -1), (dict(dk=96), -2), (dict(dv=32), -2),
+    (dict(qp=None), -1), (dict(bl=None), -1), (dict(w=None), -1), (dict(Ah=None), -1),
+    (dict(g=None), -1), (dict(q=MIS), -1), (dict(init=MIS), -1),
+    (dict(k=A + (1 << 24) + 64), -1),        # k overlaps q
+    (dict(v=A + 64), -1),                    # an output overlapping an input
+    (dict(fin=A + 64), -1),                  # conv_final partly overlapping conv_init
+])
+def test_prep_rejects(kw, code):
+    assert _prep(**kw) == code
+
+
+def test_prep_accepts_in_place_history_and_empty_batch():
+    # conv_final == conv_init exactly is allowed; nothing is launched for B*H == 0
+    assert _prep(B=0, fin=A) == 0
+    assert _prep(H=0, qp=None, w=None) == 0
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 4, 1, 64)

@@ -1,0 +1,135 @@
+"""GPU prefill preprocessing (kda_prefill_prep through the C ABI) against the fp64 CPU
+oracle: q, k, v, g, beta elementwise, the returned conv history bit-exactly, and the
+preprocessing chained into kda_chunk_fwd against the oracle's prep + prefill."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_18_amd import binding
+from gated_delta_rule_18_amd.inputs import PREP_K3, PrepSpec, prep_inputs, to_f64
+from tests.util import TOL, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "beta")
+
+
+def _bar(dtype):
+    """Elementwise bar: bf16 outputs are rounded to nearest (relative error <= 2^-9), so
+    |got - ref| <= 2^-8 |ref| + 1e-5 |ref|_inf covers the rounding plus fp32 work before it;
+    fp32 mode: 1e-5 |ref|_inf."""
+    return (2.0 ** -8, 1e-5) if dtype == "bf16" else (0.0, 1e-5)
+
+
+def assert_close_elementwise(got, ref, dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    rel, absr = _bar(dtype)
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    excess = np.abs(got - ref) - (rel * np.abs(ref) + absr * scale)
+    worst = float(excess.max()) if ref.size else -1.0
+    assert worst <= 0.0, f"{what}: exceeds the bar by {worst:.3e} (scale {scale:.3e})"
+    return float((np.abs(got - ref) / max(scale, 1e-30)).max()) if ref.size else 0.0
+
+
+def _oracle(x):
+    f = lambda n: None if x[n] is None else to_f64(x[n])
+    return oracle.prefill_prep(f("q_pre"), f("k_pre"), f("v_pre"), f("conv_w"), f("conv_init"),
+                               f("z"), f("A"), f("beta_logit"))
+
+
+def _gpu(x, **kw):
+    return binding.prefill_prep(x["q_pre"], x["k_pre"], x["v_pre"], x["conv_w"], x["conv_init"],
+                                x["z"], x["A"], x["beta_logit"], **kw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T,history", [(200, True), (131, False), (2, True), (64, True)])
+def test_prep_small(gpu, dtype, dk, dv, T, history):
+    """Several 64-token tiles with a ragged tail, T shorter than the conv history, and an
+    exact tile; with and without a caller-given history."""
+    spec = PrepSpec(B=2, T=T, H=3, dk=dk, dv=dv, dtype=dtype, seed=100 + T, history=history)
+    x = prep_inputs(spec, device=gpu)
+    out = _gpu(x)
+    torch.cuda.synchronize()
+    ref = _oracle(x)
+    errs = [assert_close_elementwise(to_f64(o), r, dtype, n) for n, o, r in zip(NAMES, out, ref)]
+    np.testing.assert_array_equal(to_f64(out[5]), ref[5])
+    print(f"prep {dtype} dk{dk} dv{dv} T{T}: max rel err q/k/v/g/beta "
+          + " ".join(f"{e:.1e}" for e in errs), flush=True)
+
+
+def test_prep_empty_sequence_returns_history(gpu):
+    x = prep_inputs(PrepSpec(B=2, T=0, H=3, dk=128, dv=128, seed=7), device=gpu)
+    out = _gpu(x)
+    torch.cuda.synchronize()
+    assert out[0].shape == (2, 0, 3, 128)
+    assert torch.equal(out[5], x["conv_init"])
+    x0 = prep_inputs(PrepSpec(B=2, T=0, H=3, dk=128, dv=128, seed=7, history=False), device=gpu)
+    out0 = _gpu(x0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out0[5].float()) == 0
+
+
+def test_prep_split_resume_and_in_place_history(gpu):
+    """One call over T tokens equals two calls joined by conv_final -> conv_init, bit for bit,
+    also when the history is carried in place (conv_final = conv_init)."""
+    spec = PrepSpec(B=2, T=300, H=4, dk=128, dv=128, seed=9)
+    x = prep_inputs(spec, device=gpu)
+    full = _gpu(x)
+    for t1 in (1, 2, 64, 100, 299):
+        cut = lambda n, s: x[n][:, s].contiguous()
+        a = {n: cut(n, slice(0, t1)) for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit")}
+        b = {n: cut(n, slice(t1, None)) for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit")}
+        hist = x["conv_init"].clone()
+        for part in (a, b):
+            part.update(conv_w=x["conv_w"], A=x["A"], conv_init=hist)
+        ra = _gpu(a, conv_final=hist)          # in place
+        rb = _gpu(b, conv_final=hist)
+        torch.cuda.synchronize()
+        for i, n in enumerate(NAMES):
+            assert torch.equal(torch.cat([ra[i], rb[i]], 1), full[i]), (t1, n)
+        assert torch.equal(hist, full[5]), t1
+
+
+def test_prep_then_prefill_matches_oracle(gpu):
+    """kda_prefill_prep -> kda_chunk_fwd equals the oracle's prep -> prefill on the same
+    pre-activations (the state-carrying parity bar of the recurrence)."""
+    spec = PrepSpec(B=2, T=333, H=3, dk=128, dv=128, seed=11)
+    x = prep_inputs(spec, device=gpu)
+    q, k, v, g, beta, _ = _gpu(x)
+    S0 = 0.02 * torch.randn((2, 3, 128, 128), generator=torch.Generator(device=gpu).manual_seed(12),
+                            device=gpu)
+    o, S_T = binding.chunk_fwd(q, k, v, g, beta, S0, chunk=16)
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb, _ = _oracle(x)
+    oo, so = oracle.prefill(rq, rk, rv, rg, rb, to_f64(S0))
+    to, ts = TOL["bf16"]
+    eo = assert_parity(to_f64(o), oo, to, "prep+prefill o")
+    es = assert_parity(to_f64(S_T), so, ts, "prep+prefill S")
+    print(f"prep -> prefill: err_o {eo:.2e} err_S {es:.2e}", flush=True)
+
+
+def test_prep_k3_full_size_sampled(gpu):
+    """B1 H96 T65536 d128 bf16, in the launch bench.py times: three heads against the oracle
+    over the whole sequence, and properties of every output at full size."""
+    x = prep_inputs(PREP_K3, device=gpu)
+    out = _gpu(x)
+    torch.cuda.synchronize()
+    q, k, v, g, beta, fin = out
+    # properties at any size: unit q, k; g in [-5, 0]; beta in [0, 1]
+    for t in (q, k):
+        n = t.float().norm(dim=-1)
+        assert float((n - 1).abs().max()) < 2e-2
+    assert float(g.float().max()) <= 0.0 and float(g.float().min()) >= -5.0
+    assert float(beta.float().max()) <= 1.0 and float(beta.float().min()) >= 0.0
+    for h in (0, 47, 95):
+        sub = {n: x[n][:, :, h:h + 1].contiguous() for n in ("q_pre", "k_pre", "v_pre", "z", "beta_logit")}
+        sub.update(conv_w=x["conv_w"][h:h + 1].contiguous(), A=x["A"][h:h + 1].contiguous(),
+                   conv_init=x["conv_init"][:, h:h + 1].contiguous())
+        ref = _oracle(sub)
+        for n, o, r in zip(NAMES, out, ref):
+            assert_close_elementwise(to_f64(o[:, :, h:h + 1]), r, "bf16", f"head {h} {n}")
+        np.testing.assert_array_equal(to_f64(fin[:, h:h + 1]), ref[5])
