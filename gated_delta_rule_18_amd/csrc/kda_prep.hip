@@ -14,13 +14,16 @@
 // The pass is elementwise along the sequence except for the conv window and
 // the two L2 norms, so it is bound by HBM traffic: every pre-activation is read
 // once (plus a 3-token halo per tile, served by L2) and every output written
-// once.  A workgroup of two wavefronts owns one (sequence, head, 64-token tile):
-//   wavefront 0: lanes hold 4 channels each of q (first dk/4 lanes) and k (next
-//                dk/4 lanes); the L2 norm is a reduction over the dk/4 lanes of
-//                the group.  It also maps beta for the tile's 64 tokens (lane =
-//                token).
-//   wavefront 1: lanes hold 4 channels each of v (first dv/4 lanes) and of the
-//                gate input z (next dk/4 lanes).
+// once.  A workgroup of four wavefronts owns two heads (h0, h0 + 1) of one
+// sequence over a 64-token tile; every wavefront runs one kind of work on all
+// of its lanes (no divergent roles inside a wavefront), 4 channels per lane:
+//   wavefronts 0, 1: q (first dk/4 lanes) and k (next dk/4 lanes) of head
+//                    h0 + w: conv, Swish, then the L2 norm as a reduction over
+//                    the dk/4 lanes of the group;
+//   wavefront 2:     v of h0 (lanes 0..) and of h0 + 1 (lanes 32..): conv, Swish;
+//   wavefront 3:     the gate input z of h0 (lanes 0..) and h0 + 1 (lanes 32..);
+//   wavefronts 2, 3 also map beta of the tile's tokens (lane = token) for h0
+//                    and h0 + 1 respectively.
 // A conv lane walks the tile token by token keeping its last three inputs in
 // registers; loads run 8 tokens ahead.
 #include "kda_device.h"
@@ -67,8 +70,60 @@ __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// What a wavefront's lanes compute.
+enum Role { kQK = 0, kV = 1, kGate = 2 };
+
+// The token walk of one lane over its tile: 4 channels starting at element c4
+// of a row of D elements of `src`, rows t0 .. t0 + n - 1 of unit (b, h) at
+// `base` (element offset of row t0), `step` elements between token rows.
+// kQK / kV lanes: conv over (hist, x_t) with taps w, Swish, and for kQK the L2
+// norm over the lane group of NG lanes; kGate lanes: g = -5 Sigmoid(eA z).
+template <int R, int NG, typename E>
+__device__ __forceinline__ void walk(const E *src, E *dst, long base, long step, int n, const f32x4 *w,
+                                     f32x4 *hist, float eA, bool active)
+{
+    for (int tb = 0; tb < n; tb += kU) {
+        // loads first (rows past the tile are clamped to its last token and not used)
+        f32x4 xin[kU];
+#pragma unroll
+        for (int i = 0; i < kU; ++i)
+            xin[i] = ld4(src + base + (tb + i < n ? tb + i : n - 1) * step);
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            if (tb + i >= n)
+                break;
+            f32x4 y;
+            if constexpr (R == kGate) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = kGMin * sigmoid_f(eA * xin[i][e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // explicit fused multiply-adds in a fixed order: a token's result
+                    // must not depend on where it falls in the unrolled walk
+                    const float u = __builtin_fmaf(w[3][e], xin[i][e],
+                                    __builtin_fmaf(w[2][e], hist[2][e],
+                                    __builtin_fmaf(w[1][e], hist[1][e], w[0][e] * hist[0][e])));
+                    y[e] = u * sigmoid_f(u);
+                }
+                hist[0] = hist[1];
+                hist[1] = hist[2];
+                hist[2] = xin[i];
+                if constexpr (R == kQK) {
+                    const float ss = group_sum<NG>(__builtin_fmaf(y[3], y[3], __builtin_fmaf(y[2], y[2],
+                                                   __builtin_fmaf(y[1], y[1], y[0] * y[0]))));
+                    y *= __builtin_amdgcn_rsqf(ss + kL2Eps);
+                }
+            }
+            if (active)
+                st4(dst + base + (tb + i) * step, y);
+        }
+    }
+}
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(128) void prep_kernel(
+__global__ __launch_bounds__(256) void prep_kernel(
     const E *__restrict__ q_pre, const E *__restrict__ k_pre, const E *__restrict__ v_pre,
     const float *__restrict__ conv_w, const E *conv_init, const E *__restrict__ z,
     const float *__restrict__ A, const E *__restrict__ beta_logit, E *__restrict__ q,
@@ -77,135 +132,101 @@ __global__ __launch_bounds__(128) void prep_kernel(
 {
     constexpr int NCH = 2 * DK + DV;
     constexpr int QK = DK / 4, VQ = DV / 4;     // 4-channel lanes per tensor
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    static_assert(2 * QK <= 64 && VQ <= 32 && QK <= 32, "lane budget");
+    const int tile = blockIdx.x, b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int t0 = tile * kTT;
-    const int t1 = T - t0 < kTT ? T - t0 : kTT;          // tokens in this tile (may be <= 0 only if T == 0)
+    const int n = T - t0 < kTT ? T - t0 : kTT;           // tokens in this tile (0 only when T == 0)
     const long tokb = (long)b * T;
-    const long bh = (long)b * H + h;
 
-    // ---- beta = Sigmoid(logit), lane = token ----------------------------------
-    if (wave == 0 && lane < t1) {
-        const long r = (tokb + t0 + lane) * H + h;
-        beta[r] = (E)sigmoid_f(to_f(beta_logit[r]));
-    }
-
-    // this lane's role: conv tensor (0 = q, 1 = k, 2 = v), gate (3) or idle (-1)
-    int role = -1, c4 = 0;                      // c4 = first channel within its tensor
-    if (wave == 0) {
-        if (lane < QK)
-            role = 0, c4 = 4 * lane;
-        else if (lane < 2 * QK)
-            role = 1, c4 = 4 * (lane - QK);
+    // this lane's head, tensor and first channel
+    int h, c4, cc;                                      // cc = conv channel (order q | k | v)
+    const E *src;
+    E *dst;
+    bool active;
+    if (wave < 2) {
+        h = 2 * blockIdx.y + wave;
+        const bool isk = lane >= QK;
+        c4 = 4 * (isk ? lane - QK : lane);
+        cc = isk ? DK + c4 : c4;
+        src = isk ? k_pre : q_pre;
+        dst = isk ? k : q;
+        active = lane < 2 * QK;
     } else {
-        if (lane < VQ)
-            role = 2, c4 = 4 * lane;
-        else if (lane < VQ + QK)
-            role = 3, c4 = 4 * (lane - VQ);
+        h = 2 * blockIdx.y + (lane >> 5);
+        c4 = 4 * (lane & 31);
+        cc = 2 * DK + c4;
+        src = wave == 2 ? v_pre : z;
+        dst = wave == 2 ? v : g;
+        active = c4 < (wave == 2 ? DV : DK);
     }
-    const int D = role == 2 ? DV : DK;
-    const E *src = role == 0 ? q_pre : role == 1 ? k_pre : role == 2 ? v_pre : z;
-    E *dst = role == 0 ? q : role == 1 ? k : role == 2 ? v : g;
-    const int cc = role == 0 ? c4 : role == 1 ? DK + c4 : 2 * DK + c4;   // conv channel
-    if (role < 0)
-        src = q_pre, dst = nullptr;
-    auto row = [&](int t) { return ((tokb + t) * H + h) * (long)D + c4; };
+    active = active && h < H;
+    if (!active)
+        h = 0, c4 = 0, cc = 0;                          // idle lanes read valid memory, store nothing
+    const int D = wave == 2 ? DV : DK;
+    const long bh = (long)b * H + h;
+    const long step = (long)H * D;
+    const long base = ((tokb + t0) * H + h) * (long)D + c4;
 
-    if (role == 3) {
-        // ---- gate: g = -5 Sigmoid(e^A z) ---------------------------------------
-        const float eA = expf(A[h]);
-        for (int tb = 0; tb < t1; tb += kU) {
-            f32x4 xin[kU];
-#pragma unroll
-            for (int i = 0; i < kU; ++i)
-                xin[i] = ld4(src + row(t0 + (tb + i < t1 ? tb + i : t1 - 1)));
-#pragma unroll
-            for (int i = 0; i < kU; ++i) {
-                if (tb + i >= t1)
-                    break;
-                f32x4 y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = kGMin * sigmoid_f(eA * xin[i][e]);
-                st4(dst + row(t0 + tb + i), y);
-            }
+    // ---- beta = Sigmoid(logit): wavefront 2 for h0, 3 for h0 + 1, lane = token --
+    if (wave >= 2) {
+        const int hb = 2 * blockIdx.y + wave - 2;
+        if (hb < H && lane < n) {
+            const long r = (tokb + t0 + lane) * H + hb;
+            beta[r] = (E)sigmoid_f(to_f(beta_logit[r]));
         }
+    }
+
+    if (wave == 3) {
+        walk<kGate, 32>(src, dst, base, step, n, nullptr, nullptr, expf(A[h]), active);
         return;
     }
 
     // ---- conv lanes (q, k, v): taps, history, then the token walk --------------
     f32x4 w[kW];                                // w[j][e] = tap j of channel cc + e
     f32x4 hist[kW - 1];                         // inputs of tokens t-3, t-2, t-1
-    if (role >= 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const f32x4 we = *reinterpret_cast<const f32x4 *>(conv_w + ((long)h * NCH + cc + e) * kW);
+    for (int e = 0; e < 4; ++e) {
+        const f32x4 we = *reinterpret_cast<const f32x4 *>(conv_w + ((long)h * NCH + cc + e) * kW);
 #pragma unroll
-            for (int j = 0; j < kW; ++j)
-                w[j][e] = we[j];
-        }
+        for (int j = 0; j < kW; ++j)
+            w[j][e] = we[j];
+    }
+    const E *ci = conv_init ? conv_init + bh * (kW - 1) * NCH + cc : nullptr;
 #pragma unroll
-        for (int j = 0; j < kW - 1; ++j) {
-            const int t = t0 - (kW - 1) + j;
-            if (t >= 0)
-                hist[j] = ld4(src + row(t));
-            else if (conv_init)
-                hist[j] = ld4(conv_init + (bh * (kW - 1) + (kW - 1) + t) * NCH + cc);
-            else
-                hist[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int j = 0; j < kW - 1; ++j) {
+        const int t = t0 - (kW - 1) + j;
+        if (t >= 0)
+            hist[j] = ld4(src + base + (long)(t - t0) * step);
+        else if (ci)
+            hist[j] = ld4(ci + ((kW - 1) + t) * NCH);
+        else
+            hist[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // the history the next call continues from (tile 0 only): the last 3
     // pre-activations, read before any of them is written (conv_final may be
     // conv_init itself)
     f32x4 fin[kW - 1];
-    const bool write_final = tile == 0 && conv_final && role >= 0;
+    const bool write_final = tile == 0 && conv_final;
     if (write_final) {
 #pragma unroll
         for (int j = 0; j < kW - 1; ++j) {
             const int t = T - (kW - 1) + j;
             if (t >= 0)
-                fin[j] = ld4(src + row(t));
-            else if (conv_init)
-                fin[j] = ld4(conv_init + (bh * (kW - 1) + (kW - 1) + t) * NCH + cc);
+                fin[j] = ld4(src + base + (long)(t - t0) * step);
+            else if (ci)
+                fin[j] = ld4(ci + ((kW - 1) + t) * NCH);
             else
                 fin[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 
-    for (int tb = 0; tb < t1; tb += kU) {
-        // loads first (rows past the tile are clamped to its last token and not used)
-        f32x4 xin[kU];
-#pragma unroll
-        for (int i = 0; i < kU; ++i) {
-            const int t = t0 + (tb + i < t1 ? tb + i : t1 - 1);
-            xin[i] = ld4(src + row(t));
-        }
-#pragma unroll
-        for (int i = 0; i < kU; ++i) {
-            if (tb + i >= t1)
-                break;
-            f32x4 a;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float u = w[0][e] * hist[0][e] + w[1][e] * hist[1][e] + w[2][e] * hist[2][e] +
-                                w[3][e] * xin[i][e];
-                a[e] = u * sigmoid_f(u);
-            }
-            hist[0] = hist[1];
-            hist[1] = hist[2];
-            hist[2] = xin[i];
-            // L2Norm over the group's lanes (v lanes take the same uniform path
-            // and ignore the scale)
-            float ss = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
-            ss = group_sum<QK>(ss);
-            const float r = role == 2 ? 1.0f : __builtin_amdgcn_rsqf(ss + kL2Eps);
-            if (role >= 0)
-                st4(dst + row(t0 + tb + i), a * r);
-        }
-    }
+    if (wave < 2)
+        walk<kQK, QK>(src, dst, base, step, n, w, hist, 0.f, active);
+    else
+        walk<kV, 32>(src, dst, base, step, n, w, hist, 0.f, active);
 
-    if (write_final) {
+    if (write_final && active) {
 #pragma unroll
         for (int j = 0; j < kW - 1; ++j)
             st4(conv_final + (bh * (kW - 1) + j) * NCH + cc, fin[j]);
@@ -221,7 +242,7 @@ hipError_t launch(const void *q_pre, const void *k_pre, const void *v_pre, const
     if ((long)B * H == 0)
         return hipSuccess;
     const int tiles = T > 0 ? (T + kTT - 1) / kTT : 1;
-    hipLaunchKernelGGL((prep_kernel<E, DK, DV>), dim3(tiles, H, B), dim3(128), 0, stream,
+    hipLaunchKernelGGL((prep_kernel<E, DK, DV>), dim3(tiles, (H + 1) / 2, B), dim3(256), 0, stream,
                        (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
                        (const E *)conv_init, (const E *)z, A, (const E *)beta_logit, (E *)q, (E *)k,
                        (E *)v, (E *)g, (E *)beta, (E *)conv_final, T, H);
