@@ -23,28 +23,38 @@
 // product of a_t = exp(g_t) (one exponential per element).
 //
 // Work decomposition.  A workgroup owns one (sequence, head, 64-wide value
-// slice); value columns of S never interact.  It runs 8 wavefronts:
+// slice); value columns of S never interact.  It runs 4 consumer wavefronts
+// and NP producer wavefronts (8 in bf16 mode, 4 in fp32 test mode):
 //   consumers 0..3  -- wavefront w keeps value columns [16w, 16w+16) of the
 //                      dk x 64 fp32 state in MFMA accumulators for the whole
 //                      sequence and runs the state-dependent products of every
 //                      chunk in order; o goes straight to HBM;
-//   producers 4..7  -- producer p owns chunks p, p+4, p+8, ...: it loads q, k,
-//                      g, v directly in its compute layout (lane = four key
-//                      channels x eight tokens; two chunks in flight), builds the decayed operands with in-register
-//                      running products, forms A and M on MFMA, inverts I + A by
-//                      forward substitution with A's entries read out of the
-//                      accumulators as wave-uniform operands, and publishes the
-//                      consumers' operands in a ring of NS LDS slots.
+//   producers       -- producer p owns chunks p, p+NP, p+2NP, ...: it loads q,
+//                      k, g, v directly in its compute layout (lane = four key
+//                      channels x eight tokens), builds the decayed operands
+//                      with in-register running products, forms A and M on
+//                      MFMA, the UT inverse on fp32 MFMA, and publishes the
+//                      consumers' operands in a ring of NS LDS slots; the loads
+//                      of its next chunk are issued as soon as the raw
+//                      registers of the current one are consumed.
 // Producers and consumers hand slots over through per-slot LDS flags ("ready"
 // and per-consumer "done"); every wait is bounded and a WG-wide abort flag ends
 // all waits if one ever runs out (the result is then wrong, never a hang).
+//
+// Instruction economy.  One wavefront issues at most one instruction every few
+// cycles, so the consumer's per-chunk instruction count bounds the state chain:
+// the slot holds -Kt so that X = V - Kt S accumulates straight onto V, O = Y +
+// M U accumulates onto Y, the o tile and snapshot pointers advance by fixed
+// steps, and every LDS operand read uses one base register plus an immediate.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kWsThreads = 512;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename E> struct Np { static constexpr int v = sizeof(E) == 2 ? 8 : 4; };
 constexpr int kC = 16;                 // tokens per chunk
 constexpr int kVS = 64;                // value columns per workgroup
 constexpr int kXCDs = 8;
@@ -69,7 +79,8 @@ constexpr int kVmcntZero = 0x0F70;
 template <typename E, int DK>
 struct WsL {
     static constexpr int ES = (int)sizeof(E);
-    static constexpr int NS = ES == 2 ? 8 : 3;        // LDS slots
+    static constexpr int NS = ES == 2 ? 6 : 3;        // LDS slots
+    static constexpr int NP = Np<E>::v;               // producer wavefronts
     static constexpr int GS = 136, MS = 4 * GS;       // image16 strides (elements)
     static constexpr int KS = 320;                    // image4 tile stride (elements, >= 256 + 8)
     static constexpr int NKS = DK / 32, NCT = DK / 16;
@@ -87,7 +98,7 @@ struct WsL {
     // byte offsets
     static constexpr int oSlots = 0;
     static constexpr int oProd = oSlots + NS * slotBytes;
-    static constexpr int oFlags = oProd + 4 * pBytes;
+    static constexpr int oFlags = oProd + NP * pBytes;
     static constexpr int nFlags = NS + NS * 4 + 1;    // ready[NS], done[NS][4], abort
     static constexpr int bytes = oFlags + nFlags * 4;
     static_assert(slotBytes % 32 == 0 && pBytes % 32 == 0, "alignment");
@@ -129,6 +140,13 @@ __device__ __forceinline__ void wait_flags(const int *f, int n, int stride, int 
         }
     }
     lds_fence();
+}
+
+// A volatile LDS read (never fused with a neighbouring read into a wider one).
+template <typename T>
+__device__ __forceinline__ T lds_load(const unsigned char *p)
+{
+    return *(const volatile __attribute__((address_space(3))) T *)(p);
 }
 
 // Two adjacent elements as one register-sized pack.
@@ -211,6 +229,23 @@ __device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff,
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
 
+// A 16-token tile column of o: rows 4 g4 + j (j < 4) of this lane's column,
+// row j at byte offset voff + j * stride.
+__device__ __forceinline__ void store_o(__amdgpu_buffer_rsrc_t r, int voff, int stride, f32x4 x, __bf16 *)
+{
+    const unsigned lo = Pair<__bf16>::pack(x[0], x[1]), hi = Pair<__bf16>::pack(x[2], x[3]);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)lo, r, voff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(lo >> 16), r, voff, stride, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)hi, r, voff, 2 * stride, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(hi >> 16), r, voff, 3 * stride, 0);
+}
+__device__ __forceinline__ void store_o(__amdgpu_buffer_rsrc_t r, int voff, int stride, f32x4 x, float *)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[j]), r, voff, j * stride, 0);
+}
+
 // Four packs (8 elements) stored contiguously.
 __device__ __forceinline__ void st_quad(__bf16 *d, unsigned a, unsigned b, unsigned c, unsigned e)
 {
@@ -245,7 +280,7 @@ __device__ __forceinline__ float row_bcast(float x)
 // 2 ct + j / 2 of row g holding Gam[16 ct + 4 g + j], j = 0..3, as gp.x (j even)
 // and gp.y (j odd).
 template <int N, int CT = 0>
-__device__ __forceinline__ void decay_rows(f32x4 *S, float2 gp)
+__device__ __forceinline__ void decay_rows(f32x4 *S, f32x2 gp)
 {
     if constexpr (CT < N) {
         S[CT][0] *= row_bcast<2 * CT>(gp.x);
@@ -254,6 +289,20 @@ __device__ __forceinline__ void decay_rows(f32x4 *S, float2 gp)
         S[CT][3] *= row_bcast<2 * CT + 1>(gp.y);
         decay_rows<N, CT + 1>(S, gp);
     }
+}
+
+// This lane's part of one head's dk x dv fp32 state from the accumulator
+// strip: Sacc[ct][j] is S[16 ct + 4 g4 + j][col]; lane_off is the byte offset
+// of S[4 g4][col].  One buffer over the head's state, uniform row offsets.
+template <int NCT>
+__device__ __forceinline__ void store_state(float *dst, const f32x4 (&Sacc)[NCT], int lane_off, int DV)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst, 0, NCT * 16 * DV * 4, 0x00020000);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sacc[ct][j]), r, lane_off, (16 * ct + j) * DV * 4, 0);
 }
 
 // Bytes spanned by `rows` rows of `width` bytes, `stride` bytes apart (0 rows: 0).
@@ -322,7 +371,7 @@ __device__ __forceinline__ void load_chunk(RawC<E> &R, const E *q, const E *k, c
 }
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
+__global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
     float *S_T, float *snaps, int snap_chunks, int n_snaps, int T, int H, int DV, int nbh, int nsl)
@@ -354,7 +403,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
     const long tokb = (long)b * T;
     const int nchunks = (T + kC - 1) / kC;
 
-    for (int i = tid; i < L::nFlags; i += kWsThreads)
+    for (int i = tid; i < L::nFlags; i += 64 * (4 + L::NP))
         flags[i] = 0;
     __syncthreads();
 
@@ -374,20 +423,29 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
         // make every chunk wait for all of its outstanding memory operations
         // (the o stores included) before the state can be touched
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
+
+        // o: this wave's 16 x 16 tile of chunk c; lane (l16 = column, g4) writes
+        // rows 4 g4 .. 4 g4 + 3.  The tile base advances by a fixed step per
+        // chunk; only the last chunk can be ragged (rows past T fall outside the
+        // buffer and are dropped).
         const int rso = H * DV * L::ES;                   // bytes between token rows of o
-        const int ovo = (4 * g4) * rso + l16 * L::ES;     // this lane's first o element in a chunk
-        // buffer over this wave's 16 x 16 tile of o in chunk c; rows past T fall
-        // outside it and are dropped
-        auto tile = [&](const E *base, int c) {
-            const int t0 = c * kC;
-            const int valid = T - t0 < kC ? T - t0 : kC;
-            return buffer(base + ((tokb + t0) * H + h) * (long)DV + slice * kVS + 16 * w,
-                          rows_bytes(valid, rso, 16 * L::ES));
-        };
+        const int ovo = (4 * g4) * rso + l16 * L::ES;
+        E *otile = o + (tokb * H + h) * (long)DV + slice * kVS + 16 * w;
+        const long ostep = (long)kC * H * DV;
+        const int ofull = rows_bytes(kC, rso, 16 * L::ES);
+        const int olast = rows_bytes(T - (nchunks - 1) * kC, rso, 16 * L::ES);
+
+        // this lane's byte offsets inside a slot: image16 pieces (Kt, Qt),
+        // image4 pieces (Ke^T, V^T, T, M) and the Gam pair (see decay_rows)
+        const int laA = (g4 * L::GS + 8 * l16) * L::ES;
+        const int laB = 4 * lane * L::ES;
+        const int laC = L::slotE * L::ES + (16 * (l16 >> 1) + 4 * g4 + 2 * (l16 & 1)) * 4;
 
         // Chunk c's operands, read from its slot into registers one chunk ahead:
         // the state chain of chunk c then runs with no LDS wait in it, while the
-        // reads for chunk c + 1 overlap chunk c's state update.
+        // reads for chunk c + 1 overlap chunk c's state update.  The reads are
+        // volatile so that none is fused with a neighbour into a wider read whose
+        // halves would then have to be copied into the operand tuples.
         // The A operands of the 16-deep products (T, M, Ke^T) sit in the low half
         // of 8-element tuples whose high half stays zero for the whole loop (the
         // zero is opaque to the compiler, so it is never rematerialised).
@@ -395,54 +453,44 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             V8 kt[NKS], qt[NKS];
             V8 tr, mr, kr[NCT];
             V4 vv;
-            float2 gp;        // Gam pair, see decay_rows
+            f32x2 gp;         // Gam pair, see decay_rows
         };
         auto low = [](V4 x, V8 keep) { return __builtin_shufflevector(cat8(x, x), keep, 0, 1, 2, 3, 12, 13, 14, 15); };
-        // element offsets of this lane's 8-byte reads of Ke^T tiles, T and M in a
-        // slot, each held in its own register (opaque to the compiler), so no two
-        // reads are fused into one double read whose halves would then have to
-        // be copied into the operand tuples
-        int o4[NCT + 2];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            o4[ct] = L::eKe + L::tile(ct) + 4 * lane;
-        o4[NCT] = L::eT + 4 * lane;
-        o4[NCT + 1] = L::eM + 4 * lane;
-#pragma unroll
-        for (int i = 0; i < NCT + 2; ++i)
-            asm volatile("" : "+v"(o4[i]));
-        auto fetch = [&](Ops &op, int c) {
-            const int s = c % NS;
+        auto rd8 = [&](int s, int off) { return lds_load<V8>(smem + L::oSlots + s * L::slotBytes + off); };
+        auto rd4 = [&](int s, int off) { return lds_load<V4>(smem + L::oSlots + s * L::slotBytes + off); };
+        auto fetch = [&](Ops &op, int s, int c) {
             wait_flags(ready + s, 1, 1, c + 1, abort_flag);
-            const E *sl = reinterpret_cast<const E *>(smem + L::oSlots + s * L::slotBytes);
-            const float *gam = reinterpret_cast<const float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
-            const E *kt = sl + L::eKt + g4 * L::GS + 8 * l16;
-            const E *qt = sl + L::eQt + g4 * L::GS + 8 * l16;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-                op.kt[m] = *reinterpret_cast<const V8 *>(kt + m * L::MS);
-                op.qt[m] = *reinterpret_cast<const V8 *>(qt + m * L::MS);
+                op.kt[m] = rd8(s, laA + (L::eKt + m * L::MS) * L::ES);
+                op.qt[m] = rd8(s, laA + (L::eQt + m * L::MS) * L::ES);
             }
-            op.vv = *reinterpret_cast<const V4 *>(sl + L::eV + L::tile(w) + 4 * lane);
-            op.tr = low(*reinterpret_cast<const V4 *>(sl + o4[NCT]), op.tr);
-            op.mr = low(*reinterpret_cast<const V4 *>(sl + o4[NCT + 1]), op.mr);
+            op.vv = rd4(s, laB + (L::eV + L::tile(w)) * L::ES);
+            op.tr = low(rd4(s, laB + L::eT * L::ES), op.tr);
+            op.mr = low(rd4(s, laB + L::eM * L::ES), op.mr);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                op.kr[ct] = low(*reinterpret_cast<const V4 *>(sl + o4[ct]), op.kr[ct]);
-            op.gp = *reinterpret_cast<const float2 *>(gam + 16 * (l16 >> 1) + 4 * g4 + 2 * (l16 & 1));
+                op.kr[ct] = low(rd4(s, laB + (L::eKe + L::tile(ct)) * L::ES), op.kr[ct]);
+            op.gp = lds_load<f32x2>(smem + L::oSlots + s * L::slotBytes + laC);
         };
 
         Ops op;
+        V8 bxv, buv;            // B operands of the 16-deep products, high half zero
         {
             V8 z = {};
             asm volatile("" : "+v"(z));
-            op.tr = op.mr = z;
+            op.tr = op.mr = bxv = buv = z;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 op.kr[ct] = z;
         }
+        const int lane_soff = ((4 * g4) * DV + col) * 4;   // byte offset of S[4 g4][col] in a state
+        int snap_left = snap_chunks, snap_idx = 0;
+        float *snap_dst = snaps ? snaps + (long)bh * DK * DV : nullptr;
+        const long snap_step = (long)nbh * DK * DV;
+        int s = 0;                                        // slot of chunk c
         if (nchunks > 0)
-            fetch(op, 0);
+            fetch(op, 0, 0);
         for (int c = 0; c < nchunks; ++c) {
             // S strip as B operands; contraction slice m holds channels
             // {32m + 4 g4 + e, 32m + 16 + 4 g4 + e}, e = 0..3
@@ -450,62 +498,51 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
             for (int m = 0; m < NKS; ++m)
                 Bs[m] = cat8(cvt4<E>(Sacc[2 * m]), cvt4<E>(Sacc[2 * m + 1]));
-            // X = Kt S as two independent accumulation chains, Y = Qt S
-            f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0, Y = X0;
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) {
-                if (m & 1)
-                    X1 = mma32(op.kt[m], Bs[m], X1);
-                else
-                    X0 = mma32(op.kt[m], Bs[m], X0);
-                Y = mma32(op.qt[m], Bs[m], Y);
-            }
-            // X <- V - Kt S   (rows 4 g4 + j = tokens, column l16)
-            f32x4 X;
+            // X = V - Kt S: the slot holds -Kt, so the accumulator starts at V
+            // (rows 4 g4 + j = tokens, column l16); Y = Qt S
+            f32x4 X, Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                X[j] = to_f(op.vv[j]) - (X0[j] + X1[j]);
+                X[j] = to_f(op.vv[j]);
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) {
+                X = mma32(op.kt[m], Bs[m], X);
+                Y = mma32(op.qt[m], Bs[m], Y);
+            }
             // U = T X, then O = Y + M U   (contraction over tokens 4 g4 + e; the
-            // B operands repeat their 4 elements in the high half, which the
-            // zero high half of the A operands cancels)
-            const V4 bx = cvt4<E>(X);
-            const f32x4 U = mma32(op.tr, cat8(bx, bx), f32x4{0.f, 0.f, 0.f, 0.f});
-            const V4 bu = cvt4<E>(U);
-            const V8 bu8 = cat8(bu, bu);
-            const f32x4 Z = mma32(op.mr, bu8, f32x4{0.f, 0.f, 0.f, 0.f});
+            // zero high halves of A and B cancel)
+            bxv = low(cvt4<E>(X), bxv);
+            const f32x4 U = mma32(op.tr, bxv, f32x4{0.f, 0.f, 0.f, 0.f});
+            buv = low(cvt4<E>(U), buv);
+            const f32x4 O = mma32(op.mr, buv, Y);
             // S <- Gam S + Ke^T U
             decay_rows<NCT>(Sacc, op.gp);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                Sacc[ct] = mma32(op.kr[ct], bu8, Sacc[ct]);
+                Sacc[ct] = mma32(op.kr[ct], buv, Sacc[ct]);
             // the state after chunk c, when c + 1 closes a snapshot block
-            if (snaps && (c + 1) % snap_chunks == 0 && (c + 1) / snap_chunks <= n_snaps) {
-                float *dst = snaps + ((long)((c + 1) / snap_chunks - 1) * nbh + bh) * DK * DV;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        dst[(long)(16 * ct + 4 * g4 + j) * DV + col] = Sacc[ct][j];
+            if (snaps) {
+                if (--snap_left == 0) {
+                    snap_left = snap_chunks;
+                    if (snap_idx < n_snaps)
+                        store_state(snap_dst, Sacc, lane_soff, DV);
+                    ++snap_idx;
+                    snap_dst += snap_step;
+                }
             }
-            // every read of slot c is in registers (and consumed): hand it back,
+            // every read of slot s is in registers (and consumed): hand it back,
             // then fetch the next chunk while the state update runs
             lds_fence();
-            if (lane == 0)
-                st_flag(done + (c % NS) * 4 + w, c + 1);
+            st_flag(done + s * 4 + w, c + 1);
+            s = s + 1 == NS ? 0 : s + 1;
             if (c + 1 < nchunks)
-                fetch(op, c + 1);
-            const __amdgpu_buffer_rsrc_t ro = tile(o, c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                store_scalar(ro, ovo, j * rso, Y[j] + Z[j], (E *)nullptr);
+                fetch(op, s, c + 1);
+            const __amdgpu_buffer_rsrc_t ro = buffer(otile, c + 1 < nchunks ? ofull : olast);
+            store_o(ro, ovo, rso, O, (E *)nullptr);
+            otile += ostep;
         }
-        if (S_T) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S_T[((long)bh * DK + 16 * ct + 4 * g4 + j) * DV + col] = Sacc[ct][j];
-        }
+        if (S_T)
+            store_state(S_T + (long)bh * DK * DV, Sacc, lane_soff, DV);
         return;
     }
 
@@ -520,7 +557,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
     };
 
     // One chunk from raw registers to a published slot.
-    auto produce = [&](const RawC<E> &raw, int c) {
+    auto produce = [&](RawC<E> &raw, int c) {
         typedef typename PE::T PT;
         const int s = c % NS;
         if (c >= NS)
@@ -600,7 +637,7 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     p[u] *= al[u][i];
-                    kt[u] = kk[u] * p[u];
+                    kt[u] = -(kk[u] * p[u]);   // stored negated (see the consumer)
                     qt[u] = qq[u] * p[u];
                     es[u][i & 3] = kk[u] * Z[u][i];
                     kc[u] = es[u][i & 3] * ig[u];
@@ -617,6 +654,8 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
                 }
             }
         }
+        const unsigned braw = raw.b;
+        load(raw, c + L::NP);
         lds_fence();
 
         // ---- A and M on MFMA (contraction over the DK channels) ----------------
@@ -662,18 +701,18 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             };
             // beta of token l16 (row l16 of A^T's columns) and of tokens 4g + j
             // (this lane's rows), the latter fetched from lanes 4g + j
-            const float bl = bits_to_f(raw.b, (E *)nullptr);
+            const float bl = bits_to_f(braw, (E *)nullptr);
             f32x4 br;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                br[j] = bits_to_f((unsigned)__builtin_amdgcn_ds_bpermute(4 * (4 * rg4 + j), (int)raw.b), (E *)nullptr);
+                br[j] = bits_to_f((unsigned)__builtin_amdgcn_ds_bpermute(4 * (4 * rg4 + j), (int)braw), (E *)nullptr);
             f32x4 I4, A, AT;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = 4 * rg4 + j;
                 I4[j] = row == r16 ? 1.f : 0.f;
-                A[j] = row > r16 ? br[j] * Ar[j] : 0.f;      // A[row][l16]
-                AT[j] = row < r16 ? bl * ATr[j] : 0.f;       // A^T[row][l16] = A[l16][row]
+                A[j] = row > r16 ? -br[j] * Ar[j] : 0.f;     // A[row][l16] (Ar holds -<Kt, Kc>)
+                AT[j] = row < r16 ? -bl * ATr[j] : 0.f;      // A^T[row][l16] = A[l16][row]
             }
             const f32x4 A2 = mul(AT, A), A2T = mul(A, AT);
             const f32x4 A4 = mul(A2T, A2), A4T = mul(A2, A2T);
@@ -689,18 +728,12 @@ __global__ __launch_bounds__(kWsThreads) void prefill_ws_kernel(
             st_flag(ready + s, c + 1);
     };
 
-    // two chunks in flight per producer, alternating register sets: the loads
-    // for chunk c + 4 are issued before chunk c is processed
-    RawC<E> ra, rb;
-    load(ra, pw);
-    for (int c = pw; c < nchunks; c += 8) {
-        load(rb, c + 4);
-        produce(ra, c);
-        if (c + 4 >= nchunks)
-            break;
-        load(ra, c + 8);
-        produce(rb, c + 4);
-    }
+    // one chunk in flight per producer: the loads for chunk c + NP are issued
+    // as soon as chunk c's raw registers have been consumed
+    RawC<E> raw;
+    load(raw, pw);
+    for (int c = pw; c < nchunks; c += L::NP)
+        produce(raw, c);
 }
 
 template <typename E, int DK>
@@ -721,7 +754,7 @@ hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g,
     }
     const int nbh = B * H, nsl = dv / kVS;
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
-    hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(kWsThreads), lds, stream,
+    hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(64 * (4 + L::NP)), lds, stream,
                        (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
                        (E *)o, S_T, snap.count > 0 ? snap.out : nullptr, snap.every_chunks, snap.count,
                        T, H, dv, nbh, nsl);
