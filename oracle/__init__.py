@@ -25,6 +25,9 @@ decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
             eps=1e-6, nthreads=None) -> o
     conv_cache and S are updated in place (they must be float64 C-contiguous
     arrays owned by the caller).
+output_gate(o, gate, w=None, eps=1e-6) -> y
+    o, gate [..., H, dv]; w [dv] or None (ones).  y = Sigmoid(gate) * RMSNorm(o) * w,
+    the RMSNorm taken over the dv channels of each (row, head).
 """
 import ctypes
 import os
@@ -37,6 +40,7 @@ _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
 L2NORM_EPS = 1e-6
+RMSNORM_EPS = 1e-6
 
 
 def _load():
@@ -53,6 +57,8 @@ def _load():
         lib.kda_oracle_prefill_prep.restype = ctypes.c_int
         lib.kda_oracle_prefill_prep.argtypes = (
             [_dp] * 14 + [ctypes.c_long] * 6 + [ctypes.c_double, ctypes.c_int])
+        lib.kda_oracle_output_gate.restype = ctypes.c_int
+        lib.kda_oracle_output_gate.argtypes = [_dp] * 4 + [ctypes.c_long] * 3 + [ctypes.c_double]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = (
             [_dp] * 5 + [ctypes.c_long] + [_dp] * 4 + [ctypes.c_long] * 5 + [ctypes.c_double, ctypes.c_int])
@@ -159,3 +165,19 @@ def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_decode_step failed ({rc})")
     return o
+
+
+def output_gate(o, gate, w=None, eps=RMSNORM_EPS):
+    o, gate = _f64(o), _f64(gate)
+    if o.shape != gate.shape or o.ndim < 2:
+        raise ValueError("oracle.output_gate: o and gate must share a shape [..., H, dv]")
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = int(np.prod(o.shape[:-2], dtype=np.int64))
+    wa = None if w is None else _f64(w)
+    if wa is not None and wa.shape != (dv,):
+        raise ValueError("oracle.output_gate: w shape")
+    y = np.empty(o.shape)
+    rc = _load().kda_oracle_output_gate(_ptr(o), _ptr(gate), _ptr(wa), _ptr(y), rows, H, dv, float(eps))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_output_gate failed ({rc})")
+    return y

@@ -496,3 +496,31 @@ int kda_oracle_prefill_prep(const double *q_pre, const double *k_pre, const doub
     free(th);
     return rc;
 }
+
+/*
+ * Output exposure gate (note, section 3.2, output equation
+ * y_t = W_o[Sigmoid(W_g x_t) (.) RMSNorm(o~_t)], without the W_o projection,
+ * which needs trained weights).  The note says RMSNorm steadies each head's
+ * readout, so it normalises the dv channels of one (token, head):
+ *     y[r,h,c] = Sigmoid(gate[r,h,c]) * o[r,h,c] / sqrt(mean_c' o[r,h,c']^2 + eps) * w[c]
+ * Readings where the pages are silent: RMSNorm carries a per-channel weight w
+ * (NULL = all ones) shared by the heads, and eps is the caller's.
+ *   o, gate, y : [rows, H, dv]     w : [dv] or NULL
+ * Returns 0, or -1 on a bad argument.
+ */
+int kda_oracle_output_gate(const double *o, const double *gate, const double *w, double *y,
+                           long rows, long H, long dv, double eps)
+{
+    if (!o || !gate || !y || rows < 0 || H < 0 || dv <= 0 || !(eps >= 0.0))
+        return -1;
+    for (long u = 0; u < rows * H; ++u) {
+        const double *ou = o + u * dv, *gu = gate + u * dv;
+        double ss = 0.0;
+        for (long c = 0; c < dv; ++c)
+            ss += ou[c] * ou[c];
+        const double inv_rms = 1.0 / sqrt(ss / (double)dv + eps);
+        for (long c = 0; c < dv; ++c)
+            y[u * dv + c] = sigmoid(gu[c]) * ou[c] * inv_rms * (w ? w[c] : 1.0);
+    }
+    return 0;
+}

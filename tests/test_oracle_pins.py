@@ -458,3 +458,64 @@ def test_prep_empty_and_rejects():
         oracle.prefill_prep(qp, kp, vp, w, init, z, A[:1], bl)
     with pytest.raises(ValueError):
         oracle.prefill_prep(qp, kp, vp, w, init[:, :, :2], z, A, bl)
+
+
+# ---------------------------------------------------------------------------
+# Output exposure gate: y = Sigmoid(gate) * RMSNorm(o) * w (note, section 3.2,
+# output equation, before W_o), RMSNorm over the dv channels of one head.
+
+def test_output_gate_worked_values():
+    with open(os.path.join(GOLDEN, "output_gate_worked.json")) as fh:
+        ref = json.load(fh)
+    for case in ref["cases"]:
+        o = np.array(case["o"])[None, None]
+        gate = np.log(np.array(case["gate_ln_arg"]))[None, None]   # Sigmoid(ln a) = a / (1 + a)
+        w = None if case["w"] is None else np.array(case["w"])
+        y = oracle.output_gate(o, gate, w, eps=case["eps"])
+        want = np.array(case["y_sqrt2_factor"]) * math.sqrt(2.0)
+        np.testing.assert_allclose(y[0, 0], want, rtol=1e-14, atol=1e-15)
+
+
+def test_output_gate_matches_library_routines():
+    rng = np.random.default_rng(41)
+    o = rng.standard_normal((5, 3, 3, 64)) * 2.5
+    gate = rng.standard_normal(o.shape) * 3
+    w = rng.standard_normal(64)
+    eps = 1e-3
+    y = oracle.output_gate(o, gate, w, eps=eps)
+    to = torch.from_numpy(o)
+    ref = torch.sigmoid(torch.from_numpy(gate)) * torch.nn.functional.rms_norm(
+        to, (64,), weight=torch.from_numpy(w), eps=eps)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_output_gate_invariants():
+    rng = np.random.default_rng(42)
+    o = rng.standard_normal((7, 4, 128))
+    gate = rng.standard_normal(o.shape)
+    # an open gate and unit weight leave exactly unit root-mean-square (eps = 0)
+    y = oracle.output_gate(o, np.full(o.shape, 800.0), None, eps=0.0)
+    np.testing.assert_allclose(np.mean(y ** 2, axis=-1), 1.0, rtol=1e-13)
+    # scale invariance of RMSNorm (eps = 0) and oddness in o
+    base = oracle.output_gate(o, gate, None, eps=0.0)
+    np.testing.assert_allclose(oracle.output_gate(37.5 * o, gate, None, eps=0.0), base, rtol=1e-12)
+    np.testing.assert_allclose(oracle.output_gate(-o, gate, None, eps=0.0), -base, rtol=0, atol=0)
+    # a closed-at-half gate (0) halves the normalised readout, channel by channel
+    half = oracle.output_gate(o, np.zeros(o.shape), None, eps=0.0)
+    np.testing.assert_allclose(half * 2, oracle.output_gate(o, np.full(o.shape, 800.0), None, eps=0.0),
+                               rtol=1e-13)
+    # heads are normalised separately: scaling one head leaves the others alone
+    o2 = o.copy()
+    o2[:, 1] *= 1e3
+    y2 = oracle.output_gate(o2, gate, None, eps=1e-6)
+    y1 = oracle.output_gate(o, gate, None, eps=1e-6)
+    np.testing.assert_array_equal(y2[:, 0], y1[:, 0])
+    np.testing.assert_array_equal(y2[:, 2:], y1[:, 2:])
+
+
+def test_output_gate_rejects():
+    o = np.zeros((2, 3, 4))
+    with pytest.raises(ValueError):
+        oracle.output_gate(o, np.zeros((2, 3, 5)))
+    with pytest.raises(ValueError):
+        oracle.output_gate(o, o, np.ones(3))
