@@ -12,7 +12,10 @@ torch.cuda.synchronize():
 A third phase (reported under "snapshots") times kda_chunk_fwd_snapshots on the
 prefill workload with a state snapshot every 512 tokens (128 snapshots), and a
 fourth (reported under "prep") kda_prefill_prep on the same B=1, H=96, T=65536
-shape: projected pre-activations to q, k, v, g, beta.
+shape: projected pre-activations to q, k, v, g, beta.  A fifth (reported under
+"gate") times kda_output_gate on the prefill output shape (65536 tokens x 96
+heads x 128, bf16), and a sixth (under "decode_gated") kda_decode_step_gated on
+the decode batch.
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
@@ -61,6 +64,12 @@ def prep_bytes(B, T, H, dk, dv, W=4):
     nch = 2 * dk + dv
     per_token_head = 2 * (2 * nch + 2 * dk + 2)
     return B * T * H * per_token_head + H * 4 * nch * W + B * H * 4 * (W - 1) * nch
+
+
+def gate_bytes(rows, H, dv):
+    """Algorithmic HBM bytes of one kda_output_gate call (bf16): read o and gate, write y,
+    2 bytes each per element; the fp32 weight (4 dv bytes) once."""
+    return rows * H * dv * 2 * 3 + 4 * dv
 
 
 def measured_traffic(profile, sources):
@@ -144,6 +153,7 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-snapshots", action="store_true")
     ap.add_argument("--skip-prep", action="store_true")
+    ap.add_argument("--skip-gate", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -156,7 +166,8 @@ def main():
     import torch
 
     from gated_delta_rule_18_amd import binding
-    from gated_delta_rule_18_amd.inputs import (DECODE, PREP_K3, WORKLOADS, decode_state, decode_step_inputs,
+    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, WORKLOADS, decode_gate_inputs,
+                                                decode_state, decode_step_inputs, gate_inputs,
                                                 prefill_inputs, prep_inputs)
 
     dev = torch.device("cuda:0")
@@ -247,6 +258,28 @@ def main():
                                                      ["kda_decode.hip", "kda_device.h"]),
                          "bytes_per_launch": d_bytes},
         }
+        # the same step with the output exposure gate fused (y written in place of o)
+        if not args.skip_gate:
+            gates = [decode_gate_inputs(ds, s % ds.steps, device=dev) for s in range(len(steps_in))]
+            nw = torch.ones(ds.dv, dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+
+            def decode_gated_step(i=0):
+                d = steps_in[pos[0] % len(steps_in)]
+                binding.decode_step_gated(d["q_pre"], d["k_pre"], d["v_pre"], st["conv_w"], st["conv_cache"],
+                                          pos[0], d["g"], d["beta"], st["S"], gates[pos[0] % len(gates)], nw,
+                                          y=od)
+                pos[0] += 1
+
+            g_wall, g_kern = _timed(decode_gated_step, args.steps, args.warmup, torch)
+            g_bytes = d_bytes + ds.N * ds.H * ds.dv * 2 + ds.dv * 4
+            decode["gated"] = {
+                "ms_per_step": g_wall, "kernel_ms": g_kern, "extra_ms_vs_decode": g_kern - d_kern,
+                "roofline": {"bound": "hbm", "achieved": g_bytes / (g_kern * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": g_bytes / (g_kern * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "traffic": None, "bytes_per_launch": g_bytes},
+            }
+            del gates
         del st, steps_in
 
     # ---------------- prefill preprocessing --------------------------------------
@@ -279,6 +312,32 @@ def main():
         }
         del xp, outs, fin
 
+    # ---------------- output exposure gate --------------------------------------
+    gate = None
+    if not args.skip_gate:
+        gk = GATE_K3
+        xg = gate_inputs(gk["rows"], gk["H"], gk["dv"], dtype=gk["dtype"], seed=gk["seed"], device=dev)
+        yg = torch.empty_like(xg["o"])
+        torch.cuda.synchronize()
+
+        def gate_step(i=0):
+            binding.output_gate(xg["o"], xg["gate"], xg["norm_w"], y=yg)
+
+        q_wall, q_kern = _timed(gate_step, args.steps, args.warmup, torch)
+        q_bytes = gate_bytes(gk["rows"], gk["H"], gk["dv"])
+        q_gbps = q_bytes / (q_kern * 1e-3) / 1e9
+        gate = {
+            "workload": f"output exposure gate rows={gk['rows']} H{gk['H']} dv={gk['dv']} {gk['dtype']}",
+            "ms_per_step": q_wall,
+            "kernel_ms": q_kern,
+            "tokens_per_s": gk["rows"] / (q_wall * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": q_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": q_gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("gate_k3_hbm_counters.txt", ["kda_gate.hip", "kda_device.h"]),
+                         "bytes_per_launch": q_bytes},
+        }
+        del xg, yg
+
     line = {
         "metric": "KDA prefill tokens/s & TFLOP/s (% MFMA peak); decode-step HBM GB/s (% peak)",
         "value": B * T / (p_wall * 1e-3),
@@ -307,6 +366,7 @@ def main():
         "decode": decode,
         "snapshots": snapshots,
         "prep": prep,
+        "gate": gate,
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -9,6 +9,9 @@ the calls raise (there is no fallback).
     o             = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
     q, k, v, g, beta, conv_final = prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A,
                                                 beta_logit)
+    y             = output_gate(o, gate, norm_w=None, eps=1e-6)
+    y             = decode_step_gated(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta,
+                                      S, gate, norm_w=None, eps=1e-6)
 
 Shapes and dtypes follow include/kda.h: bf16 activations with an fp32 state,
 or fp32 everywhere (test mode).
@@ -23,8 +26,8 @@ library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_prefill_prep",
-           "kda_strerror", "kda_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_gated",
+           "kda_output_gate", "kda_prefill_prep", "kda_strerror", "kda_version")
 
 _lib = None
 
@@ -50,6 +53,11 @@ def lib():
         L.kda_chunk_fwd_snapshots.argtypes = [vp] * 9 + [i] * 9 + [vp]
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
+        L.kda_decode_step_gated.restype = i
+        L.kda_decode_step_gated.argtypes = ([vp] * 5 + [i] + [vp] * 5 + [ctypes.c_float, vp]
+                                            + [i] * 6 + [vp])
+        L.kda_output_gate.restype = i
+        L.kda_output_gate.argtypes = [vp] * 4 + [i] * 3 + [ctypes.c_float, i, vp]
         L.kda_prefill_prep.restype = i
         L.kda_prefill_prep.argtypes = [vp] * 14 + [i] * 7 + [vp]
         L.kda_strerror.restype = ctypes.c_char_p
@@ -150,6 +158,17 @@ def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o
     """One decode step.  q_pre, k_pre [N,H,dk]; v_pre [N,H,dv]; conv_w fp32 [H,2dk+dv,W];
     conv_cache [N,H,W-1,2dk+dv] (updated); g [N,H,dk]; beta [N,H]; S fp32 [N,H,dk,dv]
     (updated in place).  Returns o [N,H,dv]."""
+    return _decode(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o, None, None, 0.0)
+
+
+def decode_step_gated(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, gate,
+                      norm_w=None, eps=1e-6, y=None):
+    """decode_step with the output exposure gate fused: returns y [N,H,dv] =
+    Sigmoid(gate) * RMSNorm(o) * norm_w (norm_w fp32 [dv] or None for ones)."""
+    return _decode(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, y, gate, norm_w, eps)
+
+
+def _decode(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o, gate, norm_w, eps):
     N, H, dk = q_pre.shape
     dv = v_pre.shape[-1]
     W = conv_w.shape[-1]
@@ -166,11 +185,46 @@ def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _want(o, "o", (N, H, dv), dt, dev)
-    rc = lib().kda_decode_step(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(conv_cache),
-                               int(conv_pos), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
-                               W, code, _stream(dev))
+    if gate is None:
+        rc = lib().kda_decode_step(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(conv_cache),
+                                   int(conv_pos), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
+                                   W, code, _stream(dev))
+    else:
+        _want(gate, "gate", (N, H, dv), dt, dev)
+        if norm_w is not None:
+            _want(norm_w, "norm_w", (dv,), torch.float32, dev)
+        rc = lib().kda_decode_step_gated(_ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w),
+                                         _ptr(conv_cache), int(conv_pos), _ptr(g), _ptr(beta), _ptr(S),
+                                         _ptr(gate), _ptr(norm_w), float(eps), _ptr(o), N, H, dk, dv, W,
+                                         code, _stream(dev))
     _check(rc)
     return o
+
+
+def output_gate(o, gate, norm_w=None, eps=1e-6, y=None):
+    """Output exposure gate: y = Sigmoid(gate) * RMSNorm(o) * norm_w, RMSNorm over the
+    last (dv) axis of each head.  o, gate [..., H, dv] (bf16 or fp32); norm_w fp32 [dv]
+    or None (ones).  y may be passed as o or gate itself (in place)."""
+    if o.dim() < 2:
+        raise ValueError("o must be [..., H, dv]")
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = 1
+    for n in o.shape[:-2]:
+        rows *= n
+    dev, dt = o.device, o.dtype
+    code = _dtype_code(o)
+    _want(o, "o", o.shape, dt, dev)
+    _want(gate, "gate", o.shape, dt, dev)
+    if norm_w is not None:
+        _want(norm_w, "norm_w", (dv,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    else:
+        _want(y, "y", o.shape, dt, dev)
+    rc = lib().kda_output_gate(_ptr(o), _ptr(gate), _ptr(norm_w), _ptr(y), rows, H, dv, float(eps), code,
+                               _stream(dev))
+    _check(rc)
+    return y
 
 
 def prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, out=None,

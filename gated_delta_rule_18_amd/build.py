@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kda_prefill.hip", "kda_prefill_ws.hip", "kda_decode.hip", "kda_prep.hip", "kda_api.cpp"]
+SOURCES = ["kda_prefill.hip", "kda_prefill_ws.hip", "kda_decode.hip", "kda_prep.hip", "kda_gate.hip",
+           "kda_api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", CSRC, "-I", INCLUDE,
           "-Wall", "-Wno-unused-command-line-argument",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

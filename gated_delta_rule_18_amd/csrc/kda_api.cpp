@@ -59,6 +59,35 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                void *conv_cache, int conv_pos, const void *g, const void *beta, float *S, void *o,
+                int N, int H, int dk, int dv, int width, int dtype, const kda::OutputGate &og,
+                void *stream)
+{
+    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || conv_pos < 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (width != 4)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk) || !head_ok(dv))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)N * H == 0)
+        return KDA_OK;
+    if (!q_pre || !k_pre || !v_pre || !conv_w || !conv_cache || !g || !beta || !S || !o)
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q_pre, k_pre, v_pre, conv_w, conv_cache, g, S, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p))
+            return KDA_ERR_INVALID;
+    if ((long long)N * H > 0x7fffffffLL)
+        return KDA_ERR_INVALID;
+    hipError_t e = kda::launch_decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache,
+                                           conv_pos % (width - 1), g, beta, S, o, N, H, dk, dv,
+                                           dtype == KDA_FP32, og, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 } // namespace
 
 extern "C" {
@@ -111,27 +140,55 @@ int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, con
                     void *conv_cache, int conv_pos, const void *g, const void *beta, float *S,
                     void *o, int N, int H, int dk, int dv, int width, int dtype, void *stream)
 {
-    if (N < 0 || H < 0 || dk <= 0 || dv <= 0 || conv_pos < 0)
+    return decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o, N, H, dk,
+                       dv, width, dtype, kda::OutputGate{}, stream);
+}
+
+int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pre,
+                          const float *conv_w, void *conv_cache, int conv_pos, const void *g,
+                          const void *beta, float *S, const void *gate, const float *norm_w,
+                          float eps, void *y, int N, int H, int dk, int dv, int width, int dtype,
+                          void *stream)
+{
+    if (!(eps > 0.f) || !(eps < 1e30f))
+        return KDA_ERR_INVALID;
+    if ((long long)N * H > 0 && (!gate || !aligned16(gate) || (norm_w && !aligned16(norm_w))))
+        return KDA_ERR_INVALID;
+    kda::OutputGate og;
+    og.gate = gate;
+    og.w = norm_w;
+    og.eps = eps;
+    return decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, y, N, H, dk,
+                       dv, width, dtype, og, stream);
+}
+
+int kda_output_gate(const void *o, const void *gate, const float *norm_w, void *y, int rows, int H,
+                    int dv, float eps, int dtype, void *stream)
+{
+    if (rows < 0 || H < 0 || dv <= 0 || !(eps > 0.f) || !(eps < 1e30f))
         return KDA_ERR_INVALID;
     if (dtype != KDA_BF16 && dtype != KDA_FP32)
         return KDA_ERR_INVALID;
-    if (width != 4)
-        return KDA_ERR_INVALID;
-    if (!head_ok(dk) || !head_ok(dv))
+    if (!head_ok(dv))
         return KDA_ERR_UNSUPPORTED;
-    if ((long long)N * H == 0)
+    const long long units = (long long)rows * H;
+    if (units == 0)
         return KDA_OK;
-    if (!q_pre || !k_pre || !v_pre || !conv_w || !conv_cache || !g || !beta || !S || !o)
+    if (!o || !gate || !y)
         return KDA_ERR_INVALID;
-    const void *ptrs[] = {q_pre, k_pre, v_pre, conv_w, conv_cache, g, S, o};
+    const void *ptrs[] = {o, gate, y, norm_w};
     for (const void *p : ptrs)
-        if (!aligned16(p))
+        if (p && !aligned16(p))
             return KDA_ERR_INVALID;
-    if ((long long)N * H > 0x7fffffffLL)
+    // y may be o or gate itself (each element is read before it is written, by
+    // the same lane); any other overlap is invalid
+    const long long bytes = units * dv * (dtype == KDA_FP32 ? 4 : 2);
+    if ((y != o && overlap(y, bytes, o, bytes)) || (y != gate && overlap(y, bytes, gate, bytes)))
         return KDA_ERR_INVALID;
-    hipError_t e = kda::launch_decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache,
-                                           conv_pos % (width - 1), g, beta, S, o, N, H, dk, dv,
-                                           dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    if (norm_w && overlap(y, bytes, norm_w, (long long)dv * 4))
+        return KDA_ERR_INVALID;
+    hipError_t e = kda::launch_output_gate(o, gate, norm_w, y, (long)units, dv, eps, dtype == KDA_FP32,
+                                           reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -16,6 +16,12 @@
 //   * the readout does not re-read S': with d = v - vhat,
 //       o = S'^T q = Sbar^T q + beta (q . k) d,
 //     so both column sums (Sbar^T k and Sbar^T q) come out of one pass.
+//
+// The gated variant (kda_decode_step_gated) also applies the output exposure
+// gate of the same section's output equation before W_o: the threads that hold
+// o (lanes 0 .. dv/4-1 of wavefront 0, four columns each) reduce its sum of
+// squares and write y = Sigmoid(gate) * o / sqrt(mean o^2 + eps) * w instead
+// of o, so o never makes a round trip through HBM.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -68,12 +74,12 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
 
 __device__ __forceinline__ float swish(float u) { return u / (1.0f + exp_f(-u)); }
 
-template <int DK, int DV, typename E>
+template <int DK, int DV, typename E, bool GATED>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const E *__restrict__ q_pre, const E *__restrict__ k_pre, const E *__restrict__ v_pre,
     const float *__restrict__ conv_w, E *__restrict__ conv_cache, int oldest,
     const E *__restrict__ g, const E *__restrict__ beta, float *__restrict__ S,
-    E *__restrict__ o, int H)
+    E *__restrict__ o, int H, const E *__restrict__ gate, const float *__restrict__ norm_w, float eps)
 {
     constexpr int NCH = 2 * DK + DV;      // conv channels q | k | v
     constexpr int CG = DV / 4;            // float4 column groups
@@ -99,6 +105,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
     for (int j = 0; j < ROWS; ++j)
         s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sp + (size_t)(rg + RG * j) * DV) + cg);
+
+    // the gate pre-activations of this thread's four output columns (gated variant)
+    float gv[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {1.f, 1.f, 1.f, 1.f};
+    if (GATED && rg == 0) {
+        load2(gate + (size_t)nh * DV + 4 * cg, gv[0], gv[1]);
+        load2(gate + (size_t)nh * DV + 4 * cg + 2, gv[2], gv[3]);
+        if (norm_w) {
+            const float4 w4 = *reinterpret_cast<const float4 *>(norm_w + 4 * cg);
+            wv[0] = w4.x, wv[1] = w4.y, wv[2] = w4.z, wv[3] = w4.w;
+        }
+    }
 
     // 2. ShortConv over the window (3 cached tokens, oldest first, then x_t) + Swish
     if (t < NCH / 2) {
@@ -216,36 +233,62 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
             r[c] += bk * d[c];
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(Sp + (size_t)i * DV) + cg);
     }
-    if (rg == 0) {
-        const float bq = bt * qdotk;
-        store4(o + (size_t)nh * DV + 4 * cg, p[0] + bq * d[0], p[1] + bq * d[1], p[2] + bq * d[2],
-               p[3] + bq * d[3]);
+    const float bq = bt * qdotk;
+    float ov[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        ov[c] = p[c] + bq * d[c];
+    if constexpr (GATED) {
+        // lanes 0 .. CG-1 of wavefront 0 hold the head's row of o; xor offsets
+        // below CG keep the reduction inside them
+        if (wave == 0) {
+            float ss = rg == 0 ? ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3] : 0.f;
+#pragma unroll
+            for (int off = CG / 2; off > 0; off >>= 1)
+                ss += __shfl_xor(ss, off, 64);
+            if (rg == 0) {
+                const float r = rsqrtf(ss * (1.0f / DV) + eps);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    ov[c] = __builtin_amdgcn_rcpf(1.0f + exp_f(-gv[c])) * ov[c] * r * wv[c];
+            }
+        }
     }
+    if (rg == 0)
+        store4(o + (size_t)nh * DV + 4 * cg, ov[0], ov[1], ov[2], ov[3]);
 }
 
 template <int DK, int DV, typename E>
 hipError_t launch(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
                   void *conv_cache, int oldest, const void *g, const void *beta, float *S, void *o,
-                  int N, int H, hipStream_t stream)
+                  int N, int H, const OutputGate &og, hipStream_t stream)
 {
     const long blocks = (long)N * H;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w, (E *)conv_cache,
-                       oldest, (const E *)g, (const E *)beta, S, (E *)o, H);
+    if (og.gate)
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
+                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H,
+                           (const E *)og.gate, og.w, og.eps);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, DV, E, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
+                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H,
+                           (const E *)nullptr, (const float *)nullptr, 0.f);
     return hipGetLastError();
 }
 
 template <typename E>
 hipError_t dispatch(int dk, int dv, const void *q_pre, const void *k_pre, const void *v_pre,
                     const float *conv_w, void *conv_cache, int oldest, const void *g,
-                    const void *beta, float *S, void *o, int N, int H, hipStream_t stream)
+                    const void *beta, float *S, void *o, int N, int H, const OutputGate &og,
+                    hipStream_t stream)
 {
 #define KDA_DECODE_CASE(A, B)                                                                    \
     if (dk == A && dv == B)                                                                     \
         return launch<A, B, E>(q_pre, k_pre, v_pre, conv_w, conv_cache, oldest, g, beta, S, o, N, \
-                               H, stream);
+                               H, og, stream);
     KDA_DECODE_CASE(128, 128)
     KDA_DECODE_CASE(128, 64)
     KDA_DECODE_CASE(64, 128)
@@ -259,13 +302,13 @@ hipError_t dispatch(int dk, int dv, const void *q_pre, const void *k_pre, const 
 hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
                               const float *conv_w, void *conv_cache, int oldest_slot,
                               const void *g, const void *beta, float *S, void *o, int N, int H,
-                              int dk, int dv, bool fp32, hipStream_t stream)
+                              int dk, int dv, bool fp32, const OutputGate &og, hipStream_t stream)
 {
     if (fp32)
         return dispatch<float>(dk, dv, q_pre, k_pre, v_pre, conv_w, conv_cache, oldest_slot, g,
-                               beta, S, o, N, H, stream);
+                               beta, S, o, N, H, og, stream);
     return dispatch<__bf16>(dk, dv, q_pre, k_pre, v_pre, conv_w, conv_cache, oldest_slot, g, beta,
-                            S, o, N, H, stream);
+                            S, o, N, H, og, stream);
 }
 
 } // namespace kda

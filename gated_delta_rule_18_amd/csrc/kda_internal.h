@@ -24,10 +24,24 @@ hipError_t launch_chunk16(const void *q, const void *k, const void *v, const voi
                           int B, int T, int H, int dk, int dv, bool fp32, const Snapshots &snap,
                           hipStream_t stream);
 
+// Output exposure gate fused into the decode step: when gate is not null the
+// step writes y = Sigmoid(gate) * o / sqrt(mean o^2 + eps) * w in place of o
+// (w null = ones).
+struct OutputGate {
+    const void *gate = nullptr;
+    const float *w = nullptr;
+    float eps = 0.f;
+};
+
 hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *v_pre,
                               const float *conv_w, void *conv_cache, int oldest_slot,
                               const void *g, const void *beta, float *S, void *o,
-                              int N, int H, int dk, int dv, bool fp32, hipStream_t stream);
+                              int N, int H, int dk, int dv, bool fp32, const OutputGate &og,
+                              hipStream_t stream);
+
+// The output exposure gate alone over `units` (row, head) rows of dv elements.
+hipError_t launch_output_gate(const void *o, const void *gate, const float *w, void *y, long units,
+                              int dv, float eps, bool fp32, hipStream_t stream);
 
 hipError_t launch_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
                                const float *conv_w, const void *conv_init, const void *z,

@@ -14,6 +14,7 @@ Workloads (shapes as named; every value is synthetic):
   stream_1m      16 segments of k3_prefill's shape, state carried          seed 3000+s
   decode         N=256 H=96 d=128, 64 steps, bf16                          seed 4000+step
   k3_prep        B=1  H=96 T=65536  d=128  bf16  prefill preprocessing     seed 5
+  k3_gate        rows=65536 H=96 dv=128 bf16  output exposure gate         seed 6
 Long-memory variants (make the state matter across chunks):
   L1  tiny_fp32 shape, g = -5 sigmoid(N(0,1) - 7), upper half of the key channels g = 0
   L2  prefill_b4h32 shape with the L1 gate distribution
@@ -22,7 +23,9 @@ Long-memory variants (make the state matter across chunks):
 Draw order per call: q, k, v, beta logits, g logits, S0, then the bound mask
 (k3_prefill only).  Decode state: conv weights, conv cache, S.  Decode step:
 q_pre, k_pre, v_pre, beta logits, g logits.  Prefill preprocessing: conv weights,
-A, conv history, then q_pre, k_pre, v_pre, z, beta logits.
+A, conv history, then q_pre, k_pre, v_pre, z, beta logits.  Output gate: o,
+gate pre-activations, RMSNorm weight.  Decode gate pre-activations: one draw per
+step from seed seed_base + 10000 + step.
 """
 from dataclasses import dataclass, field
 
@@ -87,6 +90,7 @@ WORKLOADS = {
                       g_const=-1e-3, beta_zero=True),
 }
 PREP_K3 = PrepSpec(B=1, T=65536, H=96, dk=128, dv=128, seed=5)
+GATE_K3 = dict(rows=65536, H=96, dv=128, dtype="bf16", seed=6)
 STREAM_1M = dict(base=WORKLOADS["k3_prefill"], segments=16, seed_base=3000)
 DECODE = DecodeSpec(N=256, H=96, dk=128, dv=128)
 
@@ -202,6 +206,24 @@ def prep_inputs(spec: PrepSpec, device="cpu", seed=None, T=None):
                         ("z", (B, T, H, dk)), ("beta_logit", (B, T, H)))}
     x.update(conv_w=conv_w.contiguous(), A=A.contiguous(), conv_init=init)
     return x
+
+
+def gate_inputs(rows, H, dv, dtype="bf16", seed=6, device="cpu", weight=True):
+    """Output-gate inputs: o ~ N(0,1) and gate ~ 2 N(0,1), both [rows, H, dv] in dtype;
+    norm_w fp32 [dv] ~ 1 + 0.1 N(0,1) (None when weight is False)."""
+    dt = torch_dtype(dtype)
+    gen = _gen(device, seed)
+    o = _randn((rows, H, dv), gen, device).to(dt).contiguous()
+    gate = (2.0 * _randn((rows, H, dv), gen, device)).to(dt).contiguous()
+    w = (1.0 + 0.1 * _randn((dv,), gen, device)).contiguous() if weight else None
+    return dict(o=o, gate=gate, norm_w=w)
+
+
+def decode_gate_inputs(spec: DecodeSpec, step: int, device="cpu", N=None):
+    """Gate pre-activations of one decode step: [N, H, dv] ~ 2 N(0,1) in spec.dtype."""
+    N = spec.N if N is None else N
+    gen = _gen(device, spec.seed_base + 10000 + step)
+    return (2.0 * _randn((N, spec.H, spec.dv), gen, device)).to(torch_dtype(spec.dtype)).contiguous()
 
 
 def to_f64(t):

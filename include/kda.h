@@ -177,6 +177,53 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
                      int B, int T, int H, int dk, int dv, int width, int dtype,
                      void *stream);
 
+/*
+ * kda_output_gate -- the output exposure gate of a KDA layer, before W_o.
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.2, output equation y_t = W_o[Sigmoid(W_g x_t) (.) RMSNorm(o~_t)]):
+ * the bracket, with RMSNorm over the dv channels of each (row, head) -- the
+ * section says it steadies each head's readout -- and a per-channel weight
+ * shared by the heads:
+ *     y[r,h,c] = Sigmoid(gate[r,h,c]) * o[r,h,c] / sqrt(mean_c' o[r,h,c']^2 + eps) * w[c]
+ * W_g x_t (`gate`) and W_o are the caller's GEMMs.  This is the epilogue for
+ * kda_chunk_fwd's output; kda_decode_step_gated fuses it into decode.
+ *
+ *   o      : [rows, H, dv] (dtype)   readout o~ (e.g. kda_chunk_fwd's o, rows = B*T)
+ *   gate   : [rows, H, dv] (dtype)   gate pre-activation W_g x_t
+ *   norm_w : [dv] fp32               RMSNorm weight; NULL = all ones
+ *   y      : [rows, H, dv] (dtype)   written; may be o itself or gate itself
+ *                                    (in place), any other overlap is invalid
+ *   eps    : > 0 (1e-6 is the reading used by the tests)
+ *   dv     : 64 or 128
+ * Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size or eps, overlap),
+ * KDA_ERR_UNSUPPORTED (dv), KDA_ERR_LAUNCH.
+ */
+int kda_output_gate(const void *o, const void *gate, const float *norm_w, void *y,
+                    int rows, int H, int dv, float eps, int dtype, void *stream);
+
+/*
+ * kda_decode_step_gated -- kda_decode_step with the output exposure gate fused:
+ * the step writes y = Sigmoid(gate) * RMSNorm(o~) * w (as kda_output_gate
+ * defines it, same page, section 3.2, output equation) in place of o~, so the
+ * readout never goes through HBM.  The state and the conv cache are updated
+ * exactly as kda_decode_step updates them.
+ *
+ * Arguments as kda_decode_step, with o replaced by
+ *   gate   : [N, H, dv] (dtype)   gate pre-activation W_g x_t of this step
+ *   norm_w : [dv] fp32            RMSNorm weight; NULL = all ones
+ *   eps    : > 0
+ *   y      : [N, H, dv] (dtype)   written
+ * Errors: as kda_decode_step; KDA_ERR_INVALID also for a null or misaligned
+ * gate, a misaligned norm_w or a bad eps.
+ */
+int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pre,
+                          const float *conv_w, void *conv_cache, int conv_pos,
+                          const void *g, const void *beta, float *S,
+                          const void *gate, const float *norm_w, float eps, void *y,
+                          int N, int H, int dk, int dv, int width, int dtype,
+                          void *stream);
+
 /* Human-readable text for a kda_status code (static storage, never NULL). */
 const char *kda_strerror(int status);
 

@@ -148,3 +148,56 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         binding.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def _gate(**kw):
+    big = 1 << 24
+    args = dict(o=A, gate=A + big, w=A + 2 * big, y=A + 3 * big, rows=8, H=2, dv=64, eps=1e-6, dtype=0,
+                stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_output_gate(vp(args["o"]), vp(args["gate"]), vp(args["w"]), vp(args["y"]),
+                                         args["rows"], args["H"], args["dv"], args["eps"], args["dtype"],
+                                         args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eps=0.0), -1), (dict(eps=-1.0), -1), (dict(eps=float("nan")), -1), (dict(dtype=3), -1),
+    (dict(rows=-1), -1), (dict(dv=96), -2), (dict(o=None), -1), (dict(gate=None), -1), (dict(y=None), -1),
+    (dict(w=MIS), -1), (dict(y=MIS), -1),
+    (dict(y=A + 64), -1),                    # y partly overlapping o
+    (dict(y=A + (1 << 24) + 64), -1),        # y partly overlapping gate
+    (dict(w=A + 3 * (1 << 24) + 32), -1),    # the weight inside y
+])
+def test_output_gate_rejects(kw, code):
+    assert _gate(**kw) == code
+
+
+def test_output_gate_in_place_and_empty_are_accepted():
+    assert _gate(rows=0, o=None, gate=None, y=None) == 0
+    assert _gate(H=0) == 0
+
+
+def _decode_gated(**kw):
+    big = 1 << 24
+    args = dict(qp=A, kp=A, vp=A, w=A, cache=A, pos=0, g=A, beta=A, S=A, gate=A + big, nw=None,
+                eps=1e-6, y=A + 2 * big, N=2, H=3, dk=64, dv=64, width=4, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_decode_step_gated(
+        vp(args["qp"]), vp(args["kp"]), vp(args["vp"]), vp(args["w"]), vp(args["cache"]), args["pos"],
+        vp(args["g"]), vp(args["beta"]), vp(args["S"]), vp(args["gate"]), vp(args["nw"]), args["eps"],
+        vp(args["y"]), args["N"], args["H"], args["dk"], args["dv"], args["width"], args["dtype"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate=None), -1), (dict(gate=MIS), -1), (dict(nw=MIS), -1), (dict(eps=0.0), -1),
+    (dict(y=None), -1), (dict(width=3), -1), (dict(dk=32), -2),
+])
+def test_decode_gated_rejects(kw, code):
+    assert _decode_gated(**kw) == code
+
+
+def test_decode_gated_empty_is_a_no_op():
+    assert _decode_gated(N=0, S=None, gate=None) == 0
