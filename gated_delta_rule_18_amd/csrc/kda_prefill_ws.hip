@@ -19,8 +19,9 @@
 //   S_out  = Diag(Gam) S + Ke^T U
 // With the chunk start as the reference point every factor spans at most 16
 // positions: P and Gam / P lie in [e^-80, 1] and 1 / P in [1, e^80] -- exactly
-// the range the pages' bound guarantees.  Every factor is built as a running
-// product of a_t = exp(g_t) (one exponential per element).
+// the range the pages' bound guarantees.  P is a running product of
+// a_t = exp(g_t) (one exponential per element); 1 / P comes from the hardware
+// reciprocal (e^80 = 5.5e34 is far inside fp32) and Gam / P = Gam * (1 / P).
 //
 // Work decomposition.  A workgroup owns one (sequence, head, 64-wide value
 // slice); value columns of S never interact.  It runs 4 consumer wavefronts
@@ -31,12 +32,14 @@
 //                      chunk in order; o goes straight to HBM;
 //   producers       -- producer p owns chunks p, p+NP, p+2NP, ...: it loads q,
 //                      k, g, v directly in its compute layout (lane = four key
-//                      channels x eight tokens), builds the decayed operands
-//                      with in-register running products, forms A and M on
-//                      MFMA, the UT inverse on fp32 MFMA, and publishes the
-//                      consumers' operands in a ring of NS LDS slots; the loads
-//                      of its next chunk are issued as soon as the raw
-//                      registers of the current one are consumed.
+//                      channels x eight tokens), builds the decayed operands in
+//                      registers (running products of exp(g); Kc = k / P through
+//                      the hardware reciprocal), and only then claims one of NS
+//                      LDS slots, writes the consumers' operand images, issues
+//                      the loads of its next chunk, forms A and M on MFMA and
+//                      the UT inverse on fp32 MFMA, and publishes the slot.
+//                      Claiming the slot late keeps it held for the MFMA part
+//                      only, so more chunks are in flight at once.
 // Producers and consumers hand slots over through per-slot LDS flags ("ready"
 // and per-consumer "done"); every wait is bounded and a WG-wide abort flag ends
 // all waits if one ever runs out (the result is then wrong, never a hang).
@@ -560,32 +563,32 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     auto produce = [&](RawC<E> &raw, int c) {
         typedef typename PE::T PT;
         const int s = c % NS;
-        if (c >= NS)
-            wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
-        E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
-        float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
         // lane coordinates re-derived per chunk: the masks and selects built from
         // them below are cheap, and hoisting them all out of the loop would not
         // fit the register files
         int r16 = l16, rg4 = g4;
         asm volatile("" : "+v"(r16), "+v"(rg4));
 
-        // ---- V^T image: lane (vq, tq) writes value columns 4vq .. 4vq+3 for token
+        // The operands are built in registers first and written to the slot only
+        // once it is free: a slot is then held for the MFMA part of the chunk
+        // alone, not for its elementwise part too, so more chunks are in flight.
+        // ---- V^T pieces: lane (vq, tq) holds value columns 4vq .. 4vq+3 for token
         // group tq (two 8-element pieces: columns 4vq, +1 and 4vq+2, +3) --------
-        {
-            const int vq = lane & 15, tq = lane >> 4;
-            E *vt = sl + L::eV + L::tile(vq >> 2) + 4 * (4 * (vq & 3) + 16 * tq);
-            st_quad(vt, PE::los(raw.v[0].a, raw.v[1].a), PE::los(raw.v[2].a, raw.v[3].a),
-                    PE::his(raw.v[0].a, raw.v[1].a), PE::his(raw.v[2].a, raw.v[3].a));
-            st_quad(vt + 8, PE::los(raw.v[0].b, raw.v[1].b), PE::los(raw.v[2].b, raw.v[3].b),
-                    PE::his(raw.v[0].b, raw.v[1].b), PE::his(raw.v[2].b, raw.v[3].b));
-        }
+        PT vtp[8];
+        vtp[0] = PE::los(raw.v[0].a, raw.v[1].a), vtp[1] = PE::los(raw.v[2].a, raw.v[3].a);
+        vtp[2] = PE::his(raw.v[0].a, raw.v[1].a), vtp[3] = PE::his(raw.v[2].a, raw.v[3].a);
+        vtp[4] = PE::los(raw.v[0].b, raw.v[1].b), vtp[5] = PE::los(raw.v[2].b, raw.v[3].b);
+        vtp[6] = PE::his(raw.v[0].b, raw.v[1].b), vtp[7] = PE::his(raw.v[2].b, raw.v[3].b);
 
         // ---- decay factors by running products, then the operands ------------
         // Lane (cq, th): key channels 4cq + u (u < 4), tokens 8th + i (i < 8).
         // The two halves of the chunk meet through the partner lane l ^ 32.
-        if (4 * (lane & 31) < DK) {
-            const int cq = lane & 31, th = lane >> 5;
+        const bool ew = 4 * (lane & 31) < DK;
+        const int cq = lane & 31, th = lane >> 5;
+        const int io = L::img16(8 * th, 4 * cq);          // token 8th + i adds 8 i
+        PT ktp[8][2], qtp[8][2], kep[2][8];
+        float gm4[4];
+        if (ew) {
             float al[4][8];                               // alpha = e^g
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -594,39 +597,19 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                 al[2][i] = __builtin_amdgcn_exp2f(PE::lo(raw.g[i].b) * 1.4426950408889634f);
                 al[3][i] = __builtin_amdgcn_exp2f(PE::hi(raw.g[i].b) * 1.4426950408889634f);
             }
-            // local suffix products z_i = prod_{i' > i} alpha_i' over this half, and
-            // the half's total; the partner's total completes both directions:
-            //   first half:  P_r = local prefix,             Z_r = z_r * total(second)
-            //   second half: P_r = total(first) * local prefix, Z_r = z_r
-            float Z[4][8], tot[4], oth[4];
+            // each half's total (a product tree over its 8 tokens); the partner's
+            // total starts the second half's prefix and completes Gam = e^{G_15}
+            float oth[4], p[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                float z = 1.f;
-#pragma unroll
-                for (int i = 7; i >= 0; --i) {
-                    Z[u][i] = z;
-                    z *= al[u][i];
-                }
-                tot[u] = z;
-                oth[u] = __shfl_xor(z, 32, 64);
-            }
-            float p[4], ig[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float gm = tot[u] * oth[u];         // Gam = e^{G_15}
-                ig[u] = __builtin_amdgcn_rcpf(gm);
+                const float t01 = al[u][0] * al[u][1], t23 = al[u][2] * al[u][3];
+                const float t45 = al[u][4] * al[u][5], t67 = al[u][6] * al[u][7];
+                const float tot = (t01 * t23) * (t45 * t67);
+                oth[u] = __shfl_xor(tot, 32, 64);
+                gm4[u] = tot * oth[u];
                 p[u] = th ? oth[u] : 1.f;
-                const float zm = th ? 1.f : oth[u];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    Z[u][i] *= zm;
-                tot[u] = gm;
             }
-            if (th == 0)
-                *reinterpret_cast<f32x4 *>(gam + 4 * cq) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-            // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Ke = k Z, Kc = Ke / Gam = k / P
-            const int io = L::img16(8 * th, 4 * cq);      // token 8th + i adds 8 i
-            E *ke = sl + L::eKe + L::tile(cq >> 2) + 4 * (4 * (cq & 3) + 32 * th);   // token group 2th + j adds 64 j
+            // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Kc = k / P, Ke = Kc Gam
             float es[4][4];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -639,22 +622,51 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                     p[u] *= al[u][i];
                     kt[u] = -(kk[u] * p[u]);   // stored negated (see the consumer)
                     qt[u] = qq[u] * p[u];
-                    es[u][i & 3] = kk[u] * Z[u][i];
-                    kc[u] = es[u][i & 3] * ig[u];
+                    kc[u] = kk[u] * __builtin_amdgcn_rcpf(p[u]);
+                    es[u][i & 3] = kc[u] * gm4[u];
                 }
-                st_pair2(sl + L::eKt + io + 8 * i, PE::pack(kt[0], kt[1]), PE::pack(kt[2], kt[3]));
-                st_pair2(sl + L::eQt + io + 8 * i, PE::pack(qt[0], qt[1]), PE::pack(qt[2], qt[3]));
+                ktp[i][0] = PE::pack(kt[0], kt[1]), ktp[i][1] = PE::pack(kt[2], kt[3]);
+                qtp[i][0] = PE::pack(qt[0], qt[1]), qtp[i][1] = PE::pack(qt[2], qt[3]);
+                // Kc only feeds this producer's own products: its private image
                 st_pair2(pKc + io + 8 * i, PE::pack(kc[0], kc[1]), PE::pack(kc[2], kc[3]));
                 if ((i & 3) == 3) {
-                    E *d = ke + 64 * (i >> 2);
-                    st_quad(d, PE::pack(es[0][0], es[0][1]), PE::pack(es[0][2], es[0][3]),
-                            PE::pack(es[1][0], es[1][1]), PE::pack(es[1][2], es[1][3]));
-                    st_quad(d + 8, PE::pack(es[2][0], es[2][1]), PE::pack(es[2][2], es[2][3]),
-                            PE::pack(es[3][0], es[3][1]), PE::pack(es[3][2], es[3][3]));
+                    PT *d = kep[i >> 2];
+                    d[0] = PE::pack(es[0][0], es[0][1]), d[1] = PE::pack(es[0][2], es[0][3]);
+                    d[2] = PE::pack(es[1][0], es[1][1]), d[3] = PE::pack(es[1][2], es[1][3]);
+                    d[4] = PE::pack(es[2][0], es[2][1]), d[5] = PE::pack(es[2][2], es[2][3]);
+                    d[6] = PE::pack(es[3][0], es[3][1]), d[7] = PE::pack(es[3][2], es[3][3]);
                 }
             }
         }
         const unsigned braw = raw.b;
+
+        // ---- claim the slot, then write the consumers' operand images ----------
+        if (c >= NS)
+            wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
+        E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
+        float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
+        {
+            const int vq = lane & 15, tq = lane >> 4;
+            E *vt = sl + L::eV + L::tile(vq >> 2) + 4 * (4 * (vq & 3) + 16 * tq);
+            st_quad(vt, vtp[0], vtp[1], vtp[2], vtp[3]);
+            st_quad(vt + 8, vtp[4], vtp[5], vtp[6], vtp[7]);
+        }
+        if (ew) {
+            if (th == 0)
+                *reinterpret_cast<f32x4 *>(gam + 4 * cq) = f32x4{gm4[0], gm4[1], gm4[2], gm4[3]};
+            E *ke = sl + L::eKe + L::tile(cq >> 2) + 4 * (4 * (cq & 3) + 32 * th);   // token group 2th + j adds 64 j
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                st_pair2(sl + L::eKt + io + 8 * i, ktp[i][0], ktp[i][1]);
+                st_pair2(sl + L::eQt + io + 8 * i, qtp[i][0], qtp[i][1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                st_quad(ke + 64 * j, kep[j][0], kep[j][1], kep[j][2], kep[j][3]);
+                st_quad(ke + 64 * j + 8, kep[j][4], kep[j][5], kep[j][6], kep[j][7]);
+            }
+        }
+        // the next chunk's loads, once this chunk's raw registers are dead
         load(raw, c + L::NP);
         lds_fence();
 
