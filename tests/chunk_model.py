@@ -80,3 +80,68 @@ def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve"):
         o[sl] = (qc * np.exp(G)) @ S + M @ U
         S = np.exp(G[-1])[:, None] * S + (kc * np.exp(G[-1] - G)).T @ U
     return o, S
+
+
+def chunk_backward(q, k, v, g, beta, S0, dO, dS_T, C, inverse="solve"):
+    """Gradients of <dO, o> + <dS_T, S_T> through the chunk form above (one head),
+    by reverse-mode differentiation of each chunk's matrix expressions, chunks in
+    reverse order with the incoming state of each chunk from a forward pass.
+    With chunk-relative G (cumulative log-decay), P = exp(G), Gam = P[-1]:
+        Kt = k P, Qt = q P, Kc = k / P, Ke = k Gam / P,  B = Kt Kc^T,
+        A = strict_lower(Diag(beta) B), L = (I + A)^{-1}, Tm = L Diag(beta),
+        X = V - Kt S, U = Tm X, M = lower(Qt Kc^T),
+        O = Qt S + M U,  S' = Diag(Gam) S + Ke^T U.
+    Returns (dq, dk, dv, dg, dbeta, dS0) as float64 arrays."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    starts = []                                   # incoming state of every chunk
+    for c0 in range(0, T, C):
+        starts.append(S.copy())
+        sl = slice(c0, min(T, c0 + C))
+        _, S = chunk_forward(q[sl], k[sl], v[sl], g[sl], beta[sl], S, C, ref="direct", inverse=inverse)
+    dq, dk_, dv_, dg, db = (np.zeros_like(x) for x in (q, k, v, g, beta))
+    dSn = np.array(dS_T, dtype=np.float64)        # gradient w.r.t. the chunk's outgoing state
+    for ci in range(len(starts) - 1, -1, -1):
+        c0 = ci * C
+        sl = slice(c0, min(T, c0 + C))
+        qc, kc, vc, gc, bc, dOc = q[sl], k[sl], v[sl], g[sl], beta[sl], dO[sl]
+        S = starts[ci]
+        n = qc.shape[0]
+        G = np.cumsum(gc, axis=0)
+        P = np.exp(G)
+        Gam = P[-1]
+        Kt, Qt, Kc, Ke = kc * P, qc * P, kc / P, kc * (Gam / P)
+        B = Kt @ Kc.T
+        A = np.tril(bc[:, None] * B, -1)
+        L = np.linalg.solve(np.eye(n) + A, np.eye(n)) if inverse == "solve" else nilpotent_inverse(A)
+        Tm = L * bc[None, :]
+        X = vc - Kt @ S
+        U = Tm @ X
+        M = np.tril(Qt @ Kc.T)
+        # reverse mode
+        dU = M.T @ dOc + Ke @ dSn
+        dM = np.tril(dOc @ U.T)
+        dQt = dOc @ S.T + dM @ Kc
+        dKc = dM.T @ Qt
+        dKe = U @ dSn.T
+        dX = Tm.T @ dU
+        dTm = dU @ X.T
+        dKt = -dX @ S.T
+        dS = Qt.T @ dOc + Gam[:, None] * dSn - Kt.T @ dX
+        dL = dTm * bc[None, :]
+        dbc = np.sum(L * dTm, axis=0)
+        dA = np.tril(-L.T @ dL @ L.T, -1)
+        dbc += np.sum(dA * B, axis=1)
+        dB = bc[:, None] * dA
+        dKt += dB @ Kc
+        dKc += dB.T @ Kt
+        dk_[sl] = dKt * P + dKc / P + dKe * (Gam / P)
+        dq[sl] = dQt * P
+        dG = dKt * Kt + dQt * Qt - dKc * Kc - dKe * Ke
+        dG[-1] += np.sum(dSn * S, axis=1) * Gam + np.sum(dKe * Ke, axis=0)
+        dg[sl] = np.cumsum(dG[::-1], axis=0)[::-1]
+        dv_[sl] = dX
+        db[sl] = dbc
+        dSn = dS
+    return dq, dk_, dv_, dg, db, dSn

@@ -519,3 +519,101 @@ def test_output_gate_rejects():
         oracle.output_gate(o, np.zeros((2, 3, 5)))
     with pytest.raises(ValueError):
         oracle.output_gate(o, o, np.ones(3))
+
+
+# ---------------------------------------------------------------------------
+# Backward: exact gradients of <dO, o> + <dS_T, S_T> (oracle/backward.py).
+
+from oracle import backward as obwd
+from tests.chunk_model import chunk_backward
+
+
+def _bwd_case(rng, B, T, H, dk, dv, **kw):
+    q, k, v, g, beta, S0 = _rand_inputs(rng, B, T, H, dk, dv, **kw)
+    dO = rng.standard_normal((B, T, H, dv))
+    dS = rng.standard_normal((B, H, dk, dv))
+    return q, k, v, g, beta, S0, dO, dS
+
+
+def _objective(q, k, v, g, beta, S0, dO, dS):
+    o, S_T = oracle.prefill(q, k, v, g, beta, S0)
+    return float(np.sum(o * dO) + np.sum(S_T * dS))
+
+
+def test_backward_matches_central_differences_of_the_forward_oracle():
+    """Directional derivatives of the (pinned) C forward oracle, by central
+    differences, against <gradient, direction> for every input."""
+    rng = np.random.default_rng(51)
+    x = list(_bwd_case(rng, 1, 7, 2, 5, 4))
+    grads = obwd.backward(*x)
+    names = ("q", "k", "v", "g", "beta", "S0")
+    h = 1e-6
+    for idx, name in enumerate(names):
+        d = rng.standard_normal(np.shape(x[idx]))
+        xp = list(x)
+        xm = list(x)
+        xp[idx] = x[idx] + h * d
+        xm[idx] = x[idx] - h * d
+        fd = (_objective(*xp) - _objective(*xm)) / (2 * h)
+        an = float(np.sum(grads[idx] * d))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_decay_only_closed_form():
+    """beta = 0: S_t = Diag(e^{G_t}) S0, o_t = S_t^T q_t, so dv = 0, dq_t = S_t dO_t and
+    dS0 = Diag(e^{G_T}) dS_T + sum_t Diag(e^{G_t}) q_t dO_t^T."""
+    rng = np.random.default_rng(52)
+    q, k, v, g, beta, S0, dO, dS = _bwd_case(rng, 1, 9, 1, 6, 5)
+    beta = np.zeros_like(beta)
+    dq, dk_, dv_, dg, db, dS0 = obwd.backward(q, k, v, g, beta, S0, dO, dS)
+    G = np.cumsum(g[0, :, 0], axis=0)                       # [T, dk]
+    np.testing.assert_allclose(dv_, 0.0, atol=1e-15)
+    want_dq = np.stack([(np.exp(G[t])[:, None] * S0[0, 0]) @ dO[0, t, 0] for t in range(9)])
+    np.testing.assert_allclose(dq[0, :, 0], want_dq, rtol=1e-12, atol=1e-13)
+    want_dS0 = np.exp(G[-1])[:, None] * dS[0, 0] + sum(
+        np.exp(G[t])[:, None] * np.outer(q[0, t, 0], dO[0, t, 0]) for t in range(9))
+    np.testing.assert_allclose(dS0[0, 0], want_dS0, rtol=1e-12, atol=1e-13)
+    # d/dg_s of sum_t <dO_t, S_t^T q_t> + <dS, S_T>: channel c of g_s scales rows c of S_t for t >= s
+    terms = np.stack([np.exp(G[t]) * (S0[0, 0] @ dO[0, t, 0]) * q[0, t, 0] for t in range(9)])
+    last = np.exp(G[-1]) * np.sum(S0[0, 0] * dS[0, 0], axis=1)
+    want_dg = np.cumsum(terms[::-1], axis=0)[::-1] + last[None, :]
+    np.testing.assert_allclose(dg[0, :, 0], want_dg, rtol=1e-12, atol=1e-13)
+
+
+def test_backward_is_linear_in_the_upstream_gradients():
+    rng = np.random.default_rng(53)
+    q, k, v, g, beta, S0, dO, dS = _bwd_case(rng, 1, 6, 2, 4, 4)
+    a = obwd.backward(q, k, v, g, beta, S0, dO, dS)
+    b = obwd.backward(q, k, v, g, beta, S0, 2.5 * dO, 2.5 * dS)
+    c = obwd.backward(q, k, v, g, beta, S0, dO, np.zeros_like(dS))
+    d = obwd.backward(q, k, v, g, beta, S0, np.zeros_like(dO), dS)
+    for x, y, u, w in zip(a, b, c, d):
+        np.testing.assert_allclose(y, 2.5 * x, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(u + w, x, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,inverse", [(16, "solve"), (16, "product"), (5, "solve"), (32, "solve")])
+def test_chunk_backward_matches_oracle(C, inverse):
+    """The chunk-form reverse mode (a second derivation) equals the autograd oracle."""
+    rng = np.random.default_rng(54)
+    q, k, v, g, beta, S0, dO, dS = _bwd_case(rng, 1, 40, 1, 8, 6)
+    ref = obwd.backward(q, k, v, g, beta, S0, dO, dS)
+    got = chunk_backward(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0], S0[0, 0],
+                         dO[0, :, 0], dS[0, 0], C, inverse=inverse)
+    for name, r, x in zip(("dq", "dk", "dv", "dg", "dbeta"), ref[:5], got[:5]):
+        np.testing.assert_allclose(x, r[0, :, 0], rtol=1e-9, atol=1e-10, err_msg=name)
+    np.testing.assert_allclose(got[5], ref[5][0, 0], rtol=1e-9, atol=1e-10, err_msg="dS0")
+
+
+def test_chunk_backward_at_the_bound():
+    """g = -5 everywhere (the pages' lower bound): the reciprocal decay reaches e^{75}
+    inside a 16-token chunk; the chunk form still matches the oracle."""
+    rng = np.random.default_rng(55)
+    q, k, v, g, beta, S0, dO, dS = _bwd_case(rng, 1, 32, 1, 8, 6)
+    g = np.full_like(g, -5.0)
+    ref = obwd.backward(q, k, v, g, beta, S0, dO, dS)
+    got = chunk_backward(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0], S0[0, 0],
+                         dO[0, :, 0], dS[0, 0], 16)
+    for name, r, x in zip(("dq", "dk", "dv", "dg", "dbeta"), ref[:5], got[:5]):
+        scale = max(1.0, float(np.abs(r).max()))
+        assert np.abs(x - r[0, :, 0]).max() <= 1e-9 * scale, name
