@@ -15,7 +15,8 @@ fourth (reported under "prep") kda_prefill_prep on the same B=1, H=96, T=65536
 shape: projected pre-activations to q, k, v, g, beta.  A fifth (reported under
 "gate") times kda_output_gate on the prefill output shape (65536 tokens x 96
 heads x 128, bf16), and a sixth (under "decode_gated") kda_decode_step_gated on
-the decode batch.
+the decode batch.  A seventh (under "bwd") times kda_chunk_bwd, the backward
+pass, on the B=4, H=32, T=4096, dk=dv=128 bf16 prefill shape (gradients fp32).
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, TFLOP/s (published; counts packed FP32)
 
 
 def prefill_bytes(B, T, H, dk, dv):
@@ -64,6 +66,24 @@ def prep_bytes(B, T, H, dk, dv, W=4):
     nch = 2 * dk + dv
     per_token_head = 2 * (2 * nch + 2 * dk + 2)
     return B * T * H * per_token_head + H * 4 * nch * W + B * H * 4 * (W - 1) * nch
+
+
+def bwd_flops(B, T, H, dk, dv, C=16):
+    """Arithmetic of one kda_chunk_bwd call: per token-head the chunk reverse mode,
+    2(7 dk dv + 2C(dk + 2dv) + 4C dk) + 2 dk dv / C (the products X, Ke D, dO S^T,
+    U D^T, dX S^T, the two state-gradient products; B, M, U, dX, dM, dTm; the small
+    Kc / Qt / Kt products; rowsum(D S)), plus the forward recompute F(C)."""
+    per = 2 * (7 * dk * dv + 2 * C * (dk + 2 * dv) + 4 * C * dk) + 2 * dk * dv / C
+    return B * T * H * (per + prefill_flops(1, 1, 1, dk, dv, C))
+
+
+def bwd_bytes(B, T, H, dk, dv, es=2, C=16):
+    """Algorithmic HBM bytes of one kda_chunk_bwd call: inputs q, k, v, g, beta, dO in the
+    activation dtype; the recomputed incoming state of every chunk written once and read once
+    (8 dk dv per chunk-head); fp32 gradients dq, dk, dg, dv, dbeta out; S0, dS_T in and dS0 out."""
+    nch = (T + C - 1) // C
+    per_token = es * (3 * dk + 2 * dv + 1) + 4 * (3 * dk + dv + 1)
+    return B * T * H * per_token + B * H * (max(nch - 1, 0) * 8 * dk * dv + 12 * dk * dv)
 
 
 def gate_bytes(rows, H, dv):
@@ -154,6 +174,7 @@ def main():
     ap.add_argument("--skip-snapshots", action="store_true")
     ap.add_argument("--skip-prep", action="store_true")
     ap.add_argument("--skip-gate", action="store_true")
+    ap.add_argument("--skip-bwd", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -166,7 +187,8 @@ def main():
     import torch
 
     from gated_delta_rule_18_amd import binding
-    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, WORKLOADS, decode_gate_inputs,
+    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, WORKLOADS, backward_inputs,
+                                                decode_gate_inputs,
                                                 decode_state, decode_step_inputs, gate_inputs,
                                                 prefill_inputs, prep_inputs)
 
@@ -338,6 +360,37 @@ def main():
         }
         del xg, yg
 
+    # ---------------- backward (training) -----------------------------------------
+    bwd = None
+    if not args.skip_bwd:
+        bs = WORKLOADS["prefill_b4h32"]
+        xb = prefill_inputs(bs, device=dev)
+        gb = backward_inputs(bs, device=dev)
+        ws = torch.empty(max(binding.workspace_size(bs.B, bs.T, bs.H, bs.dk, bs.dv), 1), dtype=torch.uint8,
+                         device=dev)
+        torch.cuda.synchronize()
+
+        def bwd_step(i=0):
+            binding.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["S0"], gb["dO"], gb["dS_T"],
+                              workspace=ws)
+
+        b_wall, b_kern = _timed(bwd_step, args.steps, args.warmup, torch)
+        b_fl = bwd_flops(bs.B, bs.T, bs.H, bs.dk, bs.dv)
+        b_by = bwd_bytes(bs.B, bs.T, bs.H, bs.dk, bs.dv)
+        b_tf = b_fl / (b_kern * 1e-3) / 1e12
+        bwd = {
+            "workload": f"backward B{bs.B} H{bs.H} T{bs.T} dk=dv={bs.dk} bf16 inputs, fp32 gradients",
+            "ms_per_step": b_wall,
+            "kernel_ms": b_kern,
+            "tokens_per_s": bs.B * bs.T / (b_wall * 1e-3),
+            "gbps": b_by / (b_kern * 1e-3) / 1e9,
+            "hbm_frac": b_by / (b_kern * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "roofline": {"bound": "alu", "achieved": b_tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": b_tf / FP32_VALU_PEAK_TFLOPS, "traffic": None, "flops_per_launch": b_fl,
+                         "bytes_per_launch": b_by},
+        }
+        del xb, gb, ws
+
     line = {
         "metric": "KDA prefill tokens/s & TFLOP/s (% MFMA peak); decode-step HBM GB/s (% peak)",
         "value": B * T / (p_wall * 1e-3),
@@ -367,6 +420,7 @@ def main():
         "snapshots": snapshots,
         "prep": prep,
         "gate": gate,
+        "bwd": bwd,
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu

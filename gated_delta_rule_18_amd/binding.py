@@ -10,6 +10,7 @@ the calls raise (there is no fallback).
     q, k, v, g, beta, conv_final = prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A,
                                                 beta_logit)
     y             = output_gate(o, gate, norm_w=None, eps=1e-6)
+    dq, dk, dv, dg, dbeta, dS0 = chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None)
     y             = decode_step_gated(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta,
                                       S, gate, norm_w=None, eps=1e-6)
 
@@ -26,8 +27,9 @@ library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_gated",
-           "kda_output_gate", "kda_prefill_prep", "kda_strerror", "kda_version")
+EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_snapshots",
+           "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
+           "kda_version")
 
 _lib = None
 
@@ -56,6 +58,10 @@ def lib():
         L.kda_decode_step_gated.restype = i
         L.kda_decode_step_gated.argtypes = ([vp] * 5 + [i] + [vp] * 5 + [ctypes.c_float, vp]
                                             + [i] * 6 + [vp])
+        L.kda_chunk_bwd.restype = i
+        L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t] + [i] * 6 + [vp]
+        L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_bwd_workspace_size.argtypes = [i] * 5
         L.kda_output_gate.restype = i
         L.kda_output_gate.argtypes = [vp] * 4 + [i] * 3 + [ctypes.c_float, i, vp]
         L.kda_prefill_prep.restype = i
@@ -152,6 +158,43 @@ def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_ev
                                  _ptr(S_T), B, T, H, dk, dv, code, int(chunk), _stream(dev))
     _check(rc)
     return o, S_T, snaps
+
+
+def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=None):
+    """Gradients of <dO, o> + <dS_T, S_T> through chunk_fwd.  Inputs as chunk_fwd plus
+    dO [B,T,H,dv] (input dtype) and dS_T [B,H,dk,dv] fp32 or None (zero).  Returns fp32
+    (dq, dk, dv, dg, dbeta, dS0); dS0 is None when return_dS0 is False.  `workspace`
+    may supply a uint8 device tensor of at least workspace_size(...) bytes."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)), ("dO", dO, (B, T, H, dv))):
+        _want(t, name, shp, dt, dev)
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _want(t, name, (B, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk_, dg = (torch.empty((B, T, H, dk), **f32) for _ in range(3))
+    dv_ = torch.empty((B, T, H, dv), **f32)
+    db = torch.empty((B, T, H), **f32)
+    dS0 = torch.empty((B, H, dk, dv), **f32) if return_dS0 else None
+    need = workspace_size(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need or workspace.device != dev:
+        raise ValueError(f"workspace: need {need} bytes on {dev}")
+    rc = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+                             _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace),
+                             int(workspace.numel()), B, T, H, dk, dv, code, _stream(dev))
+    _check(rc)
+    return dq, dk_, dv_, dg, db, dS0
+
+
+def workspace_size(B, T, H, dk, dv):
+    """Bytes of workspace chunk_bwd needs."""
+    return int(lib().kda_chunk_bwd_workspace_size(B, T, H, dk, dv))
 
 
 def decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S, o=None):

@@ -192,6 +192,67 @@ int kda_output_gate(const void *o, const void *gate, const float *norm_w, void *
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv)
+{
+    if (B < 0 || T < 0 || H < 0 || !head_ok(dk) || !head_ok(dv))
+        return 0;
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40))
+        return 0;
+    return kda::chunk_bwd_workspace_floats(B, T, H, dk, dv) * sizeof(float);
+}
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                  const float *S0, const void *dO, const float *dS_T, float *dq, float *dk,
+                  float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                  size_t workspace_bytes, int B, int T, int H, int dk_size, int dv_size, int dtype,
+                  void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk_size <= 0 || dv_size <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk_size) || !head_ok(dv_size))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * (dk_size > dv_size ? dk_size : dv_size) > (1LL << 40) || B > 65535 ||
+        H > 65535)
+        return KDA_ERR_INVALID;
+    if ((long long)B * H == 0)
+        return KDA_OK;
+    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, dk_size, dv_size);
+    if (workspace_bytes < need || (need > 0 && !workspace) ||
+        (reinterpret_cast<std::uintptr_t>(workspace) & 255u))
+        return KDA_ERR_INVALID;
+    const bool has_tokens = T > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDA_ERR_INVALID;
+    const long long es = dtype == KDA_FP32 ? 4 : 2;
+    const long long rows = (long long)B * T * H;
+    const long long sb = (long long)B * H * dk_size * dv_size * 4;
+    const void *in[] = {q, k, v, g, beta, S0, dO, dS_T, workspace};
+    const long long in_n[] = {rows * dk_size * es, rows * dk_size * es, rows * dv_size * es,
+                              rows * dk_size * es, rows * es, sb, rows * dv_size * es, sb,
+                              (long long)need};
+    const void *out[] = {dq, dk, dv, dg, dbeta, dS0};
+    const long long out_n[] = {rows * dk_size * 4, rows * dk_size * 4, rows * dv_size * 4,
+                               rows * dk_size * 4, rows * 4, sb};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 9; ++j)
+            if (overlap(out[i], out_n[i], in[j], in_n[j]))
+                return KDA_ERR_INVALID;
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out_n[i], out[j], out_n[j]))
+                return KDA_ERR_INVALID;
+    }
+    hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0,
+                                         static_cast<float *>(workspace), B, T, H, dk_size, dv_size,
+                                         dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
                      const void *conv_init, const void *z, const float *A, const void *beta_logit,
                      void *q, void *k, void *v, void *g, void *beta, void *conv_final, int B, int T,

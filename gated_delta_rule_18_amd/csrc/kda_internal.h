@@ -39,6 +39,14 @@ hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *
                               int N, int H, int dk, int dv, bool fp32, const OutputGate &og,
                               hipStream_t stream);
 
+// Backward pass: gradients (fp32) of <dO, o> + <dS_T, S_T> through kda_chunk_fwd.
+// workspace holds chunk_bwd_workspace_floats(...) floats.
+size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);
+hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                            const float *S0, const void *dO, const float *dST, float *dq, float *dk,
+                            float *dv, float *dg, float *dbeta, float *dS0, float *workspace, int B, int T,
+                            int H, int DK, int DV, bool fp32, hipStream_t stream);
+
 // The output exposure gate alone over `units` (row, head) rows of dv elements.
 hipError_t launch_output_gate(const void *o, const void *gate, const float *w, void *y, long units,
                               int dv, float eps, bool fp32, hipStream_t stream);

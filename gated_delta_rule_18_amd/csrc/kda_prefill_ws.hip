@@ -433,10 +433,12 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         // buffer and are dropped).
         const int rso = H * DV * L::ES;                   // bytes between token rows of o
         const int ovo = (4 * g4) * rso + l16 * L::ES;
-        E *otile = o + (tokb * H + h) * (long)DV + slice * kVS + 16 * w;
+        long ooff = (tokb * H + h) * (long)DV + slice * kVS + 16 * w;   // o tile of chunk 0
         const long ostep = (long)kC * H * DV;
-        const int ofull = rows_bytes(kC, rso, 16 * L::ES);
-        const int olast = rows_bytes(T - (nchunks - 1) * kC, rso, 16 * L::ES);
+        // o == nullptr (an internal caller that only wants states): every store
+        // falls outside an empty buffer and is dropped
+        const int ofull = o ? rows_bytes(kC, rso, 16 * L::ES) : 0;
+        const int olast = o ? rows_bytes(T - (nchunks - 1) * kC, rso, 16 * L::ES) : 0;
 
         // this lane's byte offsets inside a slot: image16 pieces (Kt, Qt),
         // image4 pieces (Ke^T, V^T, T, M) and the Gam pair (see decay_rows)
@@ -540,9 +542,9 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             s = s + 1 == NS ? 0 : s + 1;
             if (c + 1 < nchunks)
                 fetch(op, s, c + 1);
-            const __amdgpu_buffer_rsrc_t ro = buffer(otile, c + 1 < nchunks ? ofull : olast);
+            const __amdgpu_buffer_rsrc_t ro = buffer(o ? o + ooff : o, c + 1 < nchunks ? ofull : olast);
             store_o(ro, ovo, rso, O, (E *)nullptr);
-            otile += ostep;
+            ooff += ostep;
         }
         if (S_T)
             store_state(S_T + (long)bh * DK * DV, Sacc, lane_soff, DV);

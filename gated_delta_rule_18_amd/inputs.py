@@ -25,7 +25,8 @@ Draw order per call: q, k, v, beta logits, g logits, S0, then the bound mask
 q_pre, k_pre, v_pre, beta logits, g logits.  Prefill preprocessing: conv weights,
 A, conv history, then q_pre, k_pre, v_pre, z, beta logits.  Output gate: o,
 gate pre-activations, RMSNorm weight.  Decode gate pre-activations: one draw per
-step from seed seed_base + 10000 + step.
+step from seed seed_base + 10000 + step.  Backward upstream gradients: dO, then
+dS_T, from seed spec.seed + 7000.
 """
 from dataclasses import dataclass, field
 
@@ -206,6 +207,17 @@ def prep_inputs(spec: PrepSpec, device="cpu", seed=None, T=None):
                         ("z", (B, T, H, dk)), ("beta_logit", (B, T, H)))}
     x.update(conv_w=conv_w.contiguous(), A=A.contiguous(), conv_init=init)
     return x
+
+
+def backward_inputs(spec: PrefillSpec, device="cpu", seed=None, T=None, ds_std=1.0):
+    """Upstream gradients for a backward call: dO ~ N(0,1) [B,T,H,dv] in spec.dtype and
+    dS_T ~ ds_std N(0,1) [B,H,dk,dv] fp32 (None when ds_std == 0); seed spec.seed + 7000."""
+    seed = spec.seed + 7000 if seed is None else seed
+    T = spec.T if T is None else T
+    gen = _gen(device, seed)
+    dO = _randn((spec.B, T, spec.H, spec.dv), gen, device).to(torch_dtype(spec.dtype)).contiguous()
+    dS = (ds_std * _randn((spec.B, spec.H, spec.dk, spec.dv), gen, device)).contiguous() if ds_std else None
+    return dict(dO=dO, dS_T=dS)
 
 
 def gate_inputs(rows, H, dv, dtype="bf16", seed=6, device="cpu", weight=True):

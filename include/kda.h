@@ -33,6 +33,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -223,6 +225,42 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
                           const void *gate, const float *norm_w, float eps, void *y,
                           int N, int H, int dk, int dv, int width, int dtype,
                           void *stream);
+
+/*
+ * kda_chunk_bwd -- backward pass of one KDA layer's recurrence (training).
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.3: training runs the chunked form of the section 3.1 recurrence;
+ * the pages derive no backward pass): the exact gradients of
+ *     Loss = <dO, o> + <dS_T, S_T>
+ * through kda_chunk_fwd's map (q, k, v, g, beta, S0) -> (o, S_T), i.e. the
+ * reverse mode of the chunked recurrence with 16-token chunks.  The call first
+ * recomputes every chunk's incoming state (a forward pass into the workspace),
+ * then walks the chunks from last to first.
+ *
+ *   q, k, g, v, beta, S0 : as kda_chunk_fwd (S0 NULL = zero initial state)
+ *   dO    : [B, T, H, dv] (dtype)   upstream gradient of o
+ *   dS_T  : [B, H, dk, dv] fp32     upstream gradient of S_T; NULL = zero
+ *   dq, dk, dg : [B, T, H, dk] fp32 written
+ *   dv    : [B, T, H, dv] fp32      written
+ *   dbeta : [B, T, H] fp32          written
+ *   dS0   : [B, H, dk, dv] fp32     written; NULL = not returned
+ *   workspace : device memory of kda_chunk_bwd_workspace_size(B, T, H, dk, dv)
+ *               bytes (may be NULL when that size is 0), 256-byte aligned; its
+ *               contents on entry are ignored and on return unspecified
+ *   dk, dv (sizes) : 64 or 128
+ * Gradients are fp32 in both dtype modes.  No output may overlap an input or
+ * another output.  Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size,
+ * workspace too small, overlap), KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH.
+ */
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
+                  const void *beta, const float *S0, const void *dO, const float *dS_T,
+                  float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                  void *workspace, size_t workspace_bytes,
+                  int B, int T, int H, int dk_size, int dv_size, int dtype, void *stream);
+
+/* Bytes of workspace kda_chunk_bwd needs for these sizes (0 for invalid sizes). */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk_size, int dv_size);
 
 /* Human-readable text for a kda_status code (static storage, never NULL). */
 const char *kda_strerror(int status);

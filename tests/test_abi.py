@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "kda.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(kda_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(kda_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_exports():
@@ -201,3 +201,44 @@ def test_decode_gated_rejects(kw, code):
 
 def test_decode_gated_empty_is_a_no_op():
     assert _decode_gated(N=0, S=None, gate=None) == 0
+
+
+def _bwd(**kw):
+    big = 1 << 26
+    args = dict(q=A, k=A, v=A, g=A, beta=A, S0=None, dO=A, dST=None, dq=A + big, dk=A + 2 * big,
+                dv=A + 3 * big, dg=A + 4 * big, db=A + 5 * big, dS0=A + 6 * big, ws=A + 7 * big,
+                wsb=1 << 26, B=1, T=40, H=2, dk_=64, dv_=128, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    n = ("q", "k", "v", "g", "beta", "S0", "dO", "dST", "dq", "dk", "dv", "dg", "db", "dS0", "ws")
+    return binding.lib().kda_chunk_bwd(*(vp(args[a]) for a in n), args["wsb"], args["B"], args["T"], args["H"],
+                                       args["dk_"], args["dv_"], args["dtype"], args["stream"])
+
+
+def test_bwd_workspace_size():
+    # two slices of 64 value columns: the incoming state of chunks 1, 2 and the slice partials
+    want_states = 2 * 2 * 64 * 128 * 4
+    want_parts = 2 * 1 * 40 * 2 * (3 * 64 + 1) * 4
+    rnd = lambda b: (b + 255) // 256 * 256
+    assert binding.workspace_size(1, 40, 2, 64, 128) == rnd(want_states) + rnd(want_parts)
+    assert binding.workspace_size(1, 40, 2, 64, 64) == rnd(2 * 2 * 64 * 64 * 4)    # one slice: no partials
+    assert binding.workspace_size(1, 16, 2, 64, 64) == 0                            # one chunk: nothing
+    assert binding.workspace_size(1, 40, 2, 96, 64) == 0                            # unsupported size
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -1), (dict(T=-1), -1), (dict(dk_=96), -2), (dict(dv_=32), -2),
+    (dict(q=None), -1), (dict(dO=None), -1), (dict(dq=None), -1), (dict(db=None), -1),
+    (dict(wsb=64), -1),                         # workspace too small
+    (dict(ws=A + (7 << 26) + 16), -1),          # workspace not 256-byte aligned
+    (dict(ws=None), -1),
+    (dict(dq=MIS), -1), (dict(S0=MIS), -1),
+    (dict(dk=A + (1 << 26) + 64), -1),          # dk overlaps dq
+    (dict(dv=A + 64), -1),                      # an output overlapping an input
+])
+def test_bwd_rejects(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_empty_batch_is_a_no_op():
+    assert _bwd(B=0, q=None, ws=None, wsb=0) == 0

@@ -8,6 +8,12 @@ from gated_delta_rule_18_amd.inputs import to_f64
 # Parity bars: max|do| <= TOL_O * |o|_inf and max|dS| <= TOL_S * |S|_inf, with the
 # infinity norms taken from the oracle's result.
 TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
+# Gradient bars (kda_chunk_bwd), max|diff| <= TOL_GRAD * |ref|_inf per gradient tensor.
+# A gradient element is a sum over up to 16 dk dv signed products, some of whose
+# factors reach e^{+-75} at the decay bound before they cancel; fp32 accumulation
+# of such sums carries ~1e-5 of the largest term, so fp32 mode is held to 1e-4
+# (measured worst: 3.2e-5).  bf16 mode keeps the forward's bar.
+TOL_GRAD = {"bf16": 2e-2, "fp32": 1e-4}
 
 
 def rel_err(got, ref):
