@@ -28,7 +28,8 @@
 // Work decomposition: one workgroup of 256 threads per (sequence, head,
 // 64-wide value slice) walks the chunks from last to first.  The slice's part
 // of D lives in LDS for the whole walk, the slice's part of S is loaded per
-// chunk; every product is an fp32 FMA loop from LDS.  dV and dS0 are per value
+// chunk; the products are fp32 MFMAs (16 x 16 x 4) reading both operands from
+// LDS through strides, so transposed operands cost nothing extra.  dV and dS0 are per value
 // column and written directly.  dq, dk, dg and dbeta are sums over all value
 // columns, and every expression above after the column contractions (dM, dTm,
 // dQt, dKe, dKt and rowsum(D S)) is linear in them, so each slice computes the
@@ -80,8 +81,95 @@ struct BwdL {
     static constexpr int bytes = floats * 4;
 };
 
-__device__ __forceinline__ float ldE(const __bf16 *p) { return (float)*p; }
-__device__ __forceinline__ float ldE(const float *p) { return *p; }
+// acc (a 16 x 16 tile in the MFMA accumulator layout: lane (n, g) holds rows
+// 4g .. 4g+3 of column n) += sum_{k < K} A[i][k] B[k][n], with both operands read
+// from LDS through strides: A[i][k] = pa[i * sai + k * sak], B[k][n] =
+// pb[k * sbk + n * sbn].  fp32 MFMA, 4 contraction steps per instruction; K is a
+// multiple of 4.
+__device__ __forceinline__ f32x4 mm(const float *pa, int sai, int sak, const float *pb, int sbk, int sbn, int K,
+                                    f32x4 acc)
+{
+    const int lane = threadIdx.x & 63, i = lane & 15, kk = lane >> 4;
+    const float *a = pa + i * sai + kk * sak, *b = pb + kk * sbk + i * sbn;
+#pragma unroll 4
+    for (int s = 0; s < K; s += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s * sak], b[s * sbk], acc, 0, 0, 0);
+    return acc;
+}
+
+
+// Loads of one chunk's inputs for the reverse walk, held in registers: the
+// slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
+// consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
+// of token t / 16), v and dO (4 elements of token t / 16) and beta.
+template <typename E, int DK>
+struct Pre {
+    static constexpr int FPT = DK / 4, TPR = kNV / FPT;      // state floats per thread, threads per row
+    static constexpr int EPT = DK / 16;                       // q/k/g elements per thread
+    f32x4 s[FPT / 4];
+    float qv[EPT], kv[EPT], gv[EPT], vv[4], ov[4], bv;
+
+    __device__ __forceinline__ void load(const E *q, const E *k, const E *v, const E *g, const E *beta,
+                                         const E *dO, const float *S0, const float *states, int ci, int T,
+                                         int H, int DV, int nbh, int bh, long tokb, int h, int col0, int t)
+    {
+        const int t0 = ci * kC, n = T - t0 < kC ? T - t0 : kC;
+        const float *Sin = ci == 0 ? (S0 ? S0 + (long)bh * DK * DV : nullptr)
+                                   : states + ((long)(ci - 1) * nbh + bh) * DK * DV;
+        const int c = t / TPR, j0 = (t % TPR) * FPT;
+#pragma unroll
+        for (int u = 0; u < FPT / 4; ++u)
+            s[u] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (long)c * DV + col0 + j0 + 4 * u)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
+        const bool ok = r < n;
+        const long off = ((tokb + t0 + r) * H + h) * DK + cc;
+        const long offv = ((tokb + t0 + r) * H + h) * (long)DV + col0 + jj;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            qv[e] = ok ? to_f(q[off + e]) : 0.f;
+            kv[e] = ok ? to_f(k[off + e]) : 0.f;
+            gv[e] = ok ? to_f(g[off + e]) : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vv[e] = ok ? to_f(v[offv + e]) : 0.f;
+            ov[e] = ok ? to_f(dO[offv + e]) : 0.f;
+        }
+        bv = (t < kC && t < n) ? to_f(beta[(tokb + t0 + t) * H + h]) : 0.f;
+    }
+
+    template <typename LL>
+    __device__ __forceinline__ void store_to(float *Ss, float *Qt, float *Kt, float *Pm, float *Xs, float *dOs,
+                                             float *bet, int t) const
+    {
+        const int c = t / TPR, j0 = (t % TPR) * FPT;
+#pragma unroll
+        for (int u = 0; u < FPT / 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Ss[c * LL::SS + j0 + 4 * u + e] = s[u][e];
+        const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            Qt[r * LL::OS + cc + e] = qv[e];
+            Kt[r * LL::OS + cc + e] = kv[e];
+            Pm[r * LL::OS + cc + e] = gv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Xs[r * LL::CS + jj + e] = vv[e];
+            dOs[r * LL::CS + jj + e] = ov[e];
+        }
+        if (t < kC)
+            bet[t] = bv;
+    }
+    __device__ __forceinline__ void store(float *Ss, float *Qt, float *Kt, float *Pm, float *Xs, float *dOs,
+                                          float *bet, int t) const
+    {
+        store_to<BwdL<DK>>(Ss, Qt, Kt, Pm, Xs, dOs, bet, t);
+    }
+};
 
 template <typename E, int DK>
 __global__ __launch_bounds__(kBT) void bwd_kernel(
@@ -119,35 +207,19 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         Ds[c * L::SS + j] = dST ? dST[sbase + (long)c * DV + col0 + j] : 0.f;
     }
 
+    // Chunk inputs are loaded one chunk ahead into registers (vector loads, all
+    // issued before any is waited on) and moved to LDS at the top of the chunk.
+    Pre<E, DK> pre;
+    if (nchunks > 0)
+        pre.load(q, k, v, g, beta, dO, S0, states, nchunks - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
     for (int ci = nchunks - 1; ci >= 0; --ci) {
         const int t0 = ci * kC;
         const int n = T - t0 < kC ? T - t0 : kC;
         __syncthreads();   // previous chunk's readers of every array are done
-        // ---- the chunk's incoming state and inputs --------------------------------
-        const float *Sin = ci == 0 ? (S0 ? S0 + sbase : nullptr)
-                                   : states + (long)(ci - 1) * nbh * DK * DV + sbase;
-        for (int e = t; e < DK * kNV; e += kBT) {
-            const int c = e / kNV, j = e % kNV;
-            Ss[c * L::SS + j] = Sin ? Sin[(long)c * DV + col0 + j] : 0.f;
-        }
-        // q, k as Qt, Kt (scaled below), g into Pm; rows r >= n are zero
-        for (int e = t; e < kC * DK; e += kBT) {
-            const int r = e / DK, c = e % DK;
-            const long off = ((tokb + t0 + r) * H + h) * DK + c;
-            const bool ok = r < n;
-            Qt[r * L::OS + c] = ok ? ldE(q + off) : 0.f;
-            Kt[r * L::OS + c] = ok ? ldE(k + off) : 0.f;
-            Pm[r * L::OS + c] = ok ? ldE(g + off) : 0.f;
-        }
-        for (int e = t; e < kC * kNV; e += kBT) {
-            const int r = e / kNV, j = e % kNV;
-            const long off = ((tokb + t0 + r) * H + h) * (long)DV + col0 + j;
-            const bool ok = r < n;
-            Xs[r * L::CS + j] = ok ? ldE(v + off) : 0.f;
-            dOs[r * L::CS + j] = ok ? ldE(dO + off) : 0.f;
-        }
-        if (t < kC)
-            bet[t] = t < n ? ldE(beta + (tokb + t0 + t) * H + h) : 0.f;
+        // ---- the chunk's incoming state and inputs (rows r >= n are zero) ---------
+        pre.store(Ss, Qt, Kt, Pm, Xs, dOs, bet, t);
+        if (ci > 0)
+            pre.load(q, k, v, g, beta, dO, S0, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
         __syncthreads();
 
         // ---- decay factors and operands (thread per key channel) ---------------
@@ -171,18 +243,18 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         __syncthreads();
 
-        // ---- B = Kt Kc^T and M = lower(Qt Kc^T) (thread per entry) --------------
-        {
-            const int r = t >> 4, i = t & 15;
-            float sb = 0.f, sq = 0.f;
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const float kc = Kc[i * L::OS + c];
-                sb += Kt[r * L::OS + c] * kc;
-                sq += Qt[r * L::OS + c] * kc;
+        // ---- B = Kt Kc^T (wave 0) and M = lower(Qt Kc^T) (wave 1) ----------------
+        const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
+        if (w < 2) {
+            const f32x4 a = mm(w == 0 ? Kt : Qt, L::OS, 1, Kc, 1, L::OS, DK, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                if (w == 0)
+                    Bm[r * L::MS + l16] = a[j];
+                else
+                    Mm[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
             }
-            Bm[r * L::MS + i] = sb;
-            Mm[r * L::MS + i] = i <= r ? sq : 0.f;
         }
         __syncthreads();
         // ---- L = (I + A)^{-1} by forward substitution (thread per column) -------
@@ -204,96 +276,66 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 Tm[r * L::MS + i] = col[r] * bet[i];
             }
         }
-        __syncthreads();
-
-        // ---- column products: thread (r, 4 columns j = jj + 16 u) ---------------
-        const int r4 = t >> 4, jj = t & 15;
+        // ---- X = V - Kt S: wave w owns value columns [16w, 16w + 16) -------------
         {
-            // X = V - Kt S
-            float a[4];
+            const f32x4 a = mm(Kt, L::OS, 1, Ss + 16 * w, L::SS, 1, DK, f32x4{0.f, 0.f, 0.f, 0.f});
+            __syncthreads();      // every wave's reads of V done before X replaces it; L, Tm ready
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                a[u] = Xs[r4 * L::CS + jj + 16 * u];
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const float kt = Kt[r4 * L::OS + c];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    a[u] -= kt * Ss[c * L::SS + jj + 16 * u];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                Xs[r4 * L::CS + jj + 16 * u] = a[u];
-        }
-        __syncthreads();
-        {
-            // U = Tm X;  dU = M^T dO + Ke D
-            float uu[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i < kC; ++i) {
-                const float tm = Tm[r4 * L::MS + i], mt = Mm[i * L::MS + r4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    uu[u] += tm * Xs[i * L::CS + jj + 16 * u];
-                    du[u] += mt * dOs[i * L::CS + jj + 16 * u];
-                }
-            }
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const float ke = Ke[r4 * L::OS + c];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    du[u] += ke * Ds[c * L::SS + jj + 16 * u];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                Us[r4 * L::CS + jj + 16 * u] = uu[u];
-                dUs[r4 * L::CS + jj + 16 * u] = du[u];
+            for (int j = 0; j < 4; ++j) {
+                float *x = Xs + (4 * g4 + j) * L::CS + 16 * w + l16;
+                *x = *x - a[j];
             }
         }
         __syncthreads();
+        // ---- U = Tm X,  dU = M^T dO + Ke D -----------------------------------------
         {
-            // dX = Tm^T dU = dV
-            float dx[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i < kC; ++i) {
-                const float tm = Tm[i * L::MS + r4];
+            const f32x4 u = mm(Tm, L::MS, 1, Xs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 du = mm(Mm, 1, L::MS, dOs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+            du = mm(Ke, L::OS, 1, Ds + 16 * w, L::SS, 1, DK, du);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    dx[u] += tm * dUs[i * L::CS + jj + 16 * u];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                dXs[r4 * L::CS + jj + 16 * u] = dx[u];
-                if (r4 < n)
-                    dv_out[((tokb + t0 + r4) * H + h) * (long)DV + col0 + jj + 16 * u] = dx[u];
+            for (int j = 0; j < 4; ++j) {
+                Us[(4 * g4 + j) * L::CS + 16 * w + l16] = u[j];
+                dUs[(4 * g4 + j) * L::CS + 16 * w + l16] = du[j];
             }
         }
-        // dM = lower(dO U^T), dTm = dU X^T over this slice's columns
+        __syncthreads();
+        // ---- dX = Tm^T dU (= dV) -----------------------------------------------------
         {
-            const int r = t >> 4, i = t & 15;
-            float sm_ = 0.f, st = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < kNV; ++j) {
-                sm_ += dOs[r * L::CS + j] * Us[i * L::CS + j];
-                st += dUs[r * L::CS + j] * Xs[i * L::CS + j];
+            const f32x4 dx = mm(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                dXs[r * L::CS + 16 * w + l16] = dx[j];
+                if (r < n)
+                    dv_out[((tokb + t0 + r) * H + h) * (long)DV + col0 + 16 * w + l16] = dx[j];
             }
-            __syncthreads();   // dX written by every thread before it is read below
-            dM[r * L::MS + i] = i <= r ? sm_ : 0.f;
-            dT[r * L::MS + i] = st;
+        }
+        // ---- dM = lower(dO U^T) (wave 0), dTm = dU X^T (wave 1) over this slice -------
+        if (w < 2) {
+            const f32x4 a = mm(w == 0 ? dOs : dUs, L::CS, 1, w == 0 ? Us : Xs, 1, L::CS, kNV,
+                               f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                if (w == 0)
+                    dM[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
+                else
+                    dT[r * L::MS + l16] = a[j];
+            }
         }
         __syncthreads();
         // dbeta (direct part) and W = dL L^T with dL = dTm Diag(beta), in place of dTm
         {
             const int r = t >> 4, i = t & 15;
-            float w = 0.f;
+            float wv = 0.f;
             for (int j = 0; j < kC; ++j)
-                w += dT[r * L::MS + j] * bet[j] * Lm[i * L::MS + j];
+                wv += dT[r * L::MS + j] * bet[j] * Lm[i * L::MS + j];
             float dbd = 0.f;
             if (t < kC)
                 for (int rr2 = 0; rr2 < kC; ++rr2)
                     dbd += Lm[rr2 * L::MS + t] * dT[rr2 * L::MS + t];
             __syncthreads();
-            dT[r * L::MS + i] = w;
+            dT[r * L::MS + i] = wv;
             if (t < kC)
                 Gd[t] = dbd;          // temporary: direct dbeta (Gd is filled later)
         }
@@ -321,45 +363,46 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         __syncthreads();
 
-        // ---- parameter gradients: thread (r, channels c = cc + 16 u) ----------------
+        // ---- parameter gradients: wave w owns key-channel tiles ct = w, w + 4 -------
         {
-            const int r = t >> 4, cc = t & 15;
-            const long row = (tokb + t0 + r) * H + h;
             const long so = (long)slice * ((long)nbh / H * T * H) * DK;
 #pragma unroll 1
-            for (int u = 0; u < DK / 16; ++u) {
-                const int c = cc + 16 * u;
-                float qt = 0.f, ke = 0.f, ktt = 0.f, kcc = 0.f;
-#pragma unroll 8
-                for (int j = 0; j < kNV; ++j) {
-                    const float s = Ss[c * L::SS + j];
-                    qt += dOs[r * L::CS + j] * s;
-                    ktt -= dXs[r * L::CS + j] * s;
-                    ke += Us[r * L::CS + j] * Ds[c * L::SS + j];
+            for (int ct = w; ct < DK / 16; ct += 4) {
+                const int c = 16 * ct + l16;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
+                f32x4 aq = mm(dOs, L::CS, 1, Ss + 16 * ct * L::SS, 1, L::SS, kNV, z);
+                aq = mm(dM, L::MS, 1, Kc + 16 * ct, L::OS, 1, kC, aq);
+                const f32x4 ae = mm(Us, L::CS, 1, Ds + 16 * ct * L::SS, 1, L::SS, kNV, z);
+                const f32x4 ax = mm(dXs, L::CS, 1, Ss + 16 * ct * L::SS, 1, L::SS, kNV, z);
+                const f32x4 ab = mm(dB, L::MS, 1, Kc + 16 * ct, L::OS, 1, kC, z);
+                f32x4 ac = mm(dM, 1, L::MS, Qt + 16 * ct, L::OS, 1, kC, z);
+                ac = mm(dB, 1, L::MS, Kt + 16 * ct, L::OS, 1, kC, ac);
+                const float gm = Gam[c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * g4 + j;
+                    const float qt = aq[j], ke = ae[j], ktt = ab[j] - ax[j], kcc = ac[j];
+                    const float p = Pm[r * L::OS + c], ip = 1.0f / p;
+                    const float keke = ke * Ke[r * L::OS + c];
+                    if (r < n) {
+                        const long row = (tokb + t0 + r) * H + h;
+                        pq[so + row * DK + c] = qt * p;
+                        pk[so + row * DK + c] = ktt * p + kcc * ip + ke * (gm * ip);
+                    }
+                    T1[r * L::OS + c] = ktt * Kt[r * L::OS + c] + qt * Qt[r * L::OS + c] -
+                                        kcc * Kc[r * L::OS + c] - keke;
+                    T2[r * L::OS + c] = keke;
                 }
-                for (int i = 0; i < kC; ++i) {
-                    const float kci = Kc[i * L::OS + c];
-                    qt += dM[r * L::MS + i] * kci;
-                    ktt += dB[r * L::MS + i] * kci;
-                    kcc += dM[i * L::MS + r] * Qt[i * L::OS + c] + dB[i * L::MS + r] * Kt[i * L::OS + c];
-                }
-                const float p = Pm[r * L::OS + c], ip = 1.0f / p, gm = Gam[c];
-                const float keke = ke * Ke[r * L::OS + c];
-                if (r < n) {
-                    pq[so + row * DK + c] = qt * p;
-                    pk[so + row * DK + c] = ktt * p + kcc * ip + ke * (gm * ip);
-                }
-                T1[r * L::OS + c] = ktt * Kt[r * L::OS + c] + qt * Qt[r * L::OS + c] - kcc * Kc[r * L::OS + c] - keke;
-                T2[r * L::OS + c] = keke;
             }
         }
         // rowsum(D (.) S) per key channel
         if (t < DK) {
-            float s = 0.f;
+            float sacc = 0.f;
 #pragma unroll 8
             for (int j = 0; j < kNV; ++j)
-                s += Ds[t * L::SS + j] * Ss[t * L::SS + j];
-            Gd[t] = s;
+                sacc += Ds[t * L::SS + j] * Ss[t * L::SS + j];
+            Gd[t] = sacc;
         }
         __syncthreads();
         // dg: the last token's extra terms, then a reverse cumulative sum
@@ -375,47 +418,23 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 pg[so + ((tokb + t0 + r) * H + h) * DK + c] = acc;
             }
         }
+        // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: wave w owns tiles w + 4 m ----------
+        // (rowsum above read D; every tile below is read and rewritten by one wave)
         __syncthreads();
-
-        // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: thread owns 4 rows x 8 columns ----
-        // 32 row blocks of 4 x 8 column blocks of 8 cover 128 rows x 64 columns
-        // (with dk = 64 the upper half of the row blocks has no rows)
-        {
-            const int cb = t >> 3, jb = t & 7;
-            const int c0 = 4 * cb;
-            if (c0 < DK) {
-                float acc[4][8];
+#pragma unroll 1
+        for (int tau = w; tau < (DK / 16) * (kNV / 16); tau += 4) {
+            const int ct = tau / (kNV / 16), jt = tau % (kNV / 16);
+            f32x4 a;
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        acc[a][j] = Gam[c0 + a] * Ds[(c0 + a) * L::SS + 8 * jb + j];
-#pragma unroll 2
-                for (int r = 0; r < kC; ++r) {
-                    float qa[4], ka[4], dov[8], dxv[8];
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        qa[a] = Qt[r * L::OS + c0 + a];
-                        ka[a] = Kt[r * L::OS + c0 + a];
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        dov[j] = dOs[r * L::CS + 8 * jb + j];
-                        dxv[j] = dXs[r * L::CS + 8 * jb + j];
-                    }
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            acc[a][j] += qa[a] * dov[j] - ka[a] * dxv[j];
-                }
-                // every thread reads D only for its own block: write in place
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        Ds[(c0 + a) * L::SS + 8 * jb + j] = acc[a][j];
+            for (int j = 0; j < 4; ++j) {
+                const int c = 16 * ct + 4 * g4 + j;
+                a[j] = Gam[c] * Ds[c * L::SS + 16 * jt + l16];
             }
+            a = mm(Qt + 16 * ct, 1, L::OS, dOs + 16 * jt, L::CS, 1, kC, a);
+            const f32x4 bq = mm(Kt + 16 * ct, 1, L::OS, dXs + 16 * jt, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Ds[(16 * ct + 4 * g4 + j) * L::SS + 16 * jt + l16] = a[j] - bq[j];
         }
     }
     __syncthreads();
