@@ -386,7 +386,11 @@ def main():
             "gbps": b_by / (b_kern * 1e-3) / 1e9,
             "hbm_frac": b_by / (b_kern * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "roofline": {"bound": "mfma", "achieved": b_tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": b_tf / FP32_PEAK_TFLOPS, "traffic": None, "flops_per_launch": b_fl,
+                         "frac": b_tf / FP32_PEAK_TFLOPS,
+                         "traffic": measured_traffic("bwd_b4h32_hbm_counters.txt",
+                                                     ["kda_bwd.hip", "kda_prefill_ws.hip", "kda_device.h"])
+                         if (bs.B, bs.H, bs.T) == (4, 32, 4096) else None,
+                         "flops_per_launch": b_fl,
                          "bytes_per_launch": b_by},
         }
         del xb, gb, ws
