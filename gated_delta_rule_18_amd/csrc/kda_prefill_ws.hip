@@ -36,8 +36,8 @@
 //                      registers (running products of exp(g); Kc = k / P through
 //                      the hardware reciprocal), and only then claims one of NS
 //                      LDS slots, writes the consumers' operand images, issues
-//                      the loads of its next chunk, forms A and M on MFMA and
-//                      the UT inverse on fp32 MFMA, and publishes the slot.
+//                      the loads of its next chunk, forms A, M and the UT
+//                      inverse on MFMA, and publishes the slot.
 //                      Claiming the slot late keeps it held for the MFMA part
 //                      only, so more chunks are in flight at once.
 // Producers and consumers hand slots over through per-slot LDS flags ("ready"
@@ -697,21 +697,20 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         // ---- T = (I + A)^{-1} Diag(beta), A[r][i] = beta_r <Kt_r, Kc_i> (i < r) ----
         // A is strictly lower triangular, so A^16 = 0 and, exactly,
         //   (I + A)^{-1} = sum_k (-A)^k = (I - A)(I + A^2)(I + A^4)(I + A^8).
-        // Evaluated on fp32 MFMA with every 16 x 16 matrix in the accumulator
-        // layout (lane (n, g) holds rows 4g .. 4g+3 of column n).  mul(Xt, Y)
-        // forms X Y from X^T and Y in that layout: the contraction index of step
-        // s in lane group g is 4g + s, which is element s of both operands; so
-        // (XY)^T = mul(Y, X^T) comes from the same registers.  The consumers take
+        // Evaluated on MFMA with every 16 x 16 matrix in the accumulator layout
+        // (lane (n, g) holds rows 4g .. 4g+3 of column n).  mul(Xt, Y) forms X Y
+        // from X^T and Y in that layout: lane (n, g)'s four elements are the
+        // contraction indices 4g .. 4g+3 of both operands; so (XY)^T = mul(Y, X^T)
+        // comes from the same registers.  Each product is one 16-deep MFMA in
+        // the element type: the operands are rounded to bf16 in bf16 mode (the
+        // result is rounded to bf16 for the consumers anyway, and the powers of
+        // A only refine it), accumulation is fp32.  The consumers take
         // T as an MFMA A operand, whose image is T^T in the accumulator layout:
         //   T^T = Diag(beta) (I - A^T)(I + A2^T)(I + A4^T)(I + A8^T),
         // built from A and A^T (both straight from the bf16 products above).
         {
             auto mul = [](f32x4 xt, f32x4 y) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[st], y[st], acc, 0, 0, 0);
-                return acc;
+                return mma16(cvt4<E>(xt), cvt4<E>(y), f32x4{0.f, 0.f, 0.f, 0.f});
             };
             // beta of token l16 (row l16 of A^T's columns) and of tokens 4g + j
             // (this lane's rows), the latter fetched from lanes 4g + j
