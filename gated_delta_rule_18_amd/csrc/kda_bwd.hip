@@ -27,9 +27,12 @@
 //
 // Work decomposition: one workgroup of 256 threads per (sequence, head,
 // 64-wide value slice) walks the chunks from last to first.  The slice's part
-// of D lives in LDS for the whole walk, the slice's part of S is loaded per
-// chunk; the products are fp32 MFMAs (16 x 16 x 4) reading both operands from
-// LDS through strides, so transposed operands cost nothing extra.  dV and dS0 are per value
+// of D lives in LDS for the whole walk, the slice's part of S and the chunk's
+// inputs are loaded one chunk ahead into registers; the products are fp32
+// MFMAs (16 x 16 x 4) reading both operands from LDS through strides, so
+// transposed operands cost nothing extra, with long contractions split over
+// independent accumulators.  L comes from the same product form of the
+// nilpotent inverse as in the forward kernel.  dV and dS0 are per value
 // column and written directly.  dq, dk, dg and dbeta are sums over all value
 // columns, and every expression above after the column contractions (dM, dTm,
 // dQt, dKe, dKt and rowsum(D S)) is linear in them, so each slice computes the
@@ -97,17 +100,80 @@ __device__ __forceinline__ f32x4 mm(const float *pa, int sai, int sak, const flo
     return acc;
 }
 
+// The same product with the contraction split over NCH independent accumulators
+// (round robin over the 4-deep steps), fully unrolled, summed at the end: the
+// MFMAs of different accumulators do not wait for each other, so the chain
+// latency and the operand loads overlap.
+template <int K, int NCH>
+__device__ __forceinline__ f32x4 mmk(const float *pa, int sai, int sak, const float *pb, int sbk, int sbn, f32x4 acc)
+{
+    const int lane = threadIdx.x & 63, i = lane & 15, kk = lane >> 4;
+    const float *a = pa + i * sai + kk * sak, *b = pb + kk * sbk + i * sbn;
+    f32x4 part[NCH];
+    part[0] = acc;
+#pragma unroll
+    for (int c = 1; c < NCH; ++c)
+        part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s)
+        part[s % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * s * sak], b[4 * s * sbk], part[s % NCH], 0, 0, 0);
+#pragma unroll
+    for (int c = 1; c < NCH; ++c)
+        part[0] += part[c];
+    return part[0];
+}
+
 
 // Loads of one chunk's inputs for the reverse walk, held in registers: the
 // slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
 // consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
 // of token t / 16), v and dO (4 elements of token t / 16) and beta.
+// Raw element bits, converted to float only when the chunk is stored to LDS:
+// a conversion right after each load would make the wavefront wait for that
+// load (and every older one) on the spot.
+template <typename E, int N> struct Raw;
+template <int N> struct Raw<__bf16, N> {          // N bf16 = N / 2 dwords
+    typedef unsigned T __attribute__((ext_vector_type(N / 2)));
+    T x;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff)
+    {
+        if constexpr (N == 8)
+            x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        else
+            x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    }
+    __device__ __forceinline__ float get(int e) const
+    {
+        const unsigned w = x[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <int N> struct Raw<float, N> {           // N floats, N / 4 16-byte loads
+    typedef unsigned T __attribute__((ext_vector_type(4)));
+    T x[N / 4];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff)
+    {
+#pragma unroll
+        for (int u = 0; u < N / 4; ++u)
+            x[u] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * u, 0, 0);
+    }
+    __device__ __forceinline__ float get(int e) const { return __uint_as_float(x[e >> 2][e & 3]); }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_buffer(const void *base, long bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes > 0 ? (int)bytes : 0, 0x00020000);
+}
+
 template <typename E, int DK>
 struct Pre {
     static constexpr int FPT = DK / 4, TPR = kNV / FPT;      // state floats per thread, threads per row
     static constexpr int EPT = DK / 16;                       // q/k/g elements per thread
+    static constexpr int ES = (int)sizeof(E);
     f32x4 s[FPT / 4];
-    float qv[EPT], kv[EPT], gv[EPT], vv[4], ov[4], bv;
+    Raw<E, EPT> qv, kv, gv;
+    Raw<E, 4> vv, ov;
+    unsigned bv;
 
     __device__ __forceinline__ void load(const E *q, const E *k, const E *v, const E *g, const E *beta,
                                          const E *dO, const float *S0, const float *states, int ci, int T,
@@ -117,26 +183,29 @@ struct Pre {
         const float *Sin = ci == 0 ? (S0 ? S0 + (long)bh * DK * DV : nullptr)
                                    : states + ((long)(ci - 1) * nbh + bh) * DK * DV;
         const int c = t / TPR, j0 = (t % TPR) * FPT;
+        const __amdgpu_buffer_rsrc_t rs = bwd_buffer(Sin, Sin ? (long)DK * DV * 4 : 0);
 #pragma unroll
         for (int u = 0; u < FPT / 4; ++u)
-            s[u] = Sin ? *reinterpret_cast<const f32x4 *>(Sin + (long)c * DV + col0 + j0 + 4 * u)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+            s[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, (c * DV + col0 + j0 + 4 * u) * 4, 0, 0));
+        // buffers over the chunk's n token rows of this head: rows past n read 0
         const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
-        const bool ok = r < n;
-        const long off = ((tokb + t0 + r) * H + h) * DK + cc;
-        const long offv = ((tokb + t0 + r) * H + h) * (long)DV + col0 + jj;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            qv[e] = ok ? to_f(q[off + e]) : 0.f;
-            kv[e] = ok ? to_f(k[off + e]) : 0.f;
-            gv[e] = ok ? to_f(g[off + e]) : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vv[e] = ok ? to_f(v[offv + e]) : 0.f;
-            ov[e] = ok ? to_f(dO[offv + e]) : 0.f;
-        }
-        bv = (t < kC && t < n) ? to_f(beta[(tokb + t0 + t) * H + h]) : 0.f;
+        const long row0 = (tokb + t0) * H + h;
+        const long rsk = (long)H * DK * ES, rsv = (long)H * DV * ES;
+        const long nbk = n > 0 ? (n - 1) * rsk + DK * ES : 0, nbv = n > 0 ? (n - 1) * rsv + kNV * ES : 0;
+        const int ok = (int)(r * rsk + cc * ES), ov_ = (int)(r * rsv + jj * ES);
+        qv.load(bwd_buffer(q + row0 * DK, nbk), ok);
+        kv.load(bwd_buffer(k + row0 * DK, nbk), ok);
+        gv.load(bwd_buffer(g + row0 * DK, nbk), ok);
+        vv.load(bwd_buffer(v + row0 * DV + col0, nbv), ov_);
+        this->ov.load(bwd_buffer(dO + row0 * DV + col0, nbv), ov_);
+        const long nbb = n > 0 ? (n - 1) * (long)H * ES + ES : 0;
+        const __amdgpu_buffer_rsrc_t rb = bwd_buffer(beta + row0, nbb);
+        const int bo = (t < kC ? t : 0) * H * ES;
+        if constexpr (sizeof(E) == 2)
+            bv = (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rb, bo, 0, 0);
+        else
+            bv = __builtin_amdgcn_raw_buffer_load_b32(rb, bo, 0, 0);
     }
 
     template <typename LL>
@@ -152,17 +221,17 @@ struct Pre {
         const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            Qt[r * LL::OS + cc + e] = qv[e];
-            Kt[r * LL::OS + cc + e] = kv[e];
-            Pm[r * LL::OS + cc + e] = gv[e];
+            Qt[r * LL::OS + cc + e] = qv.get(e);
+            Kt[r * LL::OS + cc + e] = kv.get(e);
+            Pm[r * LL::OS + cc + e] = gv.get(e);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            Xs[r * LL::CS + jj + e] = vv[e];
-            dOs[r * LL::CS + jj + e] = ov[e];
+            Xs[r * LL::CS + jj + e] = vv.get(e);
+            dOs[r * LL::CS + jj + e] = ov.get(e);
         }
         if (t < kC)
-            bet[t] = bv;
+            bet[t] = __uint_as_float(sizeof(E) == 2 ? bv << 16 : bv);
     }
     __device__ __forceinline__ void store(float *Ss, float *Qt, float *Kt, float *Pm, float *Xs, float *dOs,
                                           float *bet, int t) const
@@ -234,7 +303,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
             Gam[c] = gm;
             for (int r = 0; r < kC; ++r) {
                 const float p = Pm[r * L::OS + c], kk = Kt[r * L::OS + c], qq = Qt[r * L::OS + c];
-                const float ip = 1.0f / p;
+                const float ip = __builtin_amdgcn_rcpf(p);
                 Kt[r * L::OS + c] = kk * p;
                 Qt[r * L::OS + c] = qq * p;
                 Kc[r * L::OS + c] = kk * ip;
@@ -243,10 +312,20 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         __syncthreads();
 
-        // ---- B = Kt Kc^T (wave 0) and M = lower(Qt Kc^T) (wave 1) ----------------
+        // ---- B = Kt Kc^T and then L = (I + A)^{-1} (wave 0), M = lower(Qt Kc^T)
+        //      (wave 1), X = V - Kt S (value tile t, 16 columns, by wave 1, 2, 3, 2 for
+        //      t = 1, 2, 3, 0): X needs neither B nor L, so it fills the other waves
         const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
+        auto x_tile = [&](int tile) {
+            const f32x4 a = mmk<DK, 4>(Kt, L::OS, 1, Ss + 16 * tile, L::SS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float *x = Xs + (4 * g4 + j) * L::CS + 16 * tile + l16;
+                *x = *x - a[j];
+            }
+        };
         if (w < 2) {
-            const f32x4 a = mm(w == 0 ? Kt : Qt, L::OS, 1, Kc, 1, L::OS, DK, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 a = mmk<DK, 4>(w == 0 ? Kt : Qt, L::OS, 1, Kc, 1, L::OS, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
@@ -256,42 +335,53 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                     Mm[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
             }
         }
-        __syncthreads();
-        // ---- L = (I + A)^{-1} by forward substitution (thread per column) -------
-        if (t < kC) {
-            const int i = t;
-            float col[kC];
+        if (w == 0) {
+            // L = (I + A)^{-1}, A = strict_lower(Diag(beta) B) nilpotent, exactly
+            // (I - A)(I + A^2)(I + A^4)(I + A^8), on fp32 MFMA with every matrix in
+            // the accumulator layout (lane (n, g) holds rows 4g .. 4g+3 of column n);
+            // mul(X^T, Y) = X Y (element s of lane group g is contraction index 4g + s
+            // of both operands).  B^T comes back from the B just written by this
+            // wave (its LDS accesses are performed in order).
+            auto mul = [](f32x4 xt, f32x4 y) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                float x = r == i ? 1.f : 0.f;
-                const float br = bet[r];
-#pragma unroll
-                for (int j = 0; j < r; ++j)
-                    x -= br * Bm[r * L::MS + j] * col[j];
-                col[r] = x;
-            }
-#pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                Lm[r * L::MS + i] = col[r];
-                Tm[r * L::MS + i] = col[r] * bet[i];
-            }
-        }
-        // ---- X = V - Kt S: wave w owns value columns [16w, 16w + 16) -------------
-        {
-            const f32x4 a = mm(Kt, L::OS, 1, Ss + 16 * w, L::SS, 1, DK, f32x4{0.f, 0.f, 0.f, 0.f});
-            __syncthreads();      // every wave's reads of V done before X replaces it; L, Tm ready
+                for (int st = 0; st < 4; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[st], y[st], acc, 0, 0, 0);
+                return acc;
+            };
+            const float bl = bet[l16];
+            f32x4 A, AT, I4, br;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float *x = Xs + (4 * g4 + j) * L::CS + 16 * w + l16;
-                *x = *x - a[j];
+                const int r = 4 * g4 + j;
+                br[j] = bet[r];
+                I4[j] = r == l16 ? 1.f : 0.f;
+                A[j] = r > l16 ? br[j] * Bm[r * L::MS + l16] : 0.f;        // A[r][l16]
+                AT[j] = r < l16 ? bl * Bm[l16 * L::MS + r] : 0.f;          // A[l16][r]
             }
+            const f32x4 A2 = mul(AT, A), A2T = mul(A, AT);
+            const f32x4 A4 = mul(A2T, A2), A4T = mul(A2, A2T);
+            const f32x4 A8T = mul(A4, A4T);
+            const f32x4 WT = I4 + A4T + A8T + mul(A4, A8T);   // ((I + A^4)(I + A^8))^T
+            const f32x4 W2T = WT + mul(A2, WT);                // ((I + A^2) W)^T
+            const f32x4 LT = W2T - mul(A, W2T);                // ((I - A) W2)^T = L^T
+            // lane (n, g) holds L[n][4g + j]
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Lm[l16 * L::MS + 4 * g4 + j] = LT[j];
+                Tm[l16 * L::MS + 4 * g4 + j] = LT[j] * br[j];
+            }
+        } else {
+            x_tile(w);
+            if (w == 2)
+                x_tile(0);
         }
         __syncthreads();
         // ---- U = Tm X,  dU = M^T dO + Ke D -----------------------------------------
         {
-            const f32x4 u = mm(Tm, L::MS, 1, Xs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
-            f32x4 du = mm(Mm, 1, L::MS, dOs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
-            du = mm(Ke, L::OS, 1, Ds + 16 * w, L::SS, 1, DK, du);
+            const f32x4 u = mmk<kC, 2>(Tm, L::MS, 1, Xs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 du = mmk<kC, 2>(Mm, 1, L::MS, dOs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+            du = mmk<DK, 4>(Ke, L::OS, 1, Ds + 16 * w, L::SS, 1, du);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 Us[(4 * g4 + j) * L::CS + 16 * w + l16] = u[j];
@@ -301,7 +391,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         __syncthreads();
         // ---- dX = Tm^T dU (= dV) -----------------------------------------------------
         {
-            const f32x4 dx = mm(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 dx = mmk<kC, 2>(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
@@ -312,8 +402,8 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         // ---- dM = lower(dO U^T) (wave 0), dTm = dU X^T (wave 1) over this slice -------
         if (w < 2) {
-            const f32x4 a = mm(w == 0 ? dOs : dUs, L::CS, 1, w == 0 ? Us : Xs, 1, L::CS, kNV,
-                               f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 a = mmk<kNV, 4>(w == 0 ? dOs : dUs, L::CS, 1, w == 0 ? Us : Xs, 1, L::CS,
+                                        f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
@@ -371,19 +461,50 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 const int c = 16 * ct + l16;
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
-                f32x4 aq = mm(dOs, L::CS, 1, Ss + 16 * ct * L::SS, 1, L::SS, kNV, z);
-                aq = mm(dM, L::MS, 1, Kc + 16 * ct, L::OS, 1, kC, aq);
-                const f32x4 ae = mm(Us, L::CS, 1, Ds + 16 * ct * L::SS, 1, L::SS, kNV, z);
-                const f32x4 ax = mm(dXs, L::CS, 1, Ss + 16 * ct * L::SS, 1, L::SS, kNV, z);
-                const f32x4 ab = mm(dB, L::MS, 1, Kc + 16 * ct, L::OS, 1, kC, z);
-                f32x4 ac = mm(dM, 1, L::MS, Qt + 16 * ct, L::OS, 1, kC, z);
-                ac = mm(dB, 1, L::MS, Kt + 16 * ct, L::OS, 1, kC, ac);
+                f32x4 aq = z, ae = z, ax = z, aq2 = z, ae2 = z, ax2 = z;
+                {
+                    // dO S^T, U D^T, dX S^T over the slice's 64 value columns, two
+                    // accumulators each; operands in the row of token i / key channel c
+                    const float *pdo = dOs + l16 * L::CS + g4, *pu = Us + l16 * L::CS + g4;
+                    const float *pdx = dXs + l16 * L::CS + g4;
+                    const float *ps = Ss + (16 * ct + l16) * L::SS + g4, *pd = Ds + (16 * ct + l16) * L::SS + g4;
+#pragma unroll
+                    for (int st = 0; st < kNV / 4; st += 2) {
+                        const float s0 = ps[4 * st], d0 = pd[4 * st], s1 = ps[4 * st + 4], d1 = pd[4 * st + 4];
+                        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(pdo[4 * st], s0, aq, 0, 0, 0);
+                        ae = __builtin_amdgcn_mfma_f32_16x16x4f32(pu[4 * st], d0, ae, 0, 0, 0);
+                        ax = __builtin_amdgcn_mfma_f32_16x16x4f32(pdx[4 * st], s0, ax, 0, 0, 0);
+                        aq2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pdo[4 * st + 4], s1, aq2, 0, 0, 0);
+                        ae2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pu[4 * st + 4], d1, ae2, 0, 0, 0);
+                        ax2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pdx[4 * st + 4], s1, ax2, 0, 0, 0);
+                    }
+                }
+                f32x4 ab = z, ac = z, ac2 = z;
+                {
+                    // dM Kc and dB Kc (shared B), dM^T Qt + dB^T Kt, over the 16 tokens
+                    const float *pm = dM + l16 * L::MS + g4, *pb2 = dB + l16 * L::MS + g4;
+                    const float *pmt = dM + g4 * L::MS + l16, *pbt = dB + g4 * L::MS + l16;
+                    const float *pkc = Kc + g4 * L::OS + 16 * ct + l16, *pqt = Qt + g4 * L::OS + 16 * ct + l16;
+                    const float *pkt = Kt + g4 * L::OS + 16 * ct + l16;
+#pragma unroll
+                    for (int st = 0; st < kC / 4; ++st) {
+                        const float kc = pkc[4 * st * L::OS];
+                        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(pm[4 * st], kc, aq, 0, 0, 0);
+                        ab = __builtin_amdgcn_mfma_f32_16x16x4f32(pb2[4 * st], kc, ab, 0, 0, 0);
+                        ac = __builtin_amdgcn_mfma_f32_16x16x4f32(pmt[4 * st * L::MS], pqt[4 * st * L::OS], ac, 0, 0, 0);
+                        ac2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pbt[4 * st * L::MS], pkt[4 * st * L::OS], ac2, 0, 0, 0);
+                    }
+                }
+                aq += aq2;
+                ae += ae2;
+                ax += ax2;
+                ac += ac2;
                 const float gm = Gam[c];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * g4 + j;
                     const float qt = aq[j], ke = ae[j], ktt = ab[j] - ax[j], kcc = ac[j];
-                    const float p = Pm[r * L::OS + c], ip = 1.0f / p;
+                    const float p = Pm[r * L::OS + c], ip = __builtin_amdgcn_rcpf(p);
                     const float keke = ke * Ke[r * L::OS + c];
                     if (r < n) {
                         const long row = (tokb + t0 + r) * H + h;
@@ -430,8 +551,25 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 const int c = 16 * ct + 4 * g4 + j;
                 a[j] = Gam[c] * Ds[c * L::SS + 16 * jt + l16];
             }
-            a = mm(Qt + 16 * ct, 1, L::OS, dOs + 16 * jt, L::CS, 1, kC, a);
-            const f32x4 bq = mm(Kt + 16 * ct, 1, L::OS, dXs + 16 * jt, L::CS, 1, kC, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 bq = {0.f, 0.f, 0.f, 0.f};
+            {
+                // every operand of the tile's 8 MFMAs loaded first, then the products
+                const float *pq2 = Qt + g4 * L::OS + 16 * ct + l16, *pk2 = Kt + g4 * L::OS + 16 * ct + l16;
+                const float *po = dOs + g4 * L::CS + 16 * jt + l16, *px = dXs + g4 * L::CS + 16 * jt + l16;
+                float vq[kC / 4], vo[kC / 4], vk[kC / 4], vx[kC / 4];
+#pragma unroll
+                for (int st = 0; st < kC / 4; ++st) {
+                    vq[st] = pq2[4 * st * L::OS];
+                    vo[st] = po[4 * st * L::CS];
+                    vk[st] = pk2[4 * st * L::OS];
+                    vx[st] = px[4 * st * L::CS];
+                }
+#pragma unroll
+                for (int st = 0; st < kC / 4; ++st) {
+                    a = __builtin_amdgcn_mfma_f32_16x16x4f32(vq[st], vo[st], a, 0, 0, 0);
+                    bq = __builtin_amdgcn_mfma_f32_16x16x4f32(vk[st], vx[st], bq, 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 Ds[(16 * ct + 4 * g4 + j) * L::SS + 16 * jt + l16] = a[j] - bq[j];
