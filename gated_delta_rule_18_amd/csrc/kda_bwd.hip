@@ -29,16 +29,16 @@
 // 64-wide value slice) walks the chunks from last to first.  The slice's part
 // of D lives in LDS for the whole walk, the slice's part of S and the chunk's
 // inputs are loaded one chunk ahead into registers; the products are fp32
-// MFMAs (16 x 16 x 4) reading both operands from LDS through strides, so
-// transposed operands cost nothing extra, with long contractions split over
-// independent accumulators.  L comes from the same product form of the
-// nilpotent inverse as in the forward kernel.  dV and dS0 are per value
-// column and written directly.  dq, dk, dg and dbeta are sums over all value
-// columns, and every expression above after the column contractions (dM, dTm,
-// dQt, dKe, dKt and rowsum(D S)) is linear in them, so each slice computes the
-// whole chain on its own columns and writes a partial; a second kernel adds
-// the slices' partials in slice order (no atomics: the result is
-// deterministic).
+// MFMAs (16 x 16 x 4) reading both operands from LDS, with 16-byte reads where
+// both run along the contraction index and strided reads (transposes for free)
+// elsewhere, long contractions split over independent accumulators.  L comes
+// from the same product form of the nilpotent inverse as in the forward kernel.
+// dV and dS0 are per value column and written directly.  dq, dk, dg and dbeta
+// are sums over all value columns, and every expression above after the column
+// contractions (dM, dTm, dQt, dKe, dKt and rowsum(D S)) is linear in them, so
+// each slice computes the whole chain on its own columns and writes a partial;
+// a second kernel adds the slices' partials in slice order (no atomics: the
+// result is deterministic).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -52,9 +52,12 @@ constexpr int kXCDs = 8;
 
 template <int DK>
 struct BwdL {
-    static constexpr int SS = kNV + 1;          // row stride of S and D  [DK][SS]
-    static constexpr int OS = DK + 1;           // row stride of [16][DK] operand arrays
-    static constexpr int CS = kNV + 1;          // row stride of [16][NV] column arrays
+    // row strides: multiples of 4 floats (16-byte rows for vector access) that
+    // are 4 mod 64, so 16 lanes reading 16 bytes each from 16 consecutive rows
+    // touch all 64 banks once
+    static constexpr int SS = kNV + 4;          // row stride of S and D  [DK][SS]
+    static constexpr int OS = DK + 4;           // row stride of [16][DK] operand arrays
+    static constexpr int CS = kNV + 4;          // row stride of [16][NV] column arrays
     static constexpr int MS = kC + 1;           // row stride of [16][16] matrices
     static constexpr int oS = 0;
     static constexpr int oD = oS + DK * SS;
@@ -87,23 +90,11 @@ struct BwdL {
 // acc (a 16 x 16 tile in the MFMA accumulator layout: lane (n, g) holds rows
 // 4g .. 4g+3 of column n) += sum_{k < K} A[i][k] B[k][n], with both operands read
 // from LDS through strides: A[i][k] = pa[i * sai + k * sak], B[k][n] =
-// pb[k * sbk + n * sbn].  fp32 MFMA, 4 contraction steps per instruction; K is a
-// multiple of 4.
-__device__ __forceinline__ f32x4 mm(const float *pa, int sai, int sak, const float *pb, int sbk, int sbn, int K,
-                                    f32x4 acc)
-{
-    const int lane = threadIdx.x & 63, i = lane & 15, kk = lane >> 4;
-    const float *a = pa + i * sai + kk * sak, *b = pb + kk * sbk + i * sbn;
-#pragma unroll 4
-    for (int s = 0; s < K; s += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s * sak], b[s * sbk], acc, 0, 0, 0);
-    return acc;
-}
-
-// The same product with the contraction split over NCH independent accumulators
-// (round robin over the 4-deep steps), fully unrolled, summed at the end: the
-// MFMAs of different accumulators do not wait for each other, so the chain
-// latency and the operand loads overlap.
+// pb[k * sbk + n * sbn] (a transposed operand is just other strides).  fp32
+// MFMA, 4 contraction steps per instruction, the steps spread round robin over
+// NCH independent accumulators summed at the end: MFMAs of different
+// accumulators do not wait for each other, so chain latency and operand loads
+// overlap.
 template <int K, int NCH>
 __device__ __forceinline__ f32x4 mmk(const float *pa, int sai, int sak, const float *pb, int sbk, int sbn, f32x4 acc)
 {
@@ -123,11 +114,34 @@ __device__ __forceinline__ f32x4 mmk(const float *pa, int sai, int sak, const fl
     return part[0];
 }
 
+// The same product with both operands contiguous along the contraction index:
+// A[i][k] = pa[i * sa + k], B[k][n] = pb[n * sb + k], rows 16-byte aligned.  Lane
+// group g takes the contraction indices [g K / 4, (g + 1) K / 4) four at a time
+// (one 16-byte read per operand feeds four MFMAs), spread over NCH accumulators.
+template <int K, int NCH>
+__device__ __forceinline__ f32x4 mmv(const float *pa, int sa, const float *pb, int sb, f32x4 acc)
+{
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+    const float *a = pa + i * sa + g * (K / 4), *b = pb + i * sb + g * (K / 4);
+    f32x4 part[NCH];
+    part[0] = acc;
+#pragma unroll
+    for (int c = 1; c < NCH; ++c)
+        part[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < K / 16; ++q) {
+        const f32x4 av = *reinterpret_cast<const f32x4 *>(a + 4 * q);
+        const f32x4 bv = *reinterpret_cast<const f32x4 *>(b + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            part[(4 * q + e) % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], part[(4 * q + e) % NCH], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 1; c < NCH; ++c)
+        part[0] += part[c];
+    return part[0];
+}
 
-// Loads of one chunk's inputs for the reverse walk, held in registers: the
-// slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
-// consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
-// of token t / 16), v and dO (4 elements of token t / 16) and beta.
 // Raw element bits, converted to float only when the chunk is stored to LDS:
 // a conversion right after each load would make the wavefront wait for that
 // load (and every older one) on the spot.
@@ -165,6 +179,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_buffer(const void *base, l
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes > 0 ? (int)bytes : 0, 0x00020000);
 }
 
+// Loads of one chunk's inputs for the reverse walk, held in registers: the
+// slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
+// consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
+// of token t / 16), v and dO (4 elements of token t / 16) and beta.
 template <typename E, int DK>
 struct Pre {
     static constexpr int FPT = DK / 4, TPR = kNV / FPT;      // state floats per thread, threads per row
@@ -215,21 +233,23 @@ struct Pre {
         const int c = t / TPR, j0 = (t % TPR) * FPT;
 #pragma unroll
         for (int u = 0; u < FPT / 4; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                Ss[c * LL::SS + j0 + 4 * u + e] = s[u][e];
+            *reinterpret_cast<f32x4 *>(Ss + c * LL::SS + j0 + 4 * u) = s[u];
         const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            Qt[r * LL::OS + cc + e] = qv.get(e);
-            Kt[r * LL::OS + cc + e] = kv.get(e);
-            Pm[r * LL::OS + cc + e] = gv.get(e);
-        }
+        for (int u = 0; u < EPT / 4; ++u) {
+            f32x4 a, b2, c2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            Xs[r * LL::CS + jj + e] = vv.get(e);
-            dOs[r * LL::CS + jj + e] = ov.get(e);
+            for (int e = 0; e < 4; ++e) {
+                a[e] = qv.get(4 * u + e);
+                b2[e] = kv.get(4 * u + e);
+                c2[e] = gv.get(4 * u + e);
+            }
+            *reinterpret_cast<f32x4 *>(Qt + r * LL::OS + cc + 4 * u) = a;
+            *reinterpret_cast<f32x4 *>(Kt + r * LL::OS + cc + 4 * u) = b2;
+            *reinterpret_cast<f32x4 *>(Pm + r * LL::OS + cc + 4 * u) = c2;
         }
+        *reinterpret_cast<f32x4 *>(Xs + r * LL::CS + jj) = f32x4{vv.get(0), vv.get(1), vv.get(2), vv.get(3)};
+        *reinterpret_cast<f32x4 *>(dOs + r * LL::CS + jj) = f32x4{ov.get(0), ov.get(1), ov.get(2), ov.get(3)};
         if (t < kC)
             bet[t] = __uint_as_float(sizeof(E) == 2 ? bv << 16 : bv);
     }
@@ -291,26 +311,44 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
             pre.load(q, k, v, g, beta, dO, S0, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
         __syncthreads();
 
-        // ---- decay factors and operands (thread per key channel) ---------------
-        if (t < DK) {
-            const int c = t;
-            float G = 0.f;
+        // ---- decay factors and operands: thread (c, part) owns key channel c for
+        //      the part's kC / NPT tokens; every thread sums the whole chunk's g of
+        //      its channel (g is 0 past the last token) for the offset and for Gam.
+        //      P goes to Pm after the barrier, once no thread reads g any more ------
+        constexpr int NPT = kBT / DK, TPP = kC / NPT;
+        const int pc = t % DK, pr0 = (t / DK) * TPP;
+        float pv[TPP];
+        {
+            float gl[kC];
+#pragma unroll
+            for (int r = 0; r < kC; ++r)
+                gl[r] = Pm[r * L::OS + pc];
+            float G = 0.f, Gt = 0.f;
+#pragma unroll
             for (int r = 0; r < kC; ++r) {
-                G += Pm[r * L::OS + c];                   // g (0 past the last token)
-                Pm[r * L::OS + c] = exp_f(G);
+                G += r < pr0 ? gl[r] : 0.f;
+                Gt += gl[r];
             }
-            const float gm = Pm[(n - 1) * L::OS + c];
-            Gam[c] = gm;
-            for (int r = 0; r < kC; ++r) {
-                const float p = Pm[r * L::OS + c], kk = Kt[r * L::OS + c], qq = Qt[r * L::OS + c];
-                const float ip = __builtin_amdgcn_rcpf(p);
-                Kt[r * L::OS + c] = kk * p;
-                Qt[r * L::OS + c] = qq * p;
-                Kc[r * L::OS + c] = kk * ip;
-                Ke[r * L::OS + c] = kk * (gm * ip);
+            const float gm = exp_f(Gt);
+            if (pr0 == 0)
+                Gam[pc] = gm;
+#pragma unroll
+            for (int u = 0; u < TPP; ++u) {
+                const int r = pr0 + u;
+                G += Pm[r * L::OS + pc];                  // g of token r
+                const float p = exp_f(G), ip = __builtin_amdgcn_rcpf(p);
+                const float kk = Kt[r * L::OS + pc], qq = Qt[r * L::OS + pc];
+                pv[u] = p;
+                Kt[r * L::OS + pc] = kk * p;
+                Qt[r * L::OS + pc] = qq * p;
+                Kc[r * L::OS + pc] = kk * ip;
+                Ke[r * L::OS + pc] = kk * (gm * ip);
             }
         }
         __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TPP; ++u)
+            Pm[(pr0 + u) * L::OS + pc] = pv[u];
 
         // ---- B = Kt Kc^T and then L = (I + A)^{-1} (wave 0), M = lower(Qt Kc^T)
         //      (wave 1), X = V - Kt S (value tile t, 16 columns, by wave 1, 2, 3, 2 for
@@ -325,7 +363,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
             }
         };
         if (w < 2) {
-            const f32x4 a = mmk<DK, 4>(w == 0 ? Kt : Qt, L::OS, 1, Kc, 1, L::OS, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 a = mmv<DK, 4>(w == 0 ? Kt : Qt, L::OS, Kc, L::OS, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
@@ -400,56 +438,61 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                     dv_out[((tokb + t0 + r) * H + h) * (long)DV + col0 + 16 * w + l16] = dx[j];
             }
         }
-        // ---- dM = lower(dO U^T) (wave 0), dTm = dU X^T (wave 1) over this slice -------
-        if (w < 2) {
-            const f32x4 a = mmk<kNV, 4>(w == 0 ? dOs : dUs, L::CS, 1, w == 0 ? Us : Xs, 1, L::CS,
-                                        f32x4{0.f, 0.f, 0.f, 0.f});
+        // ---- dM = lower(dO U^T) (wave 0); wave 1: dTm = dU X^T over this slice, then
+        //      W = dL L^T (dL = dTm Diag(beta)), dA = strict_lower(-L^T W), dB =
+        //      Diag(beta) dA and dbeta, back to back (a wavefront's LDS accesses are
+        //      performed in order, so no barrier separates them) ---------------------
+        if (w == 0) {
+            const f32x4 a = mmv<kNV, 4>(dOs, L::CS, Us, L::CS, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
-                if (w == 0)
-                    dM[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
-                else
-                    dT[r * L::MS + l16] = a[j];
+                dM[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
             }
-        }
-        __syncthreads();
-        // dbeta (direct part) and W = dL L^T with dL = dTm Diag(beta), in place of dTm
-        {
-            const int r = t >> 4, i = t & 15;
-            float wv = 0.f;
-            for (int j = 0; j < kC; ++j)
-                wv += dT[r * L::MS + j] * bet[j] * Lm[i * L::MS + j];
+        } else if (w == 1) {
+            const f32x4 a = mmv<kNV, 4>(dUs, L::CS, Xs, L::CS, f32x4{0.f, 0.f, 0.f, 0.f});
+            // direct dbeta_i = sum_r L[r][i] dTm[r][i]: lane (i, g) holds rows 4g + j
             float dbd = 0.f;
-            if (t < kC)
-                for (int rr2 = 0; rr2 < kC; ++rr2)
-                    dbd += Lm[rr2 * L::MS + t] * dT[rr2 * L::MS + t];
-            __syncthreads();
-            dT[r * L::MS + i] = wv;
-            if (t < kC)
-                Gd[t] = dbd;          // temporary: direct dbeta (Gd is filled later)
-        }
-        __syncthreads();
-        // dA = strict_lower(-L^T W), dB = Diag(beta) dA, dbeta += sum_{i<r} dA B
-        {
-            const int r = t >> 4, i = t & 15;
-            float a = 0.f;
-            if (i < r)
-                for (int j = 0; j < kC; ++j)
-                    a -= Lm[j * L::MS + r] * dT[j * L::MS + i];
-            dB[r * L::MS + i] = bet[r] * a;
-            float prod = a * Bm[r * L::MS + i];
-            // reduce prod over the 16 lanes i of row r (xor shuffles stay in the row)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                dT[r * L::MS + l16] = a[j] * bet[l16];        // dL
+                dbd += Lm[r * L::MS + l16] * a[j];
+            }
+            dbd += __shfl_xor(dbd, 16, 64);
+            dbd += __shfl_xor(dbd, 32, 64);
+            // W = dL L^T: A[r][k] = dL[r][k], B[k][n] = L[n][k]
+            const f32x4 wv = mmk<kC, 2>(dT, L::MS, 1, Lm, 1, L::MS, f32x4{0.f, 0.f, 0.f, 0.f});
+            float *Wm = T1;                                   // staging, free until the gradients
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                Wm[(4 * g4 + j) * L::MS + l16] = wv[j];
+            // dA = -L^T W: A[r][k] = L[k][r], B[k][n] = W[k][n]
+            const f32x4 da = mmk<kC, 2>(Lm, 1, L::MS, Wm, L::MS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                const float a2 = l16 < r ? -da[j] : 0.f;     // dA[r][l16]
+                dB[r * L::MS + l16] = bet[r] * a2;
+                pr[j] = a2 * Bm[r * L::MS + l16];
+            }
+            // sum over the 16 columns of each row (xor shuffles stay in the row group)
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1)
-                prod += __shfl_xor(prod, off, 64);
-            if (i == 0)
-                T2[r] = prod;         // temporary: dbeta from A
-        }
-        __syncthreads();
-        if (t < kC && t < n) {
-            const long bo = (long)slice * ((long)nbh / H * T * H) + (tokb + t0 + t) * H + h;
-            pb[bo] = Gd[t] + T2[t];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pr[j] += __shfl_xor(pr[j], off, 64);
+            // dbeta_r for r = 4 g + j sits in every lane of row group g; lane r of
+            // wave 1 takes dbd of column r (its own) and the A part of row r
+            const float pa = __shfl(pr[0], 16 * (lane >> 2), 64) * ((lane & 3) == 0) +
+                             __shfl(pr[1], 16 * (lane >> 2), 64) * ((lane & 3) == 1) +
+                             __shfl(pr[2], 16 * (lane >> 2), 64) * ((lane & 3) == 2) +
+                             __shfl(pr[3], 16 * (lane >> 2), 64) * ((lane & 3) == 3);
+            if (lane < kC && lane < n) {
+                const long bo = (long)slice * ((long)nbh / H * T * H) + (tokb + t0 + lane) * H + h;
+                pb[bo] = dbd + pa;
+            }
         }
         __syncthreads();
 
@@ -463,20 +506,29 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
                 f32x4 aq = z, ae = z, ax = z, aq2 = z, ae2 = z, ax2 = z;
                 {
-                    // dO S^T, U D^T, dX S^T over the slice's 64 value columns, two
-                    // accumulators each; operands in the row of token i / key channel c
-                    const float *pdo = dOs + l16 * L::CS + g4, *pu = Us + l16 * L::CS + g4;
-                    const float *pdx = dXs + l16 * L::CS + g4;
-                    const float *ps = Ss + (16 * ct + l16) * L::SS + g4, *pd = Ds + (16 * ct + l16) * L::SS + g4;
+                    // dO S^T, U D^T, dX S^T over the slice's 64 value columns: lane
+                    // group g4 takes columns [16 g4, 16 g4 + 16), 16 bytes of each
+                    // operand row per read; two accumulators per product
+                    const int k0 = 16 * g4;
+                    const float *pdo = dOs + l16 * L::CS + k0, *pu = Us + l16 * L::CS + k0;
+                    const float *pdx = dXs + l16 * L::CS + k0;
+                    const float *ps = Ss + (16 * ct + l16) * L::SS + k0, *pd = Ds + (16 * ct + l16) * L::SS + k0;
 #pragma unroll
-                    for (int st = 0; st < kNV / 4; st += 2) {
-                        const float s0 = ps[4 * st], d0 = pd[4 * st], s1 = ps[4 * st + 4], d1 = pd[4 * st + 4];
-                        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(pdo[4 * st], s0, aq, 0, 0, 0);
-                        ae = __builtin_amdgcn_mfma_f32_16x16x4f32(pu[4 * st], d0, ae, 0, 0, 0);
-                        ax = __builtin_amdgcn_mfma_f32_16x16x4f32(pdx[4 * st], s0, ax, 0, 0, 0);
-                        aq2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pdo[4 * st + 4], s1, aq2, 0, 0, 0);
-                        ae2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pu[4 * st + 4], d1, ae2, 0, 0, 0);
-                        ax2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pdx[4 * st + 4], s1, ax2, 0, 0, 0);
+                    for (int qq = 0; qq < kNV / 16; ++qq) {
+                        const f32x4 vo = *reinterpret_cast<const f32x4 *>(pdo + 4 * qq);
+                        const f32x4 vu = *reinterpret_cast<const f32x4 *>(pu + 4 * qq);
+                        const f32x4 vx = *reinterpret_cast<const f32x4 *>(pdx + 4 * qq);
+                        const f32x4 vs = *reinterpret_cast<const f32x4 *>(ps + 4 * qq);
+                        const f32x4 vd = *reinterpret_cast<const f32x4 *>(pd + 4 * qq);
+#pragma unroll
+                        for (int e = 0; e < 4; e += 2) {
+                            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(vo[e], vs[e], aq, 0, 0, 0);
+                            ae = __builtin_amdgcn_mfma_f32_16x16x4f32(vu[e], vd[e], ae, 0, 0, 0);
+                            ax = __builtin_amdgcn_mfma_f32_16x16x4f32(vx[e], vs[e], ax, 0, 0, 0);
+                            aq2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vo[e + 1], vs[e + 1], aq2, 0, 0, 0);
+                            ae2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vu[e + 1], vd[e + 1], ae2, 0, 0, 0);
+                            ax2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vx[e + 1], vs[e + 1], ax2, 0, 0, 0);
+                        }
                     }
                 }
                 f32x4 ab = z, ac = z, ac2 = z;
@@ -519,24 +571,29 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         // rowsum(D (.) S) per key channel
         if (t < DK) {
-            float sacc = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < kNV; ++j)
-                sacc += Ds[t * L::SS + j] * Ss[t * L::SS + j];
-            Gd[t] = sacc;
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kNV; j += 4)
+                sacc += *reinterpret_cast<const f32x4 *>(Ds + t * L::SS + j) *
+                        *reinterpret_cast<const f32x4 *>(Ss + t * L::SS + j);
+            Gd[t] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
         }
         __syncthreads();
-        // dg: the last token's extra terms, then a reverse cumulative sum
-        if (t < DK) {
-            const int c = t;
-            float extra = Gd[c] * Gam[c];
+        // dg: the last token's extra terms, then a reverse cumulative sum; thread
+        // (c, part) writes the part's tokens and first sums the tokens after them
+        // (rows past the last token hold zeros)
+        {
+            float acc = Gd[pc] * Gam[pc];
+#pragma unroll
             for (int r = 0; r < kC; ++r)
-                extra += T2[r * L::OS + c];
-            float acc = 0.f;
+                acc += T2[r * L::OS + pc] + (r >= pr0 + TPP ? T1[r * L::OS + pc] : 0.f);
             const long so = (long)slice * ((long)nbh / H * T * H) * DK;
-            for (int r = n - 1; r >= 0; --r) {
-                acc += T1[r * L::OS + c] + (r == n - 1 ? extra : 0.f);
-                pg[so + ((tokb + t0 + r) * H + h) * DK + c] = acc;
+#pragma unroll
+            for (int u = TPP - 1; u >= 0; --u) {
+                const int r = pr0 + u;
+                acc += T1[r * L::OS + pc];
+                if (r < n)
+                    pg[so + ((tokb + t0 + r) * H + h) * DK + pc] = acc;
             }
         }
         // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: wave w owns tiles w + 4 m ----------
