@@ -183,6 +183,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_buffer(const void *base, l
 // slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
 // consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
 // of token t / 16), v and dO (4 elements of token t / 16) and beta.
+// Buffer over the first n rows (stride bytes apart, width bytes each) of an
+// output: stores to rows n and beyond fall outside it and are dropped, so a
+// ragged last chunk needs no branch around its stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_out(float *base, int n, long stride, int width)
+{
+    return bwd_buffer(base, n > 0 ? (n - 1) * stride + width : 0);
+}
+__device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, int voff, float x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
+}
+
 template <typename E, int DK>
 struct Pre {
     static constexpr int FPT = DK / 4, TPR = kNV / FPT;      // state floats per thread, threads per row
@@ -430,12 +442,13 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         // ---- dX = Tm^T dU (= dV) -----------------------------------------------------
         {
             const f32x4 dx = mmk<kC, 2>(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
+            const __amdgpu_buffer_rsrc_t rv =
+                rows_out(dv_out + ((tokb + t0) * H + h) * (long)DV + col0, n, (long)H * DV * 4, kNV * 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g4 + j;
                 dXs[r * L::CS + 16 * w + l16] = dx[j];
-                if (r < n)
-                    dv_out[((tokb + t0 + r) * H + h) * (long)DV + col0 + 16 * w + l16] = dx[j];
+                st_out(rv, (r * H * DV + 16 * w + l16) * 4, dx[j]);
             }
         }
         // ---- dM = lower(dO U^T) (wave 0); wave 1: dTm = dU X^T over this slice, then
@@ -552,17 +565,17 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 ax += ax2;
                 ac += ac2;
                 const float gm = Gam[c];
+                const long rowb = ((tokb + t0) * H + h) * DK;
+                const __amdgpu_buffer_rsrc_t rq = rows_out(pq + so + rowb, n, (long)H * DK * 4, DK * 4);
+                const __amdgpu_buffer_rsrc_t rk = rows_out(pk + so + rowb, n, (long)H * DK * 4, DK * 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * g4 + j;
                     const float qt = aq[j], ke = ae[j], ktt = ab[j] - ax[j], kcc = ac[j];
                     const float p = Pm[r * L::OS + c], ip = __builtin_amdgcn_rcpf(p);
                     const float keke = ke * Ke[r * L::OS + c];
-                    if (r < n) {
-                        const long row = (tokb + t0 + r) * H + h;
-                        pq[so + row * DK + c] = qt * p;
-                        pk[so + row * DK + c] = ktt * p + kcc * ip + ke * (gm * ip);
-                    }
+                    st_out(rq, (r * H * DK + c) * 4, qt * p);
+                    st_out(rk, (r * H * DK + c) * 4, ktt * p + kcc * ip + ke * (gm * ip));
                     T1[r * L::OS + c] = ktt * Kt[r * L::OS + c] + qt * Qt[r * L::OS + c] -
                                         kcc * Kc[r * L::OS + c] - keke;
                     T2[r * L::OS + c] = keke;
@@ -588,48 +601,58 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
             for (int r = 0; r < kC; ++r)
                 acc += T2[r * L::OS + pc] + (r >= pr0 + TPP ? T1[r * L::OS + pc] : 0.f);
             const long so = (long)slice * ((long)nbh / H * T * H) * DK;
+            const __amdgpu_buffer_rsrc_t rg =
+                rows_out(pg + so + ((tokb + t0) * H + h) * DK, n, (long)H * DK * 4, DK * 4);
 #pragma unroll
             for (int u = TPP - 1; u >= 0; --u) {
                 const int r = pr0 + u;
                 acc += T1[r * L::OS + pc];
-                if (r < n)
-                    pg[so + ((tokb + t0 + r) * H + h) * DK + pc] = acc;
+                st_out(rg, (r * H * DK + pc) * 4, acc);
             }
         }
-        // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: wave w owns tiles w + 4 m ----------
-        // (rowsum above read D; every tile below is read and rewritten by one wave)
+        // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: wave w owns the key-channel tiles
+        //      ct = w, w + 4 over all 64 value columns, as four column-interleaved
+        //      16 x 16 tiles (tile e: columns 4 n + e, n = l16), so one 16-byte read
+        //      of a dO or dX row feeds four MFMAs and D moves 16 bytes at a time.
+        //      (rowsum above read D; every row below is read and rewritten by one wave)
         __syncthreads();
 #pragma unroll 1
-        for (int tau = w; tau < (DK / 16) * (kNV / 16); tau += 4) {
-            const int ct = tau / (kNV / 16), jt = tau % (kNV / 16);
-            f32x4 a;
+        for (int ct = w; ct < DK / 16; ct += 4) {
+            f32x4 acc[4];                                 // acc[e][jj] = D[16 ct + 4 g4 + jj][4 l16 + e]
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 16 * ct + 4 * g4 + j;
-                a[j] = Gam[c] * Ds[c * L::SS + 16 * jt + l16];
+            for (int jj = 0; jj < 4; ++jj) {
+                const int c = 16 * ct + 4 * g4 + jj;
+                const f32x4 d = *reinterpret_cast<const f32x4 *>(Ds + c * L::SS + 4 * l16);
+                const float gm = Gam[c];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e][jj] = gm * d[e];
             }
-            f32x4 bq = {0.f, 0.f, 0.f, 0.f};
-            {
-                // every operand of the tile's 8 MFMAs loaded first, then the products
-                const float *pq2 = Qt + g4 * L::OS + 16 * ct + l16, *pk2 = Kt + g4 * L::OS + 16 * ct + l16;
-                const float *po = dOs + g4 * L::CS + 16 * jt + l16, *px = dXs + g4 * L::CS + 16 * jt + l16;
-                float vq[kC / 4], vo[kC / 4], vk[kC / 4], vx[kC / 4];
+            // contraction over the tokens r = g4 + 4 st: A[i][r] = Qt[r][16 ct + i]
+            // (then -Kt), B[r][n] = dO[r][4 n + e] (then dX)
+            float aq[kC / 4], ak[kC / 4];
+            f32x4 bo[kC / 4], bx[kC / 4];
 #pragma unroll
-                for (int st = 0; st < kC / 4; ++st) {
-                    vq[st] = pq2[4 * st * L::OS];
-                    vo[st] = po[4 * st * L::CS];
-                    vk[st] = pk2[4 * st * L::OS];
-                    vx[st] = px[4 * st * L::CS];
-                }
-#pragma unroll
-                for (int st = 0; st < kC / 4; ++st) {
-                    a = __builtin_amdgcn_mfma_f32_16x16x4f32(vq[st], vo[st], a, 0, 0, 0);
-                    bq = __builtin_amdgcn_mfma_f32_16x16x4f32(vk[st], vx[st], bq, 0, 0, 0);
-                }
+            for (int st = 0; st < kC / 4; ++st) {
+                const int r = g4 + 4 * st;
+                aq[st] = Qt[r * L::OS + 16 * ct + l16];
+                ak[st] = -Kt[r * L::OS + 16 * ct + l16];
+                bo[st] = *reinterpret_cast<const f32x4 *>(dOs + r * L::CS + 4 * l16);
+                bx[st] = *reinterpret_cast<const f32x4 *>(dXs + r * L::CS + 4 * l16);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                Ds[(16 * ct + 4 * g4 + j) * L::SS + 16 * jt + l16] = a[j] - bq[j];
+            for (int st = 0; st < kC / 4; ++st) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[st], bo[st][e], acc[e], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[st], bx[st][e], acc[e], 0, 0, 0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                *reinterpret_cast<f32x4 *>(Ds + (16 * ct + 4 * g4 + jj) * L::SS + 4 * l16) =
+                    f32x4{acc[0][jj], acc[1][jj], acc[2][jj], acc[3][jj]};
         }
     }
     __syncthreads();
