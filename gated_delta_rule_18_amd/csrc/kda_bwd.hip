@@ -385,7 +385,31 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                     Mm[r * L::MS + l16] = l16 <= r ? a[j] : 0.f;
             }
         }
-        if (w == 0) {
+        if (w == 0 && sizeof(E) == 4) {
+            // fp32 test mode: L by forward substitution, lane i < 16 owning column i
+            // (the product form below loses about the size of its intermediate
+            // powers, up to C(14, 7) = 3432 for A all ones below the diagonal, in
+            // accuracy; B was written by this wave, whose LDS accesses are
+            // performed in order)
+            if (lane < kC) {
+                const int i = lane;
+                float col[kC];
+#pragma unroll
+                for (int r = 0; r < kC; ++r) {
+                    float x = r == i ? 1.f : 0.f;
+                    const float br = bet[r];
+#pragma unroll
+                    for (int j = 0; j < r; ++j)
+                        x -= br * Bm[r * L::MS + j] * col[j];
+                    col[r] = x;
+                }
+#pragma unroll
+                for (int r = 0; r < kC; ++r) {
+                    Lm[r * L::MS + i] = col[r];
+                    Tm[r * L::MS + i] = col[r] * bet[i];
+                }
+            }
+        } else if (w == 0) {
             // L = (I + A)^{-1}, A = strict_lower(Diag(beta) B) nilpotent, exactly
             // (I - A)(I + A^2)(I + A^4)(I + A^8), on fp32 MFMA with every matrix in
             // the accumulator layout (lane (n, g) holds rows 4g .. 4g+3 of column n);

@@ -154,6 +154,24 @@ def prefill_inputs(spec: PrefillSpec, device="cpu", seed=None, T=None):
                 S0=None if S0 is None else S0.contiguous())
 
 
+def identical_key_inputs(B, T, H, dk, dv, dtype="bf16", seed=77, device="cpu"):
+    """Edge of the input domain: every token of a head shares one unit key, beta = 1
+    and g = 0 (no decay); q unit, v ~ N(0,1), S0 ~ 0.02 N(0,1).  Within a chunk A is
+    then the strict lower part of all ones.  Same dict layout as prefill_inputs."""
+    dt = torch_dtype(dtype)
+    gen = _gen(device, seed)
+    key = _unit(_randn((1, 1, H, dk), gen, device))
+    k = key.expand(B, T, H, dk)
+    q = _unit(_randn((B, T, H, dk), gen, device))
+    v = _randn((B, T, H, dv), gen, device)
+    S0 = (0.02 * _randn((B, H, dk, dv), gen, device)).contiguous()
+    g = torch.zeros((B, T, H, dk), device=device)
+    beta = torch.ones((B, T, H), device=device)
+    out = {n: x.to(dt).contiguous() for n, x in dict(q=q, k=k, v=v, g=g, beta=beta).items()}
+    out["S0"] = S0
+    return out
+
+
 def decode_state(spec: DecodeSpec, device="cpu", N=None):
     """Initial decode state: conv_w fp32 [H, 2dk+dv, width] ~ 0.5 N(0,1);
     conv_cache [N, H, width-1, 2dk+dv] ~ N(0,1) in spec.dtype; S fp32 [N,H,dk,dv] ~ 0.02 N(0,1)."""

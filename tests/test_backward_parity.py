@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from gated_delta_rule_18_amd import binding
-from gated_delta_rule_18_amd.inputs import PrefillSpec, backward_inputs, prefill_inputs, to_f64
+from gated_delta_rule_18_amd.inputs import PrefillSpec, backward_inputs, identical_key_inputs, prefill_inputs, to_f64
 from oracle import backward as obwd
 from tests.util import TOL_GRAD, assert_parity
 
@@ -13,8 +13,8 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
 
 
-def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what=""):
-    x = prefill_inputs(spec, device=gpu, T=T)
+def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what="", x=None):
+    x = prefill_inputs(spec, device=gpu, T=T) if x is None else x
     gr = backward_inputs(spec, device=gpu, T=T, ds_std=ds_std)
     got = binding.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gr["dO"], gr["dS_T"])
     torch.cuda.synchronize()
@@ -45,6 +45,15 @@ def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what=""):
 def test_backward_small(gpu, dtype, dk, dv, T):
     spec = PrefillSpec(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, seed=90 + T, s0_std=0.3)
     _check(spec, gpu, what=f"{dtype} dk{dk} dv{dv} T{T}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_backward_identical_keys(gpu, dtype):
+    """Identical unit keys, beta = 1, g = 0: in every chunk A is all ones below the
+    diagonal, the hardest case for the chunk inverse (T = 40: a ragged last chunk)."""
+    spec = PrefillSpec(B=1, H=2, T=40, dk=128, dv=128, dtype=dtype, seed=99)
+    x = identical_key_inputs(1, 40, 2, 128, 128, dtype=dtype, device=gpu)
+    _check(spec, gpu, x=x, what=f"identical keys {dtype}")
 
 
 def test_backward_zero_initial_state_and_no_final_gradient(gpu):

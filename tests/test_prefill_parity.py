@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from gated_delta_rule_18_amd import binding
-from gated_delta_rule_18_amd.inputs import WORKLOADS, PrefillSpec, prefill_inputs, to_f64
+from gated_delta_rule_18_amd.inputs import WORKLOADS, PrefillSpec, identical_key_inputs, prefill_inputs, to_f64
 from tests.util import TOL, assert_parity, oracle_prefill_heads
 
 pytestmark = pytest.mark.gpu
@@ -65,6 +65,22 @@ def test_bound_stress_all_minus5(gpu, dtype):
                        gate="const", g_const=-5.0)
     for chunk in (16, 32):
         _check_full(spec, gpu, chunk, f"g=-5 {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_identical_keys_full_erase(gpu, dtype, chunk):
+    """Every token shares one unit key, beta = 1, g = 0: each write erases the last one
+    along k, and inside a chunk A is the strict lower part of all ones, whose powers in
+    the nilpotent inverse reach C(14, 7) = 3432 before cancelling to entries of +-1.
+    T = 80 leaves a ragged last chunk for chunk 32."""
+    inp = identical_key_inputs(1, 80, 2, 128, 128, dtype=dtype, device=gpu)
+    o, st = _run(inp, chunk)
+    oo, so = _full_oracle(inp)
+    to, ts = TOL[dtype]
+    eo = assert_parity(to_f64(o), oo, to, f"identical keys {dtype} chunk {chunk} o")
+    es = assert_parity(to_f64(st), so, ts, f"identical keys {dtype} chunk {chunk} S_T")
+    print(f"identical keys {dtype} chunk {chunk}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("chunk", [16, 32])
