@@ -73,11 +73,16 @@ def test_identical_keys_full_erase(gpu, dtype, chunk):
     """Every token shares one unit key, beta = 1, g = 0: each write erases the last one
     along k, and inside a chunk A is the strict lower part of all ones, whose powers in
     the nilpotent inverse reach C(14, 7) = 3432 before cancelling to entries of +-1.
-    T = 80 leaves a ragged last chunk for chunk 32."""
+    T = 80 leaves a ragged last chunk for chunk 32.  In bf16 mode the erase rides on U:
+    U_r = v_r - v_{r-1} once T is the +-1 bidiagonal inverse, each row rounded to bf16
+    (2^-9 relative), and the state update sums the chunk's 16 rows, so the state's error
+    grows like sqrt(16) 2^-9 ~ 8e-3 of its norm per chunk and o inherits it: both are held
+    to 2e-2 here (the o bar), fp32 test mode to its usual 1e-5."""
     inp = identical_key_inputs(1, 80, 2, 128, 128, dtype=dtype, device=gpu)
     o, st = _run(inp, chunk)
     oo, so = _full_oracle(inp)
     to, ts = TOL[dtype]
+    ts = max(ts, to)
     eo = assert_parity(to_f64(o), oo, to, f"identical keys {dtype} chunk {chunk} o")
     es = assert_parity(to_f64(st), so, ts, f"identical keys {dtype} chunk {chunk} S_T")
     print(f"identical keys {dtype} chunk {chunk}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
