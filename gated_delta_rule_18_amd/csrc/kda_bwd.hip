@@ -542,8 +542,29 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
                 f32x4 aq = z, ae = z, ax = z, aq2 = z, ae2 = z, ax2 = z;
-                {
-                    // dO S^T, U D^T, dX S^T over the slice's 64 value columns: lane
+                if constexpr (sizeof(E) == 2) {
+                    // bf16 mode: dO S^T, U D^T, dX S^T as 32-deep bf16 MFMAs (operands
+                    // rounded to bf16, as the forward pass rounds S for its products;
+                    // fp32 accumulation).  Lane group g4 takes value columns
+                    // [16 g4, 16 g4 + 16), eight per instruction.
+                    const int k0 = 16 * g4;
+                    const float *pdo = dOs + l16 * L::CS + k0, *pu = Us + l16 * L::CS + k0;
+                    const float *pdx = dXs + l16 * L::CS + k0;
+                    const float *ps = Ss + (16 * ct + l16) * L::SS + k0, *pd = Ds + (16 * ct + l16) * L::SS + k0;
+                    auto rd8 = [](const float *p) {
+                        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+                        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+                        return cat8(cvt4<__bf16>(a), cvt4<__bf16>(b));
+                    };
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb) {
+                        const auto vs = rd8(ps + 8 * hb);
+                        aq = mma32(rd8(pdo + 8 * hb), vs, aq);
+                        ax = mma32(rd8(pdx + 8 * hb), vs, ax);
+                        ae = mma32(rd8(pu + 8 * hb), rd8(pd + 8 * hb), ae);
+                    }
+                } else {
+                    // fp32: dO S^T, U D^T, dX S^T over the slice's 64 value columns: lane
                     // group g4 takes columns [16 g4, 16 g4 + 16), 16 bytes of each
                     // operand row per read; two accumulators per product
                     const int k0 = 16 * g4;
