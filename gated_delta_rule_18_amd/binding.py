@@ -29,7 +29,7 @@ KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
 EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
-           "kda_version")
+           "kda_validate_inputs", "kda_version")
 
 _lib = None
 
@@ -66,6 +66,8 @@ def lib():
         L.kda_output_gate.argtypes = [vp] * 4 + [i] * 3 + [ctypes.c_float, i, vp]
         L.kda_prefill_prep.restype = i
         L.kda_prefill_prep.argtypes = [vp] * 14 + [i] * 7 + [vp]
+        L.kda_validate_inputs.restype = i
+        L.kda_validate_inputs.argtypes = [vp] * 3 + [i] * 5 + [vp]
         L.kda_strerror.restype = ctypes.c_char_p
         L.kda_strerror.argtypes = [i]
         L.kda_version.restype = i
@@ -268,6 +270,22 @@ def output_gate(o, gate, norm_w=None, eps=1e-6, y=None):
                                _stream(dev))
     _check(rc)
     return y
+
+
+def validate_inputs(g, beta):
+    """Debug check of the value domains: g [B,T,H,dk] in [-5, 0], beta [B,T,H] in [0, 1]
+    (NaN outside both).  Waits for the GPU and returns dict(bad_g, first_bad_g, bad_beta,
+    first_bad_beta) with flat indices, -1 where nothing is outside."""
+    B, T, H, dk = g.shape
+    dev, dt = g.device, g.dtype
+    code = _dtype_code(g)
+    _want(g, "g", (B, T, H, dk), dt, dev)
+    _want(beta, "beta", (B, T, H), dt, dev)
+    report = torch.empty(4, dtype=torch.int64, device=dev)
+    rc = lib().kda_validate_inputs(_ptr(g), _ptr(beta), _ptr(report), B, T, H, dk, code, _stream(dev))
+    _check(rc)
+    r = [int(x) for x in report.cpu()]
+    return dict(bad_g=r[0], first_bad_g=r[1], bad_beta=r[2], first_bad_beta=r[3])
 
 
 def prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, out=None,

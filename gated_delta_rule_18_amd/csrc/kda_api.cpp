@@ -192,6 +192,25 @@ int kda_output_gate(const void *o, const void *gate, const float *norm_w, void *
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int kda_validate_inputs(const void *g, const void *beta, long long *report, int B, int T, int H, int dk,
+                        int dtype, void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (!report || (reinterpret_cast<std::uintptr_t>(report) & 7u) != 0)
+        return KDA_ERR_INVALID;
+    const long long nb = (long long)B * T * H, ng = nb * dk;
+    if (ng > (1LL << 40))
+        return KDA_ERR_INVALID;
+    if (ng > 0 && (!g || !beta))
+        return KDA_ERR_INVALID;
+    hipError_t e = kda::launch_validate(g, beta, report, (long)ng, (long)nb, dtype == KDA_FP32,
+                                        reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv)
 {
     if (B < 0 || T < 0 || H < 0 || !head_ok(dk) || !head_ok(dv))

@@ -24,6 +24,12 @@ hipError_t launch_chunk16(const void *q, const void *k, const void *v, const voi
                           int B, int T, int H, int dk, int dv, bool fp32, const Snapshots &snap,
                           hipStream_t stream);
 
+// Debug check of the value domains: report (device int64[4]) receives the number
+// of g outside [-5, 0] (or NaN), the first such flat index (-1 if none), and the
+// same two for beta outside [0, 1]; ng, nb are the element counts.
+hipError_t launch_validate(const void *g, const void *beta, long long *report, long ng, long nb, bool fp32,
+                           hipStream_t stream);
+
 // Output exposure gate fused into the decode step: when gate is not null the
 // step writes y = Sigmoid(gate) * o / sqrt(mean o^2 + eps) * w in place of o
 // (w null = ones).

@@ -28,7 +28,8 @@
  *   - Return 0 on success or a negative KDA_ERR_* code; nothing is enqueued
  *     when a code other than KDA_ERR_LAUNCH is returned.
  *   - Values outside the stated domains (g outside [-5, 0], beta outside
- *     [0, 1], non-finite inputs) are not diagnosed and give unspecified output.
+ *     [0, 1], non-finite inputs) are not diagnosed by the compute entry points
+ *     and give unspecified output; kda_validate_inputs reports them.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -261,6 +262,27 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
 
 /* Bytes of workspace kda_chunk_bwd needs for these sizes (0 for invalid sizes). */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk_size, int dv_size);
+
+/*
+ * kda_validate_inputs -- debug check of the value domains the kernels assume
+ * (the "values outside the stated domains" of the conventions above).
+ *
+ * Domains (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+ * section 3.3, lower-bounded decay: g in [g_min, 0], g_min = -5; section 3.1:
+ * beta in [0, 1], the write strength of the delta rule).  NaN is outside both.
+ *
+ *   g      : [B, T, H, dk] (dtype)   as passed to kda_chunk_fwd
+ *   beta   : [B, T, H]     (dtype)
+ *   report : DEVICE int64[4], 8-byte aligned, written:
+ *            report[0] = number of g elements outside [-5, 0]
+ *            report[1] = flat index of the first of them, -1 if none
+ *            report[2], report[3] = the same for beta outside [0, 1]
+ * Enqueued on `stream` like every other entry point (read the report after the
+ * stream has finished).  Errors: KDA_ERR_INVALID (null report or null tensor
+ * with elements, bad size or dtype, misaligned report), KDA_ERR_LAUNCH.
+ */
+int kda_validate_inputs(const void *g, const void *beta, long long *report,
+                        int B, int T, int H, int dk, int dtype, void *stream);
 
 /* Human-readable text for a kda_status code (static storage, never NULL). */
 const char *kda_strerror(int status);

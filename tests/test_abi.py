@@ -242,3 +242,19 @@ def test_bwd_rejects(kw, code):
 
 def test_bwd_empty_batch_is_a_no_op():
     assert _bwd(B=0, q=None, ws=None, wsb=0) == 0
+
+
+def _validate(**kw):
+    args = dict(g=A, beta=A + (1 << 24), report=A + (2 << 24), B=1, T=4, H=2, dk=64, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return binding.lib().kda_validate_inputs(vp(args["g"]), vp(args["beta"]), vp(args["report"]), args["B"],
+                                             args["T"], args["H"], args["dk"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(report=None), -1), (dict(report=A + (2 << 24) + 4), -1),   # report missing or not 8-byte aligned
+    (dict(dtype=2), -1), (dict(T=-1), -1), (dict(dk=0), -1), (dict(g=None), -1), (dict(beta=None), -1),
+])
+def test_validate_rejects(kw, code):
+    assert _validate(**kw) == code
