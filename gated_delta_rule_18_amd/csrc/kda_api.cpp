@@ -26,7 +26,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
         return KDA_ERR_INVALID;
     if (dtype != KDA_BF16 && dtype != KDA_FP32)
         return KDA_ERR_INVALID;
-    if (chunk != 16 && chunk != 32)
+    if (chunk != 16 && chunk != 32 && chunk != 64)
         return KDA_ERR_INVALID;
     if (!head_ok(dk) || !head_ok(dv))
         return KDA_ERR_UNSUPPORTED;
@@ -53,8 +53,17 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
         if (overlap(snap.out, snap_bytes, S0, state_bytes) || overlap(snap.out, snap_bytes, S_T, state_bytes))
             return KDA_ERR_INVALID;
     }
+    // chunk 64 runs the 16-token kernel: the chunk size only changes how the same
+    // map is blocked, and that kernel's chunk is already the 16-position tile in
+    // which every decay factor stays bounded.  Snapshot spacing in its chunks.
+    kda::Snapshots ks = snap;
+    int kchunk = chunk;
+    if (chunk == 64) {
+        kchunk = 16;
+        ks.every_chunks = snap.every_chunks * 4;
+    }
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
-                                         dtype == KDA_FP32, chunk, snap,
+                                         dtype == KDA_FP32, kchunk, ks,
                                          reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -72,7 +72,9 @@ enum kda_status {
  *                                        S_T may equal S0 (in-place streaming over
  *                                        segments); any other overlap is invalid.
  *   dk, dv  : 64 or 128
- *   chunk   : 16 or 32 (tokens per chunk; both give the same result up to rounding)
+ *   chunk   : 16, 32 or 64 tokens per chunk; every size gives the same result up
+ *             to rounding (64 runs the 16-token kernel: the chunk size only
+ *             changes the blocking of the same map)
  * T may be any value >= 0 (a ragged last chunk is handled); T == 0 copies S0
  * to S_T (or zeroes S_T when S0 is NULL).
  */

@@ -51,7 +51,7 @@ def _prefill(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(chunk=64), -1), (dict(chunk=7), -1), (dict(dtype=2), -1), (dict(B=-1), -1),
+    (dict(chunk=48), -1), (dict(chunk=128), -1), (dict(chunk=7), -1), (dict(dtype=2), -1), (dict(B=-1), -1),
     (dict(T=-3), -1), (dict(dk=0), -1), (dict(dk=96), -2), (dict(dv=256), -2),
     (dict(q=None), -1), (dict(o=None), -1), (dict(k=MIS), -1), (dict(S_T=A + 64), -1),
 ])
@@ -77,7 +77,9 @@ def _prefill_snap(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n=-1), -1), (dict(snaps=None), -1), (dict(every=24), -1), (dict(every=0), -1),
-    (dict(n=3), -1), (dict(snaps=MIS), -1), (dict(snaps=A + 64), -1), (dict(chunk=64), -1),
+    (dict(n=3), -1), (dict(snaps=MIS), -1), (dict(snaps=A + 64), -1),
+    (dict(chunk=64), -1),                       # every = 32 is not a multiple of the chunk
+    (dict(chunk=48), -1),
     (dict(every=64, chunk=32, n=2), -1), (dict(dk=96), -2),
 ])
 def test_prefill_snapshots_rejects(kw, code):

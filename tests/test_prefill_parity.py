@@ -68,12 +68,12 @@ def test_bound_stress_all_minus5(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_identical_keys_full_erase(gpu, dtype, chunk):
     """Every token shares one unit key, beta = 1, g = 0: each write erases the last one
     along k, and inside a chunk A is the strict lower part of all ones, whose powers in
     the nilpotent inverse reach C(14, 7) = 3432 before cancelling to entries of +-1.
-    T = 80 leaves a ragged last chunk for chunk 32.  In bf16 mode the erase rides on U:
+    T = 80 leaves a ragged last chunk for chunk 32 and 64.  In bf16 mode the erase rides on U:
     U_r = v_r - v_{r-1} once T is the +-1 bidiagonal inverse, each row rounded to bf16
     (2^-9 relative), and the state update sums the chunk's 16 rows, so the state's error
     grows like sqrt(16) 2^-9 ~ 8e-3 of its norm per chunk and o inherits it: both are held
@@ -147,6 +147,9 @@ def test_chunk_size_independence_and_determinism(gpu):
     assert torch.equal(o16, o16b) and torch.equal(s16, s16b), "run-to-run bitwise (chunk 16)"
     assert_parity(to_f64(o16), to_f64(o32), 2e-2, "chunk 16 vs 32 o")
     assert_parity(to_f64(s16), to_f64(s32), 1e-2, "chunk 16 vs 32 S")
+    # chunk 64 is served by the 16-token kernel: the same bits
+    o64, s64 = _run(inp, 64)
+    assert torch.equal(o64, o16) and torch.equal(s64, s16), "chunk 64 runs the chunk-16 kernel"
 
 
 @pytest.mark.parametrize("chunk", [16, 32])
@@ -170,6 +173,7 @@ def test_prefill_b4h32_sampled_heads(gpu, name, chunk):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("chunk,every,dk,dv", [(16, 16, 128, 128), (16, 48, 64, 128), (32, 64, 128, 64),
+                                              (64, 128, 128, 128),
                                               (32, 32, 64, 64)])
 def test_snapshots_match_oracle(gpu, dtype, chunk, every, dk, dv):
     """kda_chunk_fwd_snapshots: snapshot s against the oracle's state after (s+1)*every
