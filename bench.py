@@ -180,7 +180,7 @@ def main():
                          "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

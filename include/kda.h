@@ -50,7 +50,7 @@ enum kda_dtype {
 enum kda_status {
     KDA_OK = 0,
     KDA_ERR_INVALID = -1,     /* null required pointer, bad size, bad dtype/chunk/width/misalignment */
-    KDA_ERR_UNSUPPORTED = -2, /* a head size this build has no kernel for (dk, dv not in {64, 128}) */
+    KDA_ERR_UNSUPPORTED = -2, /* a head size the library has no kernel for (dk, dv not in {64, 128}) */
     KDA_ERR_LAUNCH = -3       /* the HIP runtime rejected the launch */
 };
 
