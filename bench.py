@@ -79,11 +79,12 @@ def bwd_flops(B, T, H, dk, dv, C=16):
 
 def bwd_bytes(B, T, H, dk, dv, es=2, C=16):
     """Algorithmic HBM bytes of one kda_chunk_bwd call: inputs q, k, v, g, beta, dO in the
-    activation dtype; the recomputed incoming state of every chunk written once and read once
-    (8 dk dv per chunk-head); fp32 gradients dq, dk, dg, dv, dbeta out; S0, dS_T in and dS0 out."""
+    activation dtype; the incoming state of every chunk, kept in the activation dtype, written
+    once by the recompute and read once by the reverse walk (2 es dk dv per chunk-head); fp32
+    gradients dq, dk, dg, dv, dbeta out; S0, dS_T in and dS0 out."""
     nch = (T + C - 1) // C
     per_token = es * (3 * dk + 2 * dv + 1) + 4 * (3 * dk + dv + 1)
-    return B * T * H * per_token + B * H * (max(nch - 1, 0) * 8 * dk * dv + 12 * dk * dv)
+    return B * T * H * per_token + B * H * (nch * 2 * es * dk * dv + 12 * dk * dv)
 
 
 def gate_bytes(rows, H, dv):

@@ -22,8 +22,10 @@
 //            dq = dQt P,  dk = dKt P + dKc / P + dKe Gam / P,
 //            dg = reverse cumulative sum of dG over the chunk's tokens,
 //            D_in = Diag(Gam) D + Qt^T dO - Kt^T dX.
-// A forward pass (the chunk-16 prefill kernel writing its state after every
-// chunk) supplies each chunk's incoming state S.
+// A forward pass (the chunk-16 prefill kernel writing the initial state and
+// its state after every chunk) supplies each chunk's incoming state S, stored
+// in the element type: in bf16 mode that is the precision the forward kernel's
+// own products read the state in, and half the bytes of fp32.
 //
 // Work decomposition: one workgroup of 256 threads per (sequence, head,
 // 64-wide value slice) walks the chunks from last to first.  The slice's part
@@ -180,9 +182,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_buffer(const void *base, l
 }
 
 // Loads of one chunk's inputs for the reverse walk, held in registers: the
-// slice's part of the incoming state (fp32 [DK][64]: thread t owns DK/4
-// consecutive floats of row t / (256 / DK)), q, k, g (thread t: DK/16 elements
-// of token t / 16), v and dO (4 elements of token t / 16) and beta.
+// slice's part of the chunk's incoming state from the packed workspace (thread
+// t: DK/16 consecutive columns of the 4-row group t / (1024 / DK)), q, k, g
+// (thread t: DK/16 elements of token t / 16), v and dO (4 elements of token
+// t / 16) and beta.
 // Buffer over the first n rows (stride bytes apart, width bytes each) of an
 // output: stores to rows n and beyond fall outside it and are dropped, so a
 // ragged last chunk needs no branch around its stores.
@@ -197,27 +200,36 @@ __device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, int voff, float
 
 template <typename E, int DK>
 struct Pre {
-    static constexpr int FPT = DK / 4, TPR = kNV / FPT;      // state floats per thread, threads per row
+    static constexpr int CPT = DK / 16, TPQ = kNV / CPT;      // state columns per thread, threads per 4-row group
     static constexpr int EPT = DK / 16;                       // q/k/g elements per thread
     static constexpr int ES = (int)sizeof(E);
-    f32x4 s[FPT / 4];
+    static constexpr int NPK = CPT * ES / 4;                  // 16-byte loads of the state piece
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    u4 sx[NPK];                       // element 4 cc + jr = (row jr of the group, column cc)
     Raw<E, EPT> qv, kv, gv;
     Raw<E, 4> vv, ov;
     unsigned bv;
 
+    __device__ __forceinline__ float state(int e) const
+    {
+        if constexpr (sizeof(E) == 2) {
+            const unsigned w = sx[e >> 3][(e >> 1) & 3];
+            return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            return __uint_as_float(sx[e >> 2][e & 3]);
+        }
+    }
+
     __device__ __forceinline__ void load(const E *q, const E *k, const E *v, const E *g, const E *beta,
-                                         const E *dO, const float *S0, const float *states, int ci, int T,
-                                         int H, int DV, int nbh, int bh, long tokb, int h, int col0, int t)
+                                         const E *dO, const E *states, int ci, int T, int H, int DV, int nbh,
+                                         int bh, long tokb, int h, int col0, int t)
     {
         const int t0 = ci * kC, n = T - t0 < kC ? T - t0 : kC;
-        const float *Sin = ci == 0 ? (S0 ? S0 + (long)bh * DK * DV : nullptr)
-                                   : states + ((long)(ci - 1) * nbh + bh) * DK * DV;
-        const int c = t / TPR, j0 = (t % TPR) * FPT;
-        const __amdgpu_buffer_rsrc_t rs = bwd_buffer(Sin, Sin ? (long)DK * DV * 4 : 0);
+        const int qd = t / TPQ, j0 = (t % TPQ) * CPT;
+        const __amdgpu_buffer_rsrc_t rs = bwd_buffer(states + ((long)ci * nbh + bh) * DK * DV, (long)DK * DV * ES);
 #pragma unroll
-        for (int u = 0; u < FPT / 4; ++u)
-            s[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rs, (c * DV + col0 + j0 + 4 * u) * 4, 0, 0));
+        for (int u = 0; u < NPK; ++u)
+            sx[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (qd * DV + col0 + j0) * 4 * ES, 16 * u, 0);
         // buffers over the chunk's n token rows of this head: rows past n read 0
         const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
         const long row0 = (tokb + t0) * H + h;
@@ -242,10 +254,17 @@ struct Pre {
     __device__ __forceinline__ void store_to(float *Ss, float *Qt, float *Kt, float *Pm, float *Xs, float *dOs,
                                              float *bet, int t) const
     {
-        const int c = t / TPR, j0 = (t % TPR) * FPT;
+        const int qd = t / TPQ, j0 = (t % TPQ) * CPT;
 #pragma unroll
-        for (int u = 0; u < FPT / 4; ++u)
-            *reinterpret_cast<f32x4 *>(Ss + c * LL::SS + j0 + 4 * u) = s[u];
+        for (int jr = 0; jr < 4; ++jr)
+#pragma unroll
+            for (int u = 0; u < CPT / 4; ++u) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = state(4 * (4 * u + e) + jr);
+                *reinterpret_cast<f32x4 *>(Ss + (4 * qd + jr) * LL::SS + j0 + 4 * u) = x;
+            }
         const int r = t >> 4, cc = (t & 15) * EPT, jj = (t & 15) * 4;
 #pragma unroll
         for (int u = 0; u < EPT / 4; ++u) {
@@ -275,8 +294,8 @@ struct Pre {
 template <typename E, int DK>
 __global__ __launch_bounds__(kBT) void bwd_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const E *__restrict__ g,
-    const E *__restrict__ beta, const float *__restrict__ S0, const E *__restrict__ dO,
-    const float *__restrict__ dST, const float *__restrict__ states, float *__restrict__ dv_out,
+    const E *__restrict__ beta, const E *__restrict__ dO,
+    const float *__restrict__ dST, const E *__restrict__ states, float *__restrict__ dv_out,
     float *__restrict__ dS0_out, float *__restrict__ pq, float *__restrict__ pk, float *__restrict__ pg,
     float *__restrict__ pb, int T, int H, int DV, int nbh, int nsl)
 {
@@ -312,7 +331,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     // issued before any is waited on) and moved to LDS at the top of the chunk.
     Pre<E, DK> pre;
     if (nchunks > 0)
-        pre.load(q, k, v, g, beta, dO, S0, states, nchunks - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
+        pre.load(q, k, v, g, beta, dO, states, nchunks - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
     for (int ci = nchunks - 1; ci >= 0; --ci) {
         const int t0 = ci * kC;
         const int n = T - t0 < kC ? T - t0 : kC;
@@ -320,7 +339,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         // ---- the chunk's incoming state and inputs (rows r >= n are zero) ---------
         pre.store(Ss, Qt, Kt, Pm, Xs, dOs, bet, t);
         if (ci > 0)
-            pre.load(q, k, v, g, beta, dO, S0, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
+            pre.load(q, k, v, g, beta, dO, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
         __syncthreads();
 
         // ---- decay factors and operands: thread (c, part) owns key channel c for
@@ -722,7 +741,7 @@ __global__ __launch_bounds__(256) void sum_slices(const float *__restrict__ part
 
 template <typename E, int DK>
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                      const float *S0, const void *dO, const float *dST, float *states, float *dq,
+                      const void *dO, const float *dST, float *states, float *dq,
                       float *dk, float *dv, float *dg, float *dbeta, float *dS0, float *partials, int B,
                       int T, int H, int DV, hipStream_t stream)
 {
@@ -744,8 +763,8 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g
     float *pb = nsl > 1 ? partials + 3L * nsl * rows * DK : dbeta;
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     hipLaunchKernelGGL((bwd_kernel<E, DK>), dim3(grid), dim3(kBT), L::bytes, stream, (const E *)q,
-                       (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0, (const E *)dO, dST,
-                       states, dv, dS0, pq, pk, pg, pb, T, H, DV, nbh, nsl);
+                       (const E *)k, (const E *)v, (const E *)g, (const E *)beta, (const E *)dO, dST,
+                       (const E *)states, dv, dS0, pq, pk, pg, pb, T, H, DV, nbh, nsl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nsl == 1 || rows == 0)
         return e;
@@ -765,7 +784,7 @@ size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv)
 {
     const long nchunks = (T + kC - 1) / kC;
     const long nsl = dv / kNV;
-    const long states = (nchunks > 1 ? nchunks - 1 : 0) * B * H * (long)dk * dv;
+    const long states = nchunks * B * H * (long)dk * dv;      // fp32-sized: either dtype fits
     const long parts = nsl > 1 ? nsl * (long)B * T * H * (3L * dk + 1) : 0;
     // each region rounded up to 64 floats (256 bytes)
     return (size_t)(((states + 63) / 64) * 64 + ((parts + 63) / 64) * 64);
@@ -777,16 +796,20 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
                             int H, int DK, int DV, bool fp32, hipStream_t stream)
 {
     const long nchunks = (T + kC - 1) / kC;
-    const long sfl = (nchunks > 1 ? nchunks - 1 : 0) * B * H * (long)DK * DV;
+    const long sfl = nchunks * B * H * (long)DK * DV;
     float *states = workspace;
     float *partials = workspace + ((sfl + 63) / 64) * 64;
-    // 1. the incoming state of every chunk: the forward pass with a snapshot
-    //    after every chunk (o not written)
-    if (nchunks > 1) {
+    // 1. the incoming state of every chunk: the forward pass writing its initial
+    //    state and its state after every chunk but the last (o not written), in
+    //    the element type (bf16 mode: the precision the forward pass's own
+    //    products see the state in) and the packed layout; the region is sized
+    //    for fp32
+    if (nchunks > 0) {
         Snapshots snap;
         snap.out = states;
         snap.every_chunks = 1;
         snap.count = (int)(nchunks - 1);
+        snap.packed = true;
         hipError_t e = launch_chunk16(q, k, v, g, beta, S0, nullptr, nullptr, B, T, H, DK, DV, fp32, snap,
                                       stream);
         if (e != hipSuccess)
@@ -794,13 +817,13 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
     }
     // 2. the reverse walk (and the slice sums)
     if (fp32)
-        return DK == 128 ? launch_bwd<float, 128>(q, k, v, g, beta, S0, dO, dST, states, dq, dk, dv, dg, dbeta,
+        return DK == 128 ? launch_bwd<float, 128>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
                                                    dS0, partials, B, T, H, DV, stream)
-                         : launch_bwd<float, 64>(q, k, v, g, beta, S0, dO, dST, states, dq, dk, dv, dg, dbeta,
+                         : launch_bwd<float, 64>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
                                                  dS0, partials, B, T, H, DV, stream);
-    return DK == 128 ? launch_bwd<__bf16, 128>(q, k, v, g, beta, S0, dO, dST, states, dq, dk, dv, dg, dbeta,
+    return DK == 128 ? launch_bwd<__bf16, 128>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
                                                 dS0, partials, B, T, H, DV, stream)
-                     : launch_bwd<__bf16, 64>(q, k, v, g, beta, S0, dO, dST, states, dq, dk, dv, dg, dbeta,
+                     : launch_bwd<__bf16, 64>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
                                               dS0, partials, B, T, H, DV, stream);
 }
 

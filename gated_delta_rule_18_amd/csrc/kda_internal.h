@@ -7,10 +7,16 @@ namespace kda {
 
 // Intermediate states a prefill writes: snapshot s (s < count) is the state
 // after the first (s + 1) * every_chunks chunks, at out + s * B*H*dk*dv.
+// packed (chunk-16 kernel only; the backward's private workspace): the initial
+// state comes first (snapshot s then sits at out + (s + 1) * B*H*dk*dv), the
+// states are stored in the element type instead of fp32, and each head's state
+// in 4-row groups, element (r, c) at ((r / 4) * dv + c) * 4 + r % 4 -- one
+// contiguous 4-element piece per accumulator lane of the writer.
 struct Snapshots {
     float *out = nullptr;
     int every_chunks = 0;
     int count = 0;
+    bool packed = false;
 };
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,

@@ -573,6 +573,8 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const v
     }
     if (chunk == 16)
         return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, snap, stream);
+    if (snap.packed)
+        return hipErrorInvalidValue;
     if (fp32)
         return dispatch<float>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
     return dispatch<__bf16>(dk, chunk, q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);

@@ -223,15 +223,6 @@ __device__ __forceinline__ unsigned load_bits(__amdgpu_buffer_rsrc_t r, int voff
 }
 __device__ __forceinline__ float bits_to_f(unsigned x, __bf16 *) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bits_to_f(unsigned x, float *) { return __uint_as_float(x); }
-__device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, __bf16 *)
-{
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), r, voff, soff, 0);
-}
-__device__ __forceinline__ void store_scalar(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, float *)
-{
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
-}
-
 // A 16-token tile column of o: rows 4 g4 + j (j < 4) of this lane's column,
 // row j at byte offset voff + j * stride.
 __device__ __forceinline__ void store_o(__amdgpu_buffer_rsrc_t r, int voff, int stride, f32x4 x, __bf16 *)
@@ -308,6 +299,32 @@ __device__ __forceinline__ void store_state(float *dst, const f32x4 (&Sacc)[NCT]
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sacc[ct][j]), r, lane_off, (16 * ct + j) * DV * 4, 0);
 }
 
+// The same strip in the packed layout of the backward's workspace: element
+// type E, element (r, c) at ((r / 4) DV + c) 4 + r % 4, so that the lane's four
+// rows 16 ct + 4 g4 + j of one column are one contiguous piece; lane_off is the
+// byte offset of the piece of (4 g4, col).  Lanes l16 of a row group g4 write
+// 16 consecutive pieces (whole cache lines).
+__device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff, f32x4 x, __bf16 *)
+{
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{Pair<__bf16>::pack(x[0], x[1]), Pair<__bf16>::pack(x[2], x[3])}, r,
+                                          voff, soff, 0);
+}
+__device__ __forceinline__ void store_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff, f32x4 x, float *)
+{
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, voff, soff, 0);
+}
+template <typename E, int NCT>
+__device__ __forceinline__ void store_state_packed(E *dst, const f32x4 (&Sacc)[NCT], int lane_off, int DV)
+{
+    constexpr int ES = (int)sizeof(E);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst, 0, NCT * 16 * DV * ES, 0x00020000);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+        store_piece(r, lane_off, ct * 4 * DV * 4 * ES, Sacc[ct], (E *)nullptr);
+}
+
 // Bytes spanned by `rows` rows of `width` bytes, `stride` bytes apart (0 rows: 0).
 __device__ __forceinline__ int rows_bytes(int rows, int stride, int width)
 {
@@ -377,7 +394,8 @@ template <typename E, int DK>
 __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
-    float *S_T, float *snaps, int snap_chunks, int n_snaps, int T, int H, int DV, int nbh, int nsl)
+    float *S_T, float *snaps, int snap_chunks, int n_snaps, int snap_packed, int T, int H, int DV, int nbh,
+    int nsl)
 {
     typedef WsL<E, DK> L;
     typedef typename Vec<E>::v4 V4;
@@ -490,9 +508,17 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                 op.kr[ct] = z;
         }
         const int lane_soff = ((4 * g4) * DV + col) * 4;   // byte offset of S[4 g4][col] in a state
+        // snapshots: fp32 row-major, or the packed layout (lane piece (g4, col))
+        const int snap_es = snap_packed ? L::ES : 4;
+        const int lane_poff = (g4 * DV + col) * 4 * L::ES;
         int snap_left = snap_chunks, snap_idx = 0;
-        float *snap_dst = snaps ? snaps + (long)bh * DK * DV : nullptr;
-        const long snap_step = (long)nbh * DK * DV;
+        char *snap_dst = snaps ? reinterpret_cast<char *>(snaps) + (long)bh * DK * DV * snap_es : nullptr;
+        const long snap_step = (long)nbh * DK * DV * snap_es;
+        // the packed workspace starts with the initial state
+        if (snap_dst && snap_packed) {
+            store_state_packed(reinterpret_cast<E *>(snap_dst), Sacc, lane_poff, DV);
+            snap_dst += snap_step;
+        }
         int s = 0;                                        // slot of chunk c
         if (nchunks > 0)
             fetch(op, 0, 0);
@@ -529,8 +555,12 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             if (snaps) {
                 if (--snap_left == 0) {
                     snap_left = snap_chunks;
-                    if (snap_idx < n_snaps)
-                        store_state(snap_dst, Sacc, lane_soff, DV);
+                    if (snap_idx < n_snaps) {
+                        if (snap_packed)
+                            store_state_packed(reinterpret_cast<E *>(snap_dst), Sacc, lane_poff, DV);
+                        else
+                            store_state(reinterpret_cast<float *>(snap_dst), Sacc, lane_soff, DV);
+                    }
                     ++snap_idx;
                     snap_dst += snap_step;
                 }
@@ -795,8 +825,8 @@ hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g,
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(64 * (4 + L::NP)), lds, stream,
                        (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
-                       (E *)o, S_T, snap.count > 0 ? snap.out : nullptr, snap.every_chunks, snap.count,
-                       T, H, dv, nbh, nsl);
+                       (E *)o, S_T, snap.count > 0 || snap.packed ? snap.out : nullptr, snap.every_chunks,
+                       snap.count, snap.packed ? 1 : 0, T, H, dv, nbh, nsl);
     return hipGetLastError();
 }
 

@@ -218,13 +218,15 @@ def _bwd(**kw):
 
 
 def test_bwd_workspace_size():
-    # two slices of 64 value columns: the incoming state of chunks 1, 2 and the slice partials
-    want_states = 2 * 2 * 64 * 128 * 4
+    # two slices of 64 value columns: the incoming state of chunks 0, 1, 2 (sized
+    # as fp32 for either dtype) and the slice partials
+    want_states = 3 * 2 * 64 * 128 * 4
     want_parts = 2 * 1 * 40 * 2 * (3 * 64 + 1) * 4
     rnd = lambda b: (b + 255) // 256 * 256
     assert binding.workspace_size(1, 40, 2, 64, 128) == rnd(want_states) + rnd(want_parts)
-    assert binding.workspace_size(1, 40, 2, 64, 64) == rnd(2 * 2 * 64 * 64 * 4)    # one slice: no partials
-    assert binding.workspace_size(1, 16, 2, 64, 64) == 0                            # one chunk: nothing
+    assert binding.workspace_size(1, 40, 2, 64, 64) == rnd(3 * 2 * 64 * 64 * 4)    # one slice: no partials
+    assert binding.workspace_size(1, 16, 2, 64, 64) == 2 * 64 * 64 * 4              # one chunk: its S0
+    assert binding.workspace_size(1, 0, 2, 64, 64) == 0                             # no tokens: nothing
     assert binding.workspace_size(1, 40, 2, 96, 64) == 0                            # unsupported size
 
 
