@@ -675,6 +675,10 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         // ---- claim the slot, then write the consumers' operand images ----------
         if (c >= NS)
             wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
+        // while it holds the slot the producer issues ahead of the other producer
+        // on its SIMD (still behind the consumer): the time a slot is held bounds
+        // how many chunks are in flight
+        __builtin_amdgcn_s_setprio(1);
         E *sl = reinterpret_cast<E *>(smem + L::oSlots + s * L::slotBytes);
         float *gam = reinterpret_cast<float *>(smem + L::oSlots + s * L::slotBytes + L::slotE * L::ES);
         {
@@ -795,6 +799,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         lds_fence();
         if (lane == 0)
             st_flag(ready + s, c + 1);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // one chunk in flight per producer: the loads for chunk c + NP are issued
