@@ -249,8 +249,11 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
  *   dbeta : [B, T, H] fp32          written
  *   dS0   : [B, H, dk, dv] fp32     written; NULL = not returned
  *   workspace : device memory of kda_chunk_bwd_workspace_size(B, T, H, dk, dv)
- *               bytes (may be NULL when that size is 0), 256-byte aligned; its
- *               contents on entry are ignored and on return unspecified
+ *               bytes (may be NULL when that size is 0, i.e. T = 0), 256-byte
+ *               aligned; its contents on entry are ignored and on return
+ *               unspecified.  It holds every chunk's incoming state (sized as
+ *               fp32 for either dtype) and, for dv = 128, the two value slices'
+ *               partial dq, dk, dg, dbeta
  *   dk, dv (sizes) : 64 or 128
  * Gradients are fp32 in both dtype modes.  No output may overlap an input or
  * another output.  Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size,
