@@ -20,8 +20,9 @@
 // With the chunk start as the reference point every factor spans at most 16
 // positions: P and Gam / P lie in [e^-80, 1] and 1 / P in [1, e^80] -- exactly
 // the range the pages' bound guarantees.  P is a running product of
-// a_t = exp(g_t) (one exponential per element); 1 / P comes from the hardware
-// reciprocal (e^80 = 5.5e34 is far inside fp32) and Gam / P = Gam * (1 / P).
+// a_t = exp(g_t) (one exponential per element), Gam / P a running suffix
+// product of the same a_t, and 1 / P = (Gam / P) * (1 / Gam) with one hardware
+// reciprocal per channel and chunk (e^80 = 5.5e34 is far inside fp32).
 //
 // Work decomposition.  A workgroup owns one (sequence, head, 64-wide value
 // slice); value columns of S never interact.  It runs 4 consumer wavefronts
@@ -33,8 +34,8 @@
 //   producers       -- producer p owns chunks p, p+NP, p+2NP, ...: it loads q,
 //                      k, g, v directly in its compute layout (lane = four key
 //                      channels x eight tokens), builds the decayed operands in
-//                      registers (running products of exp(g); Kc = k / P through
-//                      the hardware reciprocal), and only then claims one of NS
+//                      registers (prefix and suffix running products of exp(g);
+//                      Kc = k / P from the suffix), and only then claims one of NS
 //                      LDS slots, writes the consumers' operand images, issues
 //                      the loads of its next chunk, forms A, M and the UT
 //                      inverse on MFMA, and publishes the slot.
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             }
             // each half's total (a product tree over its 8 tokens); the partner's
             // total starts the second half's prefix and completes Gam = e^{G_15}
-            float oth[4], p[4];
+            float oth[4], sf[4], ig[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float t01 = al[u][0] * al[u][1], t23 = al[u][2] * al[u][3];
@@ -639,35 +640,51 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                 const float tot = (t01 * t23) * (t45 * t67);
                 oth[u] = __shfl_xor(tot, 32, 64);
                 gm4[u] = tot * oth[u];
-                p[u] = th ? oth[u] : 1.f;
+                sf[u] = th ? 1.f : oth[u];
+                ig[u] = __builtin_amdgcn_rcpf(gm4[u]);    // 1 / Gam: one reciprocal per channel
             }
-            // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P, Kc = k / P, Ke = Kc Gam
-            float es[4][4];
+            // running suffix Gam / P_r = prod_{s > r} alpha_s (no division per
+            // element); Ke = k Gam / P, Kc = k / P = Ke (1 / Gam).  Gam >= e^-80 is
+            // a normal float, so 1 / Gam <= e^80 is finite.
+            // kep[i / 4][2u + (i % 4) / 2] packs channel u of tokens i, i + 1 (i even)
+            float es[4];
+#pragma unroll
+            for (int i = 7; i >= 0; --i) {
+                float kk[4], kc[4];
+                kk[0] = PE::lo(raw.k[i].a), kk[1] = PE::hi(raw.k[i].a), kk[2] = PE::lo(raw.k[i].b), kk[3] = PE::hi(raw.k[i].b);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float e = kk[u] * sf[u];
+                    kc[u] = e * ig[u];
+                    if (i & 1)
+                        es[u] = e;
+                    else
+                        kep[i >> 2][2 * u + ((i & 3) >> 1)] = PE::pack(e, es[u]);
+                    if (i > 0)
+                        sf[u] *= al[u][i];
+                }
+                // Kc only feeds this producer's own products: its private image
+                st_pair2(pKc + io + 8 * i, PE::pack(kc[0], kc[1]), PE::pack(kc[2], kc[3]));
+            }
+            // running prefix P_r = e^{G_r}; Kt = k P, Qt = q P
+            float p[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                p[u] = th ? oth[u] : 1.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float kk[4], qq[4];
                 kk[0] = PE::lo(raw.k[i].a), kk[1] = PE::hi(raw.k[i].a), kk[2] = PE::lo(raw.k[i].b), kk[3] = PE::hi(raw.k[i].b);
                 qq[0] = PE::lo(raw.q[i].a), qq[1] = PE::hi(raw.q[i].a), qq[2] = PE::lo(raw.q[i].b), qq[3] = PE::hi(raw.q[i].b);
-                float kt[4], qt[4], kc[4];
+                float kt[4], qt[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     p[u] *= al[u][i];
                     kt[u] = -(kk[u] * p[u]);   // stored negated (see the consumer)
                     qt[u] = qq[u] * p[u];
-                    kc[u] = kk[u] * __builtin_amdgcn_rcpf(p[u]);
-                    es[u][i & 3] = kc[u] * gm4[u];
                 }
                 ktp[i][0] = PE::pack(kt[0], kt[1]), ktp[i][1] = PE::pack(kt[2], kt[3]);
                 qtp[i][0] = PE::pack(qt[0], qt[1]), qtp[i][1] = PE::pack(qt[2], qt[3]);
-                // Kc only feeds this producer's own products: its private image
-                st_pair2(pKc + io + 8 * i, PE::pack(kc[0], kc[1]), PE::pack(kc[2], kc[3]));
-                if ((i & 3) == 3) {
-                    PT *d = kep[i >> 2];
-                    d[0] = PE::pack(es[0][0], es[0][1]), d[1] = PE::pack(es[0][2], es[0][3]);
-                    d[2] = PE::pack(es[1][0], es[1][1]), d[3] = PE::pack(es[1][2], es[1][3]);
-                    d[4] = PE::pack(es[2][0], es[2][1]), d[5] = PE::pack(es[2][2], es[2][3]);
-                    d[6] = PE::pack(es[3][0], es[3][1]), d[7] = PE::pack(es[3][2], es[3][3]);
-                }
             }
         }
         const unsigned braw = raw.b;
