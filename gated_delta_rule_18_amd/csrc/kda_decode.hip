@@ -7,8 +7,10 @@
 // S' = Sbar + beta k (v - vhat)^T, o = S'^T q (read after the write).
 //
 // The step is bound by HBM traffic: the 4*dk*dv-byte fp32 state of every
-// (sequence, head) is read once and written once.  One workgroup of 256
-// threads owns one (sequence, head):
+// (sequence, head) is read once and written once.  A workgroup owns kHP
+// (sequence, head) pairs, kTPH threads each (a single head per 256-thread
+// workgroup streamed the in-place read-modify-write ~8 % slower on gfx950);
+// per head:
 //   * each thread holds a float4 column strip of ROWS key rows of S in
 //     registers from the read to the write, so HBM sees exactly one read and
 //     one write of the state (loads are issued first, before the conv work);
@@ -28,7 +30,9 @@
 namespace kda {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kHP = 2;                // heads per workgroup
+constexpr int kTPH = 128;             // threads per head
+constexpr int kThreads = kHP * kTPH;
 constexpr int kWidth = 4;
 constexpr float kL2Eps = 1e-6f;
 
@@ -79,25 +83,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const E *__restrict__ q_pre, const E *__restrict__ k_pre, const E *__restrict__ v_pre,
     const float *__restrict__ conv_w, E *__restrict__ conv_cache, int oldest,
     const E *__restrict__ g, const E *__restrict__ beta, float *__restrict__ S,
-    E *__restrict__ o, int H, const E *__restrict__ gate, const float *__restrict__ norm_w, float eps)
+    E *__restrict__ o, int H, long heads, const E *__restrict__ gate, const float *__restrict__ norm_w,
+    float eps)
 {
     constexpr int NCH = 2 * DK + DV;      // conv channels q | k | v
     constexpr int CG = DV / 4;            // float4 column groups
-    constexpr int RG = kThreads / CG;     // row groups
+    constexpr int RG = kTPH / CG;         // row groups
     constexpr int ROWS = DK / RG;         // rows per thread
-    constexpr int NW = kThreads / 64;
-    static_assert(NCH / 2 <= kThreads && DK <= kThreads && ROWS >= 1, "shape");
+    constexpr int NW = kTPH / 64;         // wavefronts per head
+    static_assert(kTPH % 64 == 0 && CG < 64 && ROWS >= 1 && RG * ROWS == DK, "shape");
 
-    const int nh = blockIdx.x;            // sequence * H + head
-    const int h = nh % H;
-    const int t = threadIdx.x;
+    // head slot hs of the workgroup owns (sequence * H + head) nh; in a ragged
+    // last workgroup a slot past the end redoes the last head's arithmetic (its
+    // barriers are the workgroup's) and writes nothing
+    const int hs = threadIdx.x / kTPH;
+    const long nh_raw = (long)blockIdx.x * kHP + hs;
+    const bool live = nh_raw < heads;
+    const long nh = live ? nh_raw : heads - 1;
+    const int h = (int)(nh % H);
+    const int t = threadIdx.x % kTPH;
     const int cg = t % CG, rg = t / CG;
     const int lane = t & 63, wave = t >> 6;
 
-    __shared__ float act[NCH];
-    __shared__ float alpha[DK];
-    __shared__ float red[NW][2 * DV];
-    __shared__ float scal[3];
+    __shared__ float act_s[kHP][NCH];
+    __shared__ float alpha_s[kHP][DK];
+    __shared__ float red_s[kHP][NW][2 * DV];
+    __shared__ float scal_s[kHP][3];
+    float *act = act_s[hs], *alpha = alpha_s[hs], *scal = scal_s[hs];
+    float (*red)[2 * DV] = red_s[hs];
 
     // 1. the state strip, loaded before anything else so the reads are in flight
     float *Sp = S + (size_t)nh * DK * DV;
@@ -118,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
 
     // 2. ShortConv over the window (3 cached tokens, oldest first, then x_t) + Swish
-    if (t < NCH / 2) {
-        const int c = 2 * t;
+    for (int c2 = t; c2 < NCH / 2; c2 += kTPH) {
+        const int c = 2 * c2;
         const E *src;
         int off;
         if (c < DK) {
@@ -148,12 +161,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
             u0 += wa0[j] * a0;
             u1 += wa1[j] * a1;
         }
-        store2(cache + oldest * NCH + c, x0, x1);   // x_t replaces the oldest token
+        if (live)
+            store2(cache + oldest * NCH + c, x0, x1);   // x_t replaces the oldest token
         act[c] = swish(u0);
         act[c + 1] = swish(u1);
     }
-    if (t < DK)
-        alpha[t] = exp_f(to_f(g[(size_t)nh * DK + t]));
+    for (int i = t; i < DK; i += kTPH)
+        alpha[i] = exp_f(to_f(g[(size_t)nh * DK + i]));
     __syncthreads();
 
     // 3. L2Norm scales of q and k, and q . k, by wavefront 0
@@ -231,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             r[c] += bk * d[c];
-        __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(Sp + (size_t)i * DV) + cg);
+        if (live)
+            __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(Sp + (size_t)i * DV) + cg);
     }
     const float bq = bt * qdotk;
     float ov[4];
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
             }
         }
     }
-    if (rg == 0)
+    if (rg == 0 && live)
         store4(o + (size_t)nh * DV + 4 * cg, ov[0], ov[1], ov[2], ov[3]);
 }
 
@@ -263,18 +278,19 @@ hipError_t launch(const void *q_pre, const void *k_pre, const void *v_pre, const
                   void *conv_cache, int oldest, const void *g, const void *beta, float *S, void *o,
                   int N, int H, const OutputGate &og, hipStream_t stream)
 {
-    const long blocks = (long)N * H;
-    if (blocks == 0)
+    const long heads = (long)N * H;
+    if (heads == 0)
         return hipSuccess;
+    const long blocks = (heads + kHP - 1) / kHP;
     if (og.gate)
         hipLaunchKernelGGL((decode_kernel<DK, DV, E, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
-                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H,
+                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H, heads,
                            (const E *)og.gate, og.w, og.eps);
     else
         hipLaunchKernelGGL((decode_kernel<DK, DV, E, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
-                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H,
+                           (E *)conv_cache, oldest, (const E *)g, (const E *)beta, S, (E *)o, H, heads,
                            (const E *)nullptr, (const float *)nullptr, 0.f);
     return hipGetLastError();
 }

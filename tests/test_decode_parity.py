@@ -83,3 +83,32 @@ def test_decode_matches_prefill_token_by_token(gpu):
     torch.cuda.synchronize()
     assert_parity(to_f64(torch.stack(outs, 1)), to_f64(o), 1e-5, "decode vs prefill o")
     assert_parity(to_f64(S), to_f64(sT), 1e-5, "decode vs prefill S")
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_ragged_workgroup_writes_nothing_past_end(gpu, gated):
+    """An odd number of (sequence, head) pairs leaves the last workgroup with a spare
+    head slot: it must not write. S, the conv cache and o are views into buffers one
+    sequence longer, whose tail holds a sentinel that has to survive the step."""
+    spec = DecodeSpec(N=5, H=3, dk=128, dv=128, steps=1, seed_base=90, state_seed=91)
+    N, H, dk, dv = spec.N, spec.H, spec.dk, spec.dv
+    st = decode_state(spec, device=gpu)
+    x = decode_step_inputs(spec, 0, device=gpu)
+    big = lambda t: torch.cat([t, torch.full_like(t[:1], 7.0)], 0)
+    S_big, c_big = big(st["S"]), big(st["conv_cache"])
+    o_big = torch.full((N + 1, H, dv), 7.0, dtype=torch.bfloat16, device=gpu)
+    S, cache, o = S_big[:N], c_big[:N], o_big[:N]
+    if gated:
+        gate = torch.randn((N, H, dv), generator=torch.Generator(device=gpu).manual_seed(92),
+                           device=gpu).to(torch.bfloat16)
+        binding.decode_step_gated(x["q_pre"], x["k_pre"], x["v_pre"], st["conv_w"], cache, 0, x["g"],
+                                  x["beta"], S, gate, None, 1e-6, y=o)
+    else:
+        binding.decode_step(x["q_pre"], x["k_pre"], x["v_pre"], st["conv_w"], cache, 0, x["g"], x["beta"],
+                            S, o=o)
+    torch.cuda.synchronize()
+    assert bool((S_big[N:] == 7.0).all()), "state written past the last head"
+    assert bool((c_big[N:] == 7.0).all()), "conv cache written past the last head"
+    assert bool((o_big[N:] == 7.0).all()), "output written past the last head"
+    # and every real head was written
+    assert not bool((o == 7.0).all(-1).any()), "a head's output row was not written"
