@@ -14,7 +14,7 @@
 // elements each (one 16-byte load per tensor in bf16, two in fp32); the sum of
 // squares is reduced over the unit's lanes with xor shuffles, which stay
 // inside the unit's aligned group of LPU lanes.  Wavefronts stride over the
-// units with two units in flight per lane.
+// units with kGateUnroll units in flight per lane.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -22,7 +22,10 @@ namespace kda {
 namespace {
 
 constexpr int kGateThreads = 256;
-constexpr int kGateBlocksPerCU = 8;
+// two resident workgroups per CU, each lane with 16 units' loads in flight: on
+// gfx950 this streamed 27 % faster than 8 workgroups per CU with 2 units each
+constexpr int kGateBlocksPerCU = 2;
+constexpr int kGateUnroll = 16;
 constexpr int kCUs = 256;
 
 template <typename E> struct Oct;
@@ -107,15 +110,20 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(const E *__restrict_
     const long wave = (long)blockIdx.x * (kGateThreads / 64) + (threadIdx.x >> 6);
     const long stride = (long)gridDim.x * (kGateThreads / 64) * UPW;
     long u = wave * UPW + slot;
-    // two units per lane per iteration: both units' loads are issued first
-    for (; u + stride < units; u += 2 * stride) {
-        const long e0 = u * DV + 8 * sub, e1 = (u + stride) * DV + 8 * sub;
-        const Oct<E> o0 = Oct<E>::load(o + e0), g0 = Oct<E>::load(gate + e0);
-        const Oct<E> o1 = Oct<E>::load(o + e1), g1 = Oct<E>::load(gate + e1);
-        gate_unit<E, DV>(o0, g0, wv, eps, y + e0);
-        gate_unit<E, DV>(o1, g1, wv, eps, y + e1);
+    // kGateUnroll units per lane per iteration: all their loads are issued first
+    for (; u + (kGateUnroll - 1) * stride < units; u += kGateUnroll * stride) {
+        Oct<E> xo[kGateUnroll], xg[kGateUnroll];
+#pragma unroll
+        for (int j = 0; j < kGateUnroll; ++j) {
+            const long e = (u + j * stride) * DV + 8 * sub;
+            xo[j] = Oct<E>::load(o + e);
+            xg[j] = Oct<E>::load(gate + e);
+        }
+#pragma unroll
+        for (int j = 0; j < kGateUnroll; ++j)
+            gate_unit<E, DV>(xo[j], xg[j], wv, eps, y + (u + j * stride) * DV + 8 * sub);
     }
-    if (u < units) {
+    for (; u < units; u += stride) {
         const long e0 = u * DV + 8 * sub;
         gate_unit<E, DV>(Oct<E>::load(o + e0), Oct<E>::load(gate + e0), wv, eps, y + e0);
     }

@@ -15,14 +15,14 @@
 // the two L2 norms, so it is bound by HBM traffic: every pre-activation is read
 // once (plus a 3-token halo per tile, served by L2) and every output written
 // once.  A workgroup of four wavefronts owns two heads (h0, h0 + 1) of one
-// sequence over a 64-token tile; every wavefront runs one kind of work on all
+// sequence over a kTT-token tile; every wavefront runs one kind of work on all
 // of its lanes (no divergent roles inside a wavefront), 4 channels per lane:
 //   wavefronts 0, 1: q (first dk/4 lanes) and k (next dk/4 lanes) of head
 //                    h0 + w: conv, Swish, then the L2 norm as a reduction over
 //                    the dk/4 lanes of the group;
 //   wavefront 2:     v of h0 (lanes 0..) and of h0 + 1 (lanes 32..): conv, Swish;
 //   wavefront 3:     the gate input z of h0 (lanes 0..) and h0 + 1 (lanes 32..);
-//   wavefronts 2, 3 also map beta of the tile's tokens (lane = token) for h0
+//   wavefronts 2, 3 also map beta of the tile's tokens (lane = token mod 64) for h0
 //                    and h0 + 1 respectively.
 // A conv lane walks the tile token by token keeping its last three inputs in
 // registers; loads run 8 tokens ahead.
@@ -32,7 +32,7 @@
 namespace kda {
 namespace {
 
-constexpr int kTT = 64;                  // tokens per tile
+constexpr int kTT = 256;                 // tokens per tile
 constexpr int kW = 4;                    // conv width
 constexpr int kU = 8;                    // tokens loaded ahead
 constexpr float kL2Eps = 1e-6f;
@@ -171,9 +171,11 @@ __global__ __launch_bounds__(256) void prep_kernel(
     // ---- beta = Sigmoid(logit): wavefront 2 for h0, 3 for h0 + 1, lane = token --
     if (wave >= 2) {
         const int hb = 2 * blockIdx.y + wave - 2;
-        if (hb < H && lane < n) {
-            const long r = (tokb + t0 + lane) * H + hb;
-            beta[r] = (E)sigmoid_f(to_f(beta_logit[r]));
+        if (hb < H) {
+            for (int tt = lane; tt < n; tt += 64) {
+                const long r = (tokb + t0 + tt) * H + hb;
+                beta[r] = (E)sigmoid_f(to_f(beta_logit[r]));
+            }
         }
     }
 

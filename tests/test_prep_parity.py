@@ -46,7 +46,7 @@ def _gpu(x, **kw):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("T,history", [(200, True), (131, False), (2, True), (64, True)])
+@pytest.mark.parametrize("T,history", [(200, True), (131, False), (2, True), (64, True), (600, True)])
 def test_prep_small(gpu, dtype, dk, dv, T, history):
     """Several 64-token tiles with a ragged tail, T shorter than the conv history, and an
     exact tile; with and without a caller-given history."""
