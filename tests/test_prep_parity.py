@@ -46,10 +46,12 @@ def _gpu(x, **kw):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-@pytest.mark.parametrize("T,history", [(200, True), (131, False), (2, True), (64, True), (600, True)])
+@pytest.mark.parametrize("T,history", [(200, True), (131, False), (2, True), (64, True), (600, True),
+                                       (512, False)])
 def test_prep_small(gpu, dtype, dk, dv, T, history):
-    """Several 64-token tiles with a ragged tail, T shorter than the conv history, and an
-    exact tile; with and without a caller-given history."""
+    """The kernel's 256-token tiles: one partial tile (200, 131, 64), T shorter than the conv
+    history (2), three tiles with a ragged tail (600) and two exact tiles (512); with and
+    without a caller-given history."""
     spec = PrepSpec(B=2, T=T, H=3, dk=dk, dv=dv, dtype=dtype, seed=100 + T, history=history)
     x = prep_inputs(spec, device=gpu)
     out = _gpu(x)
