@@ -43,6 +43,15 @@ def test_decode_small(gpu, dtype, dk, dv):
     print(f"decode {dtype} dk{dk} dv{dv}: err_o {w[0]:.2e} err_S {w[1]:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("N,H", [(1, 1), (1, 2), (3, 1)])
+def test_decode_tiny_batches(gpu, N, H):
+    """One or a few (sequence, head) pairs: workgroups hold two, so a single pair leaves the
+    only workgroup's second slot spare."""
+    spec = DecodeSpec(N=N, H=H, dk=128, dv=128, steps=3, seed_base=80 + 10 * N + H, state_seed=81)
+    w = _run_steps(spec, gpu, 3)
+    print(f"decode N{N} H{H}: err_o {w[0]:.2e} err_S {w[1]:.2e}", flush=True)
+
+
 def test_decode_long_memory(gpu):
     """g close to 0: the carried state dominates."""
     spec = DecodeSpec(N=8, H=96, dk=128, dv=128, steps=16, gate="long", seed_base=60, state_seed=61)
