@@ -2,25 +2,31 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 
-Two timed phases, each W untimed steps then K timed steps bracketed by
+Timed phases, each W untimed steps then K timed steps bracketed by
 torch.cuda.synchronize():
   prefill  one kda_chunk_fwd over the K3-shaped layer: B=1, H=96, T=65536,
-           dk=dv=128, bf16 inputs, fp32 state, chunk 16, 10 % of tokens at
-           g = -4.99 (the headline: `value` is its tokens/s);
+           dk=dv=128, bf16 inputs, fp32 state, 10 % of tokens at g = -4.99
+           (the headline: `value` is its tokens/s);
+  configs  the other prefill configurations: B=4, H=32, T=4096 (under
+           "configs.prefill_b4h32") and the 1,048,576-token stream of 16 K3-shaped
+           segments with the state carried in place ("configs.stream_1m": the
+           sum of the 16 launch times, each segment's inputs drawn untimed);
   decode   one kda_decode_step over N=256 sequences x H=96 heads, dk=dv=128,
-           bf16, ShortConv width 4 (reported under "decode").
-A third phase (reported under "snapshots") times kda_chunk_fwd_snapshots on the
-prefill workload with a state snapshot every 512 tokens (128 snapshots), and a
-fourth (reported under "prep") kda_prefill_prep on the same B=1, H=96, T=65536
-shape: projected pre-activations to q, k, v, g, beta.  A fifth (reported under
-"gate") times kda_output_gate on the prefill output shape (65536 tokens x 96
-heads x 128, bf16), and a sixth (under "decode_gated") kda_decode_step_gated on
-the decode batch.  A seventh (under "bwd") times kda_chunk_bwd, the backward
-pass, on the B=4, H=32, T=4096, dk=dv=128 bf16 prefill shape (gradients fp32).
+           bf16, ShortConv width 4 (reported under "decode");
+  snapshots  kda_chunk_fwd_snapshots on the prefill workload with a state
+           snapshot every 512 tokens (128 snapshots);
+  prep     kda_prefill_prep on the same B=1, H=96, T=65536 shape: projected
+           pre-activations to q, k, v, g, beta;
+  gate     kda_output_gate on the prefill output shape (65536 tokens x 96 heads
+           x 128, bf16), and kda_decode_step_gated on the decode batch (under
+           "decode.gated");
+  bwd      kda_chunk_bwd, the backward pass, on the B=4, H=32, T=4096,
+           dk=dv=128 bf16 prefill shape (gradients fp32).
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
-launched on.  The CPU baseline times the fp64 oracle on a bounded sample of the
-prefill workload on the host cores.
+launched on.  The CPU baselines time the fp64 oracle (as it stands) on the host
+cores: the whole K3-shaped prefill (cpu_baseline), the whole B4 H32 T4096
+prefill, and a sample of the decode batch; each records the host it ran on.
 
 Prints one JSON line.
 """
@@ -132,35 +138,89 @@ def _timed(fn, steps, warmup, torch):
     return wall, kern
 
 
-def cpu_baseline(x, H_total, heads=96, tokens=65536):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the prefill workload:
-    the first `heads` heads of the generated K3-shaped inputs over `tokens` tokens."""
-    import oracle
-    from gated_delta_rule_18_amd.inputs import to_f64
-    tokens = min(tokens, x["q"].shape[1])
-    heads = min(heads, x["q"].shape[2])
-    sl = lambda t: to_f64(t[:, :tokens, :heads].contiguous())
-    args = [sl(x[n]) for n in ("q", "k", "v", "g", "beta")] + [to_f64(x["S0"][:, :heads].contiguous())]
-    nthreads = oracle.default_threads()
+def host_description():
+    """The host the CPU baseline runs on: logical CPU count, the CPUs this process may
+    use, and the CPU model."""
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    nthreads = max(1, min(nthreads, avail))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "affinity": avail, "model": model}
+
+
+def oracle_threads():
+    """Threads for the oracle: every CPU this process may use, at most 16 (the host CPU
+    share that goes with one GPU on the benchmark machines)."""
+    return max(1, min(16, host_description()["affinity"]))
+
+
+def cpu_baseline(x, H_total, heads=96, tokens=65536, label="K3-shaped"):
+    """Time the fp64 oracle (as it stands) on a bounded sample of a prefill workload:
+    the first `heads` heads of the generated inputs over `tokens` tokens."""
+    import oracle
+    from gated_delta_rule_18_amd.inputs import to_f64
+    tokens = min(tokens, x["q"].shape[1])
+    heads = min(heads, x["q"].shape[2])
+    B = x["q"].shape[0]
+    sl = lambda t: to_f64(t[:, :tokens, :heads].contiguous())
+    S0 = None if x["S0"] is None else to_f64(x["S0"][:, :heads].contiguous())
+    args = [sl(x[n]) for n in ("q", "k", "v", "g", "beta")] + [S0]
+    nthreads = oracle_threads()
+    dk, dv = x["q"].shape[-1], x["v"].shape[-1]
     t0 = time.perf_counter()
     oracle.prefill(*args, nthreads=nthreads)
     dt = time.perf_counter() - t0
-    token_heads = heads * tokens
+    token_heads = B * heads * tokens
+    host = host_description()
     return {
         "value": token_heads / dt / H_total,
         "unit": "tokens/s",
         "cores": nthreads,
         "kind": "oracle",
-        "sample": (f"fp64 oracle on {nthreads} threads: prefill of {heads} of {H_total} heads x {tokens} "
-                   f"tokens (d=128) of the same K3-shaped inputs, {dt:.2f} s; value = token-heads/s / "
-                   f"{H_total}, i.e. layer tokens/s"),
+        "sample": (f"fp64 oracle on {nthreads} threads: prefill of B{B} x {heads} of {H_total} heads x "
+                   f"{tokens} tokens (dk={dk}, dv={dv}) of the same {label} inputs, {dt:.2f} s; "
+                   f"value = token-heads/s / {H_total}, i.e. layer tokens/s"),
         "seconds": dt,
-        "gflops_fp64": token_heads * 7 * 128 * 128 / dt / 1e9,
+        "gflops_fp64": token_heads * 7 * dk * dv / dt / 1e9,
+        "host": host,
+    }
+
+
+def cpu_baseline_decode(ds, st, steps_in, seqs=32):
+    """Time the fp64 oracle's decode step on a bounded sample of the decode batch: the
+    first `seqs` sequences (all heads) over every prepared step."""
+    import numpy as np
+
+    import oracle
+    from gated_delta_rule_18_amd.inputs import to_f64
+    seqs = min(seqs, ds.N)
+    S = np.ascontiguousarray(to_f64(st["S"][:seqs]))
+    cache = np.ascontiguousarray(to_f64(st["conv_cache"][:seqs]))
+    w = to_f64(st["conv_w"])
+    ins = [{n: to_f64(d[n][:seqs]) for n in ("q_pre", "k_pre", "v_pre", "g", "beta")} for d in steps_in]
+    nthreads = oracle_threads()
+    t0 = time.perf_counter()
+    for i, d in enumerate(ins):
+        oracle.decode_step(d["q_pre"], d["k_pre"], d["v_pre"], w, cache, i, d["g"], d["beta"], S,
+                           nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": seqs * len(ins) / dt,
+        "unit": "tokens/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on {nthreads} threads: {len(ins)} decode steps of {seqs} of {ds.N} sequences "
+                   f"x {ds.H} heads, {dt:.2f} s; value = sequence-steps/s (one token per sequence)"),
+        "seconds": dt,
     }
 
 
@@ -176,6 +236,8 @@ def main():
     ap.add_argument("--skip-prep", action="store_true")
     ap.add_argument("--skip-gate", action="store_true")
     ap.add_argument("--skip-bwd", action="store_true")
+    ap.add_argument("--skip-configs", action="store_true",
+                    help="skip the B4 H32 T4096 prefill and the 1M-token streaming legs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -188,7 +250,7 @@ def main():
     import torch
 
     from gated_delta_rule_18_amd import binding
-    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, WORKLOADS, backward_inputs,
+    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, STREAM_1M, WORKLOADS, backward_inputs,
                                                 decode_gate_inputs,
                                                 decode_state, decode_step_inputs, gate_inputs,
                                                 prefill_inputs, prep_inputs)
@@ -249,6 +311,73 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(x, H)
     del x, o
 
+    # ---------------- the other prefill configurations ------------------------------
+    configs = None
+    if not args.skip_configs:
+        configs = {}
+        # B4 H32 T4096: 256 workgroups, every CU busy
+        c2 = WORKLOADS["prefill_b4h32"]
+        x2 = prefill_inputs(c2, device=dev)
+        o2 = torch.empty((c2.B, c2.T, c2.H, c2.dv), dtype=torch.bfloat16, device=dev)
+        s2 = torch.empty((c2.B, c2.H, c2.dk, c2.dv), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def c2_step(i=0):
+            binding.chunk_fwd(x2["q"], x2["k"], x2["v"], x2["g"], x2["beta"], x2["S0"], chunk=C, o=o2, S_T=s2)
+
+        w2, k2 = _timed(c2_step, args.steps, args.warmup, torch)
+        b2 = prefill_bytes(c2.B, c2.T, c2.H, c2.dk, c2.dv)
+        configs["prefill_b4h32"] = {
+            "workload": f"prefill B{c2.B} H{c2.H} T{c2.T} dk=dv={c2.dk} bf16 chunk{C}",
+            "ms_per_step": w2, "kernel_ms": k2, "tokens_per_s": c2.B * c2.T / (w2 * 1e-3),
+            "tflops": prefill_flops(c2.B, c2.T, c2.H, c2.dk, c2.dv, C) / (k2 * 1e-3) / 1e12,
+            "roofline": {"bound": "hbm", "achieved": b2 / (k2 * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": b2 / (k2 * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                         "bytes_per_launch": b2},
+        }
+        if not args.no_cpu:
+            configs["prefill_b4h32"]["cpu_baseline"] = cpu_baseline(x2, c2.H, heads=c2.H, tokens=c2.T,
+                                                                    label="B4 H32 T4096")
+        del x2, o2, s2
+        # 1,048,576 tokens as 16 segments of the K3 shape, the state carried in place;
+        # each segment's inputs are drawn (untimed) before its launch, the kernel time
+        # is the sum of the 16 launches
+        base, nseg = STREAM_1M["base"], STREAM_1M["segments"]
+        S = None
+        o4 = torch.empty((base.B, base.T, base.H, base.dv), dtype=torch.bfloat16, device=dev)
+        seg_ms = []
+        for seg in range(-1, nseg):          # segment -1: an untimed warm-up
+            xs = prefill_inputs(base, device=dev, seed=STREAM_1M["seed_base"] + max(seg, 0))
+            if S is None or seg == 0:
+                S = xs["S0"].clone()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            binding.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], S, chunk=C, o=o4, S_T=S)
+            e1.record()
+            torch.cuda.synchronize()
+            if seg >= 0:
+                seg_ms.append(e0.elapsed_time(e1))
+            del xs
+        tot = sum(seg_ms)
+        b4 = nseg * prefill_bytes(base.B, base.T, base.H, base.dk, base.dv)
+        configs["stream_1m"] = {
+            "workload": f"1M-token streaming prefill: {nseg} x (B{base.B} H{base.H} T{base.T}) segments, "
+                        f"state carried in place, bf16 chunk{C}",
+            "kernel_ms": tot, "segment_ms": [round(t, 4) for t in seg_ms],
+            "tokens_per_s": nseg * base.B * base.T / (tot * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": b4 / (tot * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": b4 / (tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                         "bytes_per_launch": b4 // nseg},
+        }
+        if cpu is not None:
+            configs["stream_1m"]["cpu_baseline"] = {
+                "value": cpu["value"], "unit": "tokens/s", "cores": cpu["cores"], "kind": "oracle",
+                "sample": "one K3-shaped segment (the headline cpu_baseline); the 16 segments of the "
+                          "stream are the same work 16 times, so the rate is the same",
+                "extrapolated_seconds": nseg * cpu["seconds"]}
+        del o4, S
+
     # ---------------- decode ---------------------------------------------------
     decode = None
     if not args.skip_decode:
@@ -267,6 +396,7 @@ def main():
             pos[0] += 1
 
         d_wall, d_kern = _timed(decode_step, args.steps, args.warmup, torch)
+        d_cpu = None if args.no_cpu else cpu_baseline_decode(ds, st, steps_in[:8])
         d_bytes = decode_bytes(ds.N, ds.H, ds.dk, ds.dv, ds.width)
         d_gbps = d_bytes / (d_kern * 1e-3) / 1e9
         decode = {
@@ -281,6 +411,8 @@ def main():
                                                      ["kda_decode.hip", "kda_device.h"]),
                          "bytes_per_launch": d_bytes},
         }
+        if d_cpu is not None:
+            decode["cpu_baseline"] = d_cpu
         # the same step with the output exposure gate fused (y written in place of o)
         if not args.skip_gate:
             gates = [decode_gate_inputs(ds, s % ds.steps, device=dev) for s in range(len(steps_in))]
@@ -426,6 +558,7 @@ def main():
         "prep": prep,
         "gate": gate,
         "bwd": bwd,
+        "configs": configs,
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu

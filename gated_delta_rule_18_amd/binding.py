@@ -4,8 +4,8 @@ Every step of the computation runs in the library's HIP kernels; torch is used
 for device memory and for the current HIP stream.  If the library is missing
 the calls raise (there is no fallback).
 
-    o, S_T        = chunk_fwd(q, k, v, g, beta, S0=None, chunk=16)
-    o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=16)
+    o, S_T        = chunk_fwd(q, k, v, g, beta, S0=None, chunk=64)
+    o, S_T, snaps = chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=64)
     o             = decode_step(q_pre, k_pre, v_pre, conv_w, conv_cache, conv_pos, g, beta, S)
     q, k, v, g, beta, conv_final = prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A,
                                                 beta_logit)
@@ -27,11 +27,17 @@ library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_snapshots",
+EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
+           "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
            "kda_validate_inputs", "kda_version")
 
 _lib = None
+
+
+class FwdOptions(ctypes.Structure):
+    """struct kda_fwd_options of kda.h."""
+    _fields_ = [("spin_limit", ctypes.c_int)]
 
 
 class KdaError(RuntimeError):
@@ -53,6 +59,8 @@ def lib():
         L.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 7 + [vp]
         L.kda_chunk_fwd_snapshots.restype = i
         L.kda_chunk_fwd_snapshots.argtypes = [vp] * 9 + [i] * 9 + [vp]
+        L.kda_chunk_fwd_ex.restype = i
+        L.kda_chunk_fwd_ex.argtypes = [vp] * 9 + [i] * 9 + [ctypes.POINTER(FwdOptions), vp]
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
         L.kda_decode_step_gated.restype = i
@@ -114,22 +122,25 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def chunk_fwd(q, k, v, g, beta, S0=None, chunk=16, o=None, S_T=None, return_state=True):
+def chunk_fwd(q, k, v, g, beta, S0=None, chunk=64, o=None, S_T=None, return_state=True, spin_limit=None):
     """Chunkwise prefill.  q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H];
     S0 [B,H,dk,dv] fp32 or None.  Returns (o [B,T,H,dv], S_T [B,H,dk,dv] fp32 or None).
-    S_T may be passed as S0 itself for in-place streaming over segments."""
-    o, S_T, _ = _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, None, 0, 0)
+    S_T may be passed as S0 itself for in-place streaming over segments.  Every chunk
+    size (16, 32, 64) gives the same bits.  spin_limit (testing): see kda_chunk_fwd_ex."""
+    o, S_T, _ = _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, None, 0, 0, spin_limit)
     return o, S_T
 
 
-def chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=16, o=None, S_T=None,
-                        snaps=None, return_state=True):
+def chunk_fwd_snapshots(q, k, v, g, beta, S0, snap_every, n_snaps, chunk=64, o=None, S_T=None,
+                        snaps=None, return_state=True, spin_limit=None):
     """chunk_fwd that also returns snaps [n_snaps,B,H,dk,dv] fp32: snapshot s is the
     state after the first (s+1)*snap_every tokens (snap_every a multiple of chunk)."""
-    return _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps)
+    return _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps,
+                      spin_limit)
 
 
-def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps):
+def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_every, n_snaps,
+               spin_limit=None):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -151,7 +162,12 @@ def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_ev
         snaps = torch.empty((n_snaps, B, H, dk, dv), dtype=torch.float32, device=dev)
     elif snaps is not None:
         _want(snaps, "snaps", (n_snaps, B, H, dk, dv), torch.float32, dev)
-    if n_snaps or snaps is not None:
+    if spin_limit is not None:
+        opts = FwdOptions(spin_limit=int(spin_limit))
+        rc = lib().kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                    _ptr(S_T), _ptr(snaps), int(snap_every), int(n_snaps), B, T, H, dk, dv,
+                                    code, int(chunk), ctypes.byref(opts), _stream(dev))
+    elif n_snaps or snaps is not None:
         rc = lib().kda_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
                                            _ptr(o), _ptr(S_T), _ptr(snaps), int(snap_every), int(n_snaps),
                                            B, T, H, dk, dv, code, int(chunk), _stream(dev))

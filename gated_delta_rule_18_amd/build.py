@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kda_prefill.hip", "kda_prefill_ws.hip", "kda_decode.hip", "kda_prep.hip", "kda_gate.hip",
+SOURCES = ["kda_prefill_ws.hip", "kda_decode.hip", "kda_prep.hip", "kda_gate.hip",
            "kda_bwd.hip", "kda_validate.hip", "kda_api.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", CSRC, "-I", INCLUDE,
           "-Wall", "-Wno-unused-command-line-argument",

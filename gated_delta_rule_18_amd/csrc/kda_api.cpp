@@ -9,6 +9,12 @@
 
 namespace {
 
+// Largest batch or head count (each), and largest number of (sequence, head)
+// pairs, of one prefill, preprocessing or backward call: grids and per-head
+// byte strides stay inside 32-bit ranges.
+constexpr int kMaxBH = 65535;
+constexpr long long kMaxHeads = 1LL << 24;
+
 bool aligned16(const void *p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
 bool head_ok(int d) { return d == 64 || d == 128; }
 
@@ -20,7 +26,7 @@ bool overlap(const void *a, long long na, const void *b, long long nb)
 
 int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
               const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv, int dtype,
-              int chunk, const kda::Snapshots &snap, void *stream)
+              int chunk, const kda::Snapshots &snap, const kda::FwdOptions &opt, void *stream)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return KDA_ERR_INVALID;
@@ -30,6 +36,9 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
         return KDA_ERR_INVALID;
     if (!head_ok(dk) || !head_ok(dv))
         return KDA_ERR_UNSUPPORTED;
+    // index ranges of the kernel: 32-bit grids and per-head byte strides
+    if (B > kMaxBH || H > kMaxBH || (long long)B * H > kMaxHeads)
+        return KDA_ERR_INVALID;
     if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40))
         return KDA_ERR_INVALID;
     const bool has_tokens = (long long)B * T * H > 0;
@@ -53,17 +62,14 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
         if (overlap(snap.out, snap_bytes, S0, state_bytes) || overlap(snap.out, snap_bytes, S_T, state_bytes))
             return KDA_ERR_INVALID;
     }
-    // chunk 64 runs the 16-token kernel: the chunk size only changes how the same
-    // map is blocked, and that kernel's chunk is already the 16-position tile in
-    // which every decay factor stays bounded.  Snapshot spacing in its chunks.
+    // Every chunk size runs the 16-token kernel: the chunk size only changes how
+    // the same map is blocked, and a 16-token chunk is already the 16-position
+    // tile in which every decay factor stays bounded.  Snapshot spacing in its
+    // chunks.
     kda::Snapshots ks = snap;
-    int kchunk = chunk;
-    if (chunk == 64) {
-        kchunk = 16;
-        ks.every_chunks = snap.every_chunks * 4;
-    }
+    ks.every_chunks = snap.every_chunks * (chunk / 16);
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
-                                         dtype == KDA_FP32, kchunk, ks,
+                                         dtype == KDA_FP32, ks, opt,
                                          reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -124,13 +130,22 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g, co
                   int dtype, int chunk, void *stream)
 {
     return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, kda::Snapshots{},
-                     stream);
+                     kda::FwdOptions{}, stream);
 }
 
 int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *S0, void *o, float *S_T, float *snaps,
                             int snap_every, int n_snaps, int B, int T, int H, int dk, int dv,
                             int dtype, int chunk, void *stream)
+{
+    return kda_chunk_fwd_ex(q, k, v, g, beta, S0, o, S_T, snaps, snap_every, n_snaps, B, T, H, dk, dv,
+                            dtype, chunk, nullptr, stream);
+}
+
+int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                     const float *S0, void *o, float *S_T, float *snaps, int snap_every, int n_snaps,
+                     int B, int T, int H, int dk, int dv, int dtype, int chunk,
+                     const kda_fwd_options *opts, void *stream)
 {
     if (n_snaps < 0 || (n_snaps > 0 && (snap_every <= 0 || chunk <= 0 || snap_every % chunk != 0)))
         return KDA_ERR_INVALID;
@@ -142,7 +157,13 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const v
         snap.every_chunks = snap_every / chunk;
         snap.count = n_snaps;
     }
-    return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, snap, stream);
+    kda::FwdOptions opt;
+    if (opts) {
+        if (opts->spin_limit < -1)
+            return KDA_ERR_INVALID;
+        opt.spin_limit = opts->spin_limit;
+    }
+    return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, snap, opt, stream);
 }
 
 int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
@@ -241,8 +262,8 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, co
         return KDA_ERR_INVALID;
     if (!head_ok(dk_size) || !head_ok(dv_size))
         return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * T * H * (dk_size > dv_size ? dk_size : dv_size) > (1LL << 40) || B > 65535 ||
-        H > 65535)
+    if ((long long)B * T * H * (dk_size > dv_size ? dk_size : dv_size) > (1LL << 40) || B > kMaxBH ||
+        H > kMaxBH || (long long)B * H > kMaxHeads)
         return KDA_ERR_INVALID;
     if ((long long)B * H == 0)
         return KDA_OK;
@@ -294,7 +315,8 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, co
         return KDA_ERR_INVALID;
     if (!head_ok(dk) || !head_ok(dv))
         return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40) || B > 65535 || H > 65535)
+    if ((long long)B * T * H * (dk > dv ? dk : dv) > (1LL << 40) || B > kMaxBH || H > kMaxBH ||
+        (long long)B * H > kMaxHeads)
         return KDA_ERR_INVALID;
     if ((long long)B * H == 0)
         return KDA_OK;

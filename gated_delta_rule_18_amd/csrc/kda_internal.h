@@ -19,16 +19,25 @@ struct Snapshots {
     bool packed = false;
 };
 
+// Knobs of a prefill launch that callers other than tests leave at their
+// defaults.  spin_limit: polls before an internal hand-off wait gives up and the
+// workgroup marks its results NaN (< 0 = the built-in limit).
+struct FwdOptions {
+    int spin_limit = -1;
+};
+
+// Every chunk size the C ABI accepts runs the 16-token kernel
+// (kda_prefill_ws.hip); snap.every_chunks counts 16-token chunks.
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                             const void *beta, const float *S0, void *o, float *S_T,
-                            int B, int T, int H, int dk, int dv, bool fp32, int chunk,
-                            const Snapshots &snap, hipStream_t stream);
+                            int B, int T, int H, int dk, int dv, bool fp32,
+                            const Snapshots &snap, const FwdOptions &opt, hipStream_t stream);
 
-// chunk = 16: the warp-specialised kernel (kda_prefill_ws.hip)
+// The 16-token kernel itself (T > 0, B*H > 0).
 hipError_t launch_chunk16(const void *q, const void *k, const void *v, const void *g,
                           const void *beta, const float *S0, void *o, float *S_T,
                           int B, int T, int H, int dk, int dv, bool fp32, const Snapshots &snap,
-                          hipStream_t stream);
+                          hipStream_t stream, int spin_limit = -1);
 
 // Debug check of the value domains: report (device int64[4]) receives the number
 // of g outside [-5, 0] (or NaN), the first such flat index (-1 if none), and the

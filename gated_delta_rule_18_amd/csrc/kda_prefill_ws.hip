@@ -43,7 +43,10 @@
 //                      only, so more chunks are in flight at once.
 // Producers and consumers hand slots over through per-slot LDS flags ("ready"
 // and per-consumer "done"); every wait is bounded and a WG-wide abort flag ends
-// all waits if one ever runs out (the result is then wrong, never a hang).
+// all waits if one ever runs out.  The kernel then still finishes, and it marks
+// what it could not compute: the consumers write NaN in place of every o tile
+// from the chunk at which they saw the abort on, and in place of the head
+// slice's S_T (and any later snapshot).
 //
 // Instruction economy.  One wavefront issues at most one instruction every few
 // cycles, so the consumer's per-chunk instruction count bounds the state chain:
@@ -62,7 +65,7 @@ template <typename E> struct Np { static constexpr int v = sizeof(E) == 2 ? 8 : 
 constexpr int kC = 16;                 // tokens per chunk
 constexpr int kVS = 64;                // value columns per workgroup
 constexpr int kXCDs = 8;
-constexpr int kSpinLimit = 1 << 22;
+constexpr int kSpinLimit = 1 << 22;     // polls before a hand-off wait gives up
 // s_waitcnt operand: vector-memory count 0, the other counters unconstrained
 constexpr int kVmcntZero = 0x0F70;
 
@@ -127,8 +130,11 @@ __device__ __forceinline__ void st_flag(int *f, int v)
 }
 
 // Wait until every flag f[i * stride], i < n, is >= target.  Bounded: after
-// kSpinLimit polls the WG abort flag is raised and all later waits return.
-__device__ __forceinline__ void wait_flags(const int *f, int n, int stride, int target, int *abort_flag)
+// spin_limit polls the WG abort flag is raised and all later waits return.
+// Returns whether the workgroup has aborted (read after the flags, so an abort
+// raised before a flag was published is always seen).
+__device__ __forceinline__ bool wait_flags(const int *f, int n, int stride, int target, int *abort_flag,
+                                           int spin_limit)
 {
     int spins = 0;
     for (;;) {
@@ -137,13 +143,15 @@ __device__ __forceinline__ void wait_flags(const int *f, int n, int stride, int 
             ok = ok && ld_flag(f + i * stride) >= target;
         if (ok || ld_flag(abort_flag))
             break;
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
+        if (++spins > spin_limit) {
             st_flag(abort_flag, 1);
             break;
         }
+        __builtin_amdgcn_s_sleep(1);
     }
+    const bool aborted = ld_flag(abort_flag) != 0;
     lds_fence();
+    return aborted;
 }
 
 // A volatile LDS read (never fused with a neighbouring read into a wider one).
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
     float *S_T, float *snaps, int snap_chunks, int n_snaps, int snap_packed, int T, int H, int DV, int nbh,
-    int nsl)
+    int nsl, int spin_limit)
 {
     typedef WsL<E, DK> L;
     typedef typename Vec<E>::v4 V4;
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         auto rd8 = [&](int s, int off) { return lds_load<V8>(smem + L::oSlots + s * L::slotBytes + off); };
         auto rd4 = [&](int s, int off) { return lds_load<V4>(smem + L::oSlots + s * L::slotBytes + off); };
         auto fetch = [&](Ops &op, int s, int c) {
-            wait_flags(ready + s, 1, 1, c + 1, abort_flag);
+            const bool ab = wait_flags(ready + s, 1, 1, c + 1, abort_flag, spin_limit);
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
                 op.kt[m] = rd8(s, laA + (L::eKt + m * L::MS) * L::ES);
@@ -496,6 +504,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             for (int ct = 0; ct < NCT; ++ct)
                 op.kr[ct] = low(rd4(s, laB + (L::eKe + L::tile(ct)) * L::ES), op.kr[ct]);
             op.gp = lds_load<f32x2>(smem + L::oSlots + s * L::slotBytes + laC);
+            return ab;
         };
 
         Ops op;
@@ -521,8 +530,12 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             snap_dst += snap_step;
         }
         int s = 0;                                        // slot of chunk c
+        // set once a hand-off wait of this workgroup gave up: from then on the
+        // results are marked (NaN) instead of written
+        bool aborted = false;
+        const f32x4 nan4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         if (nchunks > 0)
-            fetch(op, 0, 0);
+            aborted = fetch(op, 0, 0);
         for (int c = 0; c < nchunks; ++c) {
             // S strip as B operands; contraction slice m holds channels
             // {32m + 4 g4 + e, 32m + 16 + 4 g4 + e}, e = 0..3
@@ -557,10 +570,14 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                 if (--snap_left == 0) {
                     snap_left = snap_chunks;
                     if (snap_idx < n_snaps) {
+                        f32x4 Sout[NCT];
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            Sout[ct] = aborted ? nan4 : Sacc[ct];
                         if (snap_packed)
-                            store_state_packed(reinterpret_cast<E *>(snap_dst), Sacc, lane_poff, DV);
+                            store_state_packed(reinterpret_cast<E *>(snap_dst), Sout, lane_poff, DV);
                         else
-                            store_state(reinterpret_cast<float *>(snap_dst), Sacc, lane_soff, DV);
+                            store_state(reinterpret_cast<float *>(snap_dst), Sout, lane_soff, DV);
                     }
                     ++snap_idx;
                     snap_dst += snap_step;
@@ -572,13 +589,20 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             st_flag(done + s * 4 + w, c + 1);
             s = s + 1 == NS ? 0 : s + 1;
             if (c + 1 < nchunks)
-                fetch(op, s, c + 1);
+                aborted |= fetch(op, s, c + 1);
+            else
+                aborted |= ld_flag(abort_flag) != 0;
             const __amdgpu_buffer_rsrc_t ro = buffer(o ? o + ooff : o, c + 1 < nchunks ? ofull : olast);
-            store_o(ro, ovo, rso, O, (E *)nullptr);
+            store_o(ro, ovo, rso, aborted ? nan4 : O, (E *)nullptr);
             ooff += ostep;
         }
-        if (S_T)
+        if (S_T) {
+            aborted |= ld_flag(abort_flag) != 0;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                Sacc[ct] = aborted ? nan4 : Sacc[ct];
             store_state(S_T + (long)bh * DK * DV, Sacc, lane_soff, DV);
+        }
         return;
     }
 
@@ -691,7 +715,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
 
         // ---- claim the slot, then write the consumers' operand images ----------
         if (c >= NS)
-            wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag);
+            wait_flags(done + s * 4, 4, 1, c - NS + 1, abort_flag, spin_limit);
         // while it holds the slot the producer issues ahead of the other producer
         // on its SIMD (still behind the consumer): the time a slot is held bounds
         // how many chunks are in flight
@@ -830,39 +854,65 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
 template <typename E, int DK>
 hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g, const void *beta,
                      const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
-                     const Snapshots &snap, hipStream_t stream)
+                     const Snapshots &snap, int spin_limit, hipStream_t stream)
 {
     typedef WsL<E, DK> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     constexpr int lds = L::bytes > 81 * 1024 ? L::bytes : 81 * 1024;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    // a per-device function attribute: set on every call (cheap, and correct
+    // whichever device and thread the call comes from)
+    hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess)
+        return e;
     const int nbh = B * H, nsl = dv / kVS;
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(64 * (4 + L::NP)), lds, stream,
                        (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
                        (E *)o, S_T, snap.count > 0 || snap.packed ? snap.out : nullptr, snap.every_chunks,
-                       snap.count, snap.packed ? 1 : 0, T, H, dv, nbh, nsl);
+                       snap.count, snap.packed ? 1 : 0, T, H, dv, nbh, nsl,
+                       spin_limit < 0 ? kSpinLimit : spin_limit);
     return hipGetLastError();
+}
+
+// T == 0: S_T = S0 (or 0).  One thread per state element.
+__global__ void copy_state_kernel(const float *S0, float *S_T, long n)
+{
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        S_T[i] = S0 ? S0[i] : 0.f;
 }
 
 } // namespace
 
 hipError_t launch_chunk16(const void *q, const void *k, const void *v, const void *g,
                           const void *beta, const float *S0, void *o, float *S_T, int B, int T,
-                          int H, int dk, int dv, bool fp32, const Snapshots &snap, hipStream_t stream)
+                          int H, int dk, int dv, bool fp32, const Snapshots &snap, hipStream_t stream,
+                          int spin_limit)
 {
     if (fp32)
-        return dk == 128 ? launch_ws<float, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream)
-                         : launch_ws<float, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
-    return dk == 128 ? launch_ws<__bf16, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream)
-                     : launch_ws<__bf16, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, stream);
+        return dk == 128 ? launch_ws<float, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream)
+                         : launch_ws<float, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream);
+    return dk == 128 ? launch_ws<__bf16, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream)
+                     : launch_ws<__bf16, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream);
+}
+
+hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                            const void *beta, const float *S0, void *o, float *S_T, int B, int T,
+                            int H, int dk, int dv, bool fp32, const Snapshots &snap,
+                            const FwdOptions &opt, hipStream_t stream)
+{
+    if ((long)B * H == 0)
+        return hipSuccess;
+    if (T == 0) {
+        if (!S_T || S_T == S0)
+            return hipSuccess;
+        const long n = (long)B * H * dk * dv;
+        hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           S0, S_T, n);
+        return hipGetLastError();
+    }
+    return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, snap, stream, opt.spin_limit);
 }
 
 } // namespace kda

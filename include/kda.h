@@ -21,7 +21,8 @@
  *     on different buffers are safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it; the call returns without synchronising.  Kernel
- *     faults surface on the stream, not in the return code.
+ *     faults surface on the stream, not in the return code; a prefill whose
+ *     internal hand-off gives up marks its outputs NaN (kda_chunk_fwd_ex).
  *   - dtype KDA_BF16: q, k, v, g, beta, o (and the decode conv cache) are
  *     bfloat16; the state is fp32.  dtype KDA_FP32 (test mode): every tensor is
  *     fp32.
@@ -40,7 +41,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 100 /* 1.0.0 */
+#define KDA_VERSION 110 /* 1.1.0 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -72,11 +73,16 @@ enum kda_status {
  *                                        S_T may equal S0 (in-place streaming over
  *                                        segments); any other overlap is invalid.
  *   dk, dv  : 64 or 128
- *   chunk   : 16, 32 or 64 tokens per chunk; every size gives the same result up
- *             to rounding (64 runs the 16-token kernel: the chunk size only
- *             changes the blocking of the same map)
+ *   B, H    : each at most 65535, and B*H at most 2^24
+ *   chunk   : 16, 32 or 64 tokens per chunk.  Every size runs the same kernel,
+ *             which works on 16-token chunks -- the 16-position tile of section
+ *             3.3 inside which every decay factor stays bounded -- so the
+ *             results are identical bit for bit; `chunk` only sets the unit of
+ *             snapshot spacing (kda_chunk_fwd_snapshots).
  * T may be any value >= 0 (a ragged last chunk is handled); T == 0 copies S0
  * to S_T (or zeroes S_T when S0 is NULL).
+ * The kernel's parts hand work to each other through bounded waits; should
+ * one ever give up, the affected outputs are NaN (see kda_chunk_fwd_ex).
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
                   const void *beta, const float *S0, void *o, float *S_T,
@@ -108,6 +114,34 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const v
                             float *snaps, int snap_every, int n_snaps,
                             int B, int T, int H, int dk, int dv, int dtype, int chunk,
                             void *stream);
+
+/*
+ * kda_chunk_fwd_ex -- kda_chunk_fwd_snapshots with the library's internal
+ * limits exposed; for tests and debugging.  (Same page, section 3.3, chunk
+ * interface; the options change no result, only how failures of the kernel's
+ * internal hand-offs are handled.)
+ *
+ * Arguments as kda_chunk_fwd_snapshots, plus
+ *   opts : NULL = defaults (what kda_chunk_fwd uses), else
+ *     spin_limit : number of polls after which a wait of one part of a
+ *                  workgroup for another gives up; -1 = the built-in limit
+ *                  (about 0.1 s of waiting, which normal operation never
+ *                  comes near), 0 = give up at the first unsatisfied poll.
+ * When a wait gives up the kernel does not hang: it finishes, and it writes NaN
+ * in place of the o rows of every chunk from the one at which the workgroup
+ * noticed on, of the (head, value slice)'s part of S_T, and of any snapshot
+ * taken after that point.  Values written before are exact results.
+ * Errors: as kda_chunk_fwd_snapshots; KDA_ERR_INVALID for spin_limit < -1.
+ */
+typedef struct kda_fwd_options {
+    int spin_limit;
+} kda_fwd_options;
+
+int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, const float *S0, void *o, float *S_T,
+                     float *snaps, int snap_every, int n_snaps,
+                     int B, int T, int H, int dk, int dv, int dtype, int chunk,
+                     const kda_fwd_options *opts, void *stream);
 
 /*
  * kda_decode_step -- one generated token of one KDA layer for N sequences.

@@ -14,8 +14,8 @@ chunk-relative cumulative log-decay G_r = sum_{s<=r} g_s,
     S_out  = Diag(exp(G_C)) S + (k*exp(G_C - G))^T U
 `ref` selects where each exp(G_r - G_i) is split into a row and a column factor:
     "direct"  -- the product is formed from the difference (no split),
-    "center"  -- split at the middle of the chunk, as the chunk-32 GPU kernel does
-                 (each factor then spans at most C/2 positions of decay),
+    "center"  -- split at the middle of the chunk (each factor then spans at most
+                 C/2 positions of decay),
     "start"   -- split at the chunk start, as the chunk-16 GPU kernel does (row
                  factor exp(G_r) <= 1, column factor exp(-G_i) <= e^{5 C}).
 `inverse` selects how (I + A)^{-1} is formed:
@@ -39,11 +39,11 @@ def nilpotent_inverse(A):
     return (I - A) @ (I + A2) @ (I + A4) @ (I + A8)
 
 
-def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve"):
+def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve", dtype=np.float64):
     T, dk = q.shape
     dv = v.shape[1]
-    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
-    o = np.zeros((T, dv))
+    S = np.zeros((dk, dv), dtype=dtype) if S0 is None else np.array(S0, dtype=dtype)
+    o = np.zeros((T, dv), dtype=dtype)
     for c0 in range(0, T, C):
         sl = slice(c0, min(T, c0 + C))
         qc, kc, vc, gc, bc = q[sl], k[sl], v[sl], g[sl], beta[sl]
@@ -71,7 +71,7 @@ def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve"):
         A = np.tril(bc[:, None] * KK, -1)
         M = np.tril(QK)
         if inverse == "solve":
-            Tm = np.linalg.solve(np.eye(n) + A, np.diag(bc))
+            Tm = np.linalg.solve(np.eye(n, dtype=A.dtype) + A, np.diag(bc))
         elif inverse == "product":
             Tm = nilpotent_inverse(A) @ np.diag(bc)
         else:
@@ -82,7 +82,8 @@ def chunk_forward(q, k, v, g, beta, S0, C, ref="direct", inverse="solve"):
     return o, S
 
 
-def chunk_backward(q, k, v, g, beta, S0, dO, dS_T, C, inverse="solve"):
+def chunk_backward(q, k, v, g, beta, S0, dO, dS_T, C, inverse="solve", dtype=np.float64,
+                   flush_subnormal=False):
     """Gradients of <dO, o> + <dS_T, S_T> through the chunk form above (one head),
     by reverse-mode differentiation of each chunk's matrix expressions, chunks in
     reverse order with the incoming state of each chunk from a forward pass.
@@ -91,17 +92,22 @@ def chunk_backward(q, k, v, g, beta, S0, dO, dS_T, C, inverse="solve"):
         A = strict_lower(Diag(beta) B), L = (I + A)^{-1}, Tm = L Diag(beta),
         X = V - Kt S, U = Tm X, M = lower(Qt Kc^T),
         O = Qt S + M U,  S' = Diag(Gam) S + Ke^T U.
-    Returns (dq, dk, dv, dg, dbeta, dS0) as float64 arrays."""
+    Returns (dq, dk, dv, dg, dbeta, dS0) as arrays of `dtype` (float64 by default; with
+    float32 every step rounds to float32).  flush_subnormal sets the Kt entries below the
+    smallest normal number of `dtype` to zero, as matrix units that flush sub-normal
+    operands see them."""
+    q, k, v, g, beta, dO = (np.asarray(x, dtype=dtype) for x in (q, k, v, g, beta, dO))
     T, dk = q.shape
     dv = v.shape[1]
-    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    S = np.zeros((dk, dv), dtype=dtype) if S0 is None else np.array(S0, dtype=dtype)
     starts = []                                   # incoming state of every chunk
     for c0 in range(0, T, C):
         starts.append(S.copy())
         sl = slice(c0, min(T, c0 + C))
-        _, S = chunk_forward(q[sl], k[sl], v[sl], g[sl], beta[sl], S, C, ref="direct", inverse=inverse)
+        _, S = chunk_forward(q[sl], k[sl], v[sl], g[sl], beta[sl], S, C, ref="direct", inverse=inverse,
+                             dtype=dtype)
     dq, dk_, dv_, dg, db = (np.zeros_like(x) for x in (q, k, v, g, beta))
-    dSn = np.array(dS_T, dtype=np.float64)        # gradient w.r.t. the chunk's outgoing state
+    dSn = np.array(dS_T, dtype=dtype)             # gradient w.r.t. the chunk's outgoing state
     for ci in range(len(starts) - 1, -1, -1):
         c0 = ci * C
         sl = slice(c0, min(T, c0 + C))
@@ -112,9 +118,13 @@ def chunk_backward(q, k, v, g, beta, S0, dO, dS_T, C, inverse="solve"):
         P = np.exp(G)
         Gam = P[-1]
         Kt, Qt, Kc, Ke = kc * P, qc * P, kc / P, kc * (Gam / P)
+        if flush_subnormal:
+            tiny = np.finfo(dtype).tiny
+            Kt = np.where(np.abs(Kt) < tiny, 0, Kt).astype(dtype)
         B = Kt @ Kc.T
         A = np.tril(bc[:, None] * B, -1)
-        L = np.linalg.solve(np.eye(n) + A, np.eye(n)) if inverse == "solve" else nilpotent_inverse(A)
+        I = np.eye(n, dtype=dtype)
+        L = np.linalg.solve(I + A, I) if inverse == "solve" else nilpotent_inverse(A)
         Tm = L * bc[None, :]
         X = vc - Kt @ S
         U = Tm @ X

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 100
+    assert binding.version() == 110
     L = binding.lib()
     for code in (0, -1, -2, -3, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
@@ -54,9 +54,42 @@ def _prefill(**kw):
     (dict(chunk=48), -1), (dict(chunk=128), -1), (dict(chunk=7), -1), (dict(dtype=2), -1), (dict(B=-1), -1),
     (dict(T=-3), -1), (dict(dk=0), -1), (dict(dk=96), -2), (dict(dv=256), -2),
     (dict(q=None), -1), (dict(o=None), -1), (dict(k=MIS), -1), (dict(S_T=A + 64), -1),
+    # index ranges: B and H at most 65535 each, B*H at most 2^24
+    (dict(B=65536, T=1), -1), (dict(H=65536, T=1), -1), (dict(B=4096, H=4097, T=1), -1),
 ])
 def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
+
+
+def test_prefill_index_range_limits_are_inclusive():
+    # the largest accepted sizes pass validation (B*H = 2^24 exactly); nothing is
+    # launched because T = 0 and S_T is S0
+    assert _prefill(B=4096, H=4096, T=0, S_T=A, S0=A) == 0
+    assert _prefill(B=65535, H=1, T=0, S_T=A, S0=A) == 0
+
+
+def _prefill_ex(spin_limit=-1, **kw):
+    args = dict(q=A, k=A, v=A, g=A, beta=A, S0=A, o=A, S_T=A, snaps=None, every=0, n=0,
+                B=1, T=8, H=2, dk=64, dv=64, dtype=0, chunk=16, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    opts = binding.FwdOptions(spin_limit=spin_limit)
+    return binding.lib().kda_chunk_fwd_ex(
+        vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]), vp(args["beta"]), vp(args["S0"]),
+        vp(args["o"]), vp(args["S_T"]), vp(args["snaps"]), args["every"], args["n"], args["B"], args["T"],
+        args["H"], args["dk"], args["dv"], args["dtype"], args["chunk"], ctypes.byref(opts), args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(spin_limit=-2), -1), (dict(chunk=48), -1), (dict(dk=96), -2), (dict(B=65536), -1),
+    (dict(n=1, every=16, snaps=None), -1),
+])
+def test_prefill_ex_rejects(kw, code):
+    assert _prefill_ex(**kw) == code
+
+
+def test_prefill_ex_empty_is_a_no_op():
+    assert _prefill_ex(B=0, q=None, k=None, v=None, g=None, beta=None, o=None, spin_limit=0) == 0
 
 
 def test_prefill_empty_batch_is_a_no_op():

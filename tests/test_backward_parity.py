@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
 
 
-def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what="", x=None):
+def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what="", x=None, tol_by_name=None):
     x = prefill_inputs(spec, device=gpu, T=T) if x is None else x
     gr = backward_inputs(spec, device=gpu, T=T, ds_std=ds_std)
     got = binding.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gr["dO"], gr["dS_T"])
@@ -34,7 +34,8 @@ def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what="", x=None)
         for name, m, r in zip(NAMES, mine, ref):
             if Tn == 0 and name != "dS0":
                 continue
-            worst[name] = max(worst[name], assert_parity(m, r, tol, f"{what} b{b} h{h} {name}"))
+            t = (tol_by_name or {}).get(name, tol)
+            worst[name] = max(worst[name], assert_parity(m, r, t, f"{what} b{b} h{h} {name}"))
     print(f"backward {what}: " + " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
     return got
 
@@ -72,9 +73,16 @@ def test_backward_empty_sequence(gpu):
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_backward_at_the_bound(gpu, dtype):
-    """g = -5 for every token and channel: the reciprocal decay reaches e^{75} in a chunk."""
+    """g = -5 for every token and channel: the reciprocal decay reaches e^{75} in a chunk,
+    and the chunk-start-referenced operands k e^G fall to e^-80 |k|, below fp32's smallest
+    normal number (1.2e-38) for |k| < 6.6e-3.  dg sums products whose factors reach
+    e^{+-80} before they cancel: the float32 evaluation of this chunk algebra holds dg to
+    5.5e-6 - 1.2e-5 of its norm with sub-normal operands kept and 2.3e-5 - 4.1e-5 with them
+    flushed to zero, as the fp32 matrix cores flush them
+    (tests/test_chunk_algebra.py::test_fp32_backward_at_the_bound_needs_subnormal_operands).
+    dg alone is held to 1e-4 here; every other gradient to the 1e-5 bar."""
     spec = PrefillSpec(B=1, H=2, T=48, dk=128, dv=128, dtype=dtype, seed=99, gate="const", g_const=-5.0)
-    _check(spec, gpu, what=f"g=-5 {dtype}")
+    _check(spec, gpu, what=f"g=-5 {dtype}", tol_by_name={"dg": 1e-4} if dtype == "fp32" else None)
 
 
 @pytest.mark.parametrize("name", ["L1", "L1_bf16"])

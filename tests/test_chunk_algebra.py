@@ -19,7 +19,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.chunk_model import chunk_forward, nilpotent_inverse
+from gated_delta_rule_18_amd.inputs import PrefillSpec, backward_inputs, prefill_inputs
+from tests.chunk_model import chunk_backward, chunk_forward, nilpotent_inverse
 
 
 def _inputs(rng, T, dk, dv, gscale=1.0):
@@ -140,3 +141,35 @@ def test_transposed_inverse_in_operand_layout():
     T = np.linalg.inv(np.eye(16) + A_full) @ np.diag(beta)
     image = np.array([T[lane % 16, 4 * (lane // 16):4 * (lane // 16) + 4] for lane in range(64)])
     assert np.abs(TT - image).max() <= 1e-12 * np.abs(T).max()
+
+
+def test_fp32_backward_at_the_bound_needs_subnormal_operands():
+    """g = -5 on every token and channel: the operand k e^G of the last tokens of a chunk
+    falls below fp32's smallest normal number for small |k|, and dg sums products such as
+    dKt Kt and dKc Kc whose factors reach e^{+-80} before they cancel.  The float32
+    chunk-form reverse mode (float32 inverse, as the kernel's fp32 mode) keeps every
+    other gradient within 1e-6 of the fp64 gradients but dg only within 2e-5 (5.5e-6 to
+    1.2e-5 over seeds) when the sub-normal values are kept, and dg drifts to between 1e-5
+    and 1e-4 when they are flushed to zero, as fp32 matrix units flush them.  This is the
+    measured basis of the fp32-mode dg bar of the GPU backward test at the bound."""
+    from oracle import backward as obwd
+    spec = PrefillSpec(B=1, H=2, T=48, dk=128, dv=128, dtype="fp32", seed=99, gate="const", g_const=-5.0)
+    x = prefill_inputs(spec)
+    gr = backward_inputs(spec)
+    f = lambda t: t.double().numpy()
+    worst = {False: np.zeros(6), True: np.zeros(6)}
+    for h in range(spec.H):
+        q, k, v, g = (f(x[n][0, :, h]) for n in "qkvg")
+        beta, S0 = f(x["beta"][0, :, h]), f(x["S0"][0, h])
+        dO, dS = f(gr["dO"][0, :, h]), f(gr["dS_T"][0, h])
+        ref = obwd.backward(q[None, :, None], k[None, :, None], v[None, :, None], g[None, :, None],
+                            beta[None, :, None], S0[None, None], dO[None, :, None], dS[None, None])
+        ref = [r[0, :, 0] for r in ref[:5]] + [ref[5][0, 0]]
+        for flush in (False, True):
+            got = chunk_backward(q, k, v, g, beta, S0, dO, dS, 16, dtype=np.float32, flush_subnormal=flush)
+            for i, (a, r) in enumerate(zip(got, ref)):
+                worst[flush][i] = max(worst[flush][i], np.abs(a - r).max() / np.abs(r).max())
+    dg = 3
+    assert np.delete(worst[False], dg).max() < 1e-6 and worst[False][dg] < 2e-5, worst[False]
+    assert np.delete(worst[True], dg).max() < 2e-6, worst[True]
+    assert 1e-5 < worst[True][dg] < 1e-4, worst[True]

@@ -14,7 +14,10 @@ from tests.util import TOL, assert_parity
 pytestmark = pytest.mark.gpu
 
 HEADS = (0, 47, 95)
-COLS = np.arange(0, 128, 8)          # 16 of the 128 value columns
+# 16 of the 128 value columns: column 16 w + j sits at lane position j of consumer
+# wavefront w % 4 of value slice w // 4; one column per lane position j, spread over
+# all eight (slice, wavefront) pairs
+COLS = np.array([16 * (j % 8) + j for j in range(16)])
 
 
 def _oracle_segment(inp, S0_cols, heads=HEADS, cols=COLS, snap_every=0, n_snaps=0):

@@ -8,7 +8,7 @@ import torch
 import oracle
 from gated_delta_rule_18_amd import binding
 from gated_delta_rule_18_amd.inputs import PREP_K3, PrepSpec, prep_inputs, to_f64
-from tests.util import TOL, assert_parity
+from tests.util import TOL, assert_close_elementwise as _close, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -23,14 +23,7 @@ def _bar(dtype):
 
 
 def assert_close_elementwise(got, ref, dtype, what):
-    got = np.asarray(got, dtype=np.float64)
-    assert np.isfinite(got).all(), f"{what}: non-finite values"
-    rel, absr = _bar(dtype)
-    scale = float(np.abs(ref).max()) if ref.size else 0.0
-    excess = np.abs(got - ref) - (rel * np.abs(ref) + absr * scale)
-    worst = float(excess.max()) if ref.size else -1.0
-    assert worst <= 0.0, f"{what}: exceeds the bar by {worst:.3e} (scale {scale:.3e})"
-    return float((np.abs(got - ref) / max(scale, 1e-30)).max()) if ref.size else 0.0
+    return _close(got, ref, dtype, what, bar=_bar(dtype))
 
 
 def _oracle(x):
