@@ -26,8 +26,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_FP32 = 0, 1
-KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, -1, -2, -3
-EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
+KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20      # KDA_NOALLOC_SCRATCH_BYTES
+EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
            "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
            "kda_validate_inputs", "kda_version")
@@ -68,6 +69,8 @@ def lib():
                                             + [i] * 6 + [vp])
         L.kda_chunk_bwd.restype = i
         L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t] + [i] * 6 + [vp]
+        L.kda_chunk_bwd_noalloc.restype = i
+        L.kda_chunk_bwd_noalloc.argtypes = [vp] * 14 + [i] * 6 + [vp]
         L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         L.kda_chunk_bwd_workspace_size.argtypes = [i] * 5
         L.kda_output_gate.restype = i
@@ -178,11 +181,9 @@ def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_ev
     return o, S_T, snaps
 
 
-def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=None):
-    """Gradients of <dO, o> + <dS_T, S_T> through chunk_fwd.  Inputs as chunk_fwd plus
-    dO [B,T,H,dv] (input dtype) and dS_T [B,H,dk,dv] fp32 or None (zero).  Returns fp32
-    (dq, dk, dv, dg, dbeta, dS0); dS0 is None when return_dS0 is False.  `workspace`
-    may supply a uint8 device tensor of at least workspace_size(...) bytes."""
+def _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T, return_dS0, out):
+    """Checks the backward's inputs; returns the sizes, the dtype code and the fp32
+    outputs (dq, dk, dv, dg, dbeta, dS0): `out` when given (checked), else new tensors."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -193,11 +194,26 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=No
     for name, t in (("S0", S0), ("dS_T", dS_T)):
         if t is not None:
             _want(t, name, (B, H, dk, dv), torch.float32, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dq, dk_, dg = (torch.empty((B, T, H, dk), **f32) for _ in range(3))
-    dv_ = torch.empty((B, T, H, dv), **f32)
-    db = torch.empty((B, T, H), **f32)
-    dS0 = torch.empty((B, H, dk, dv), **f32) if return_dS0 else None
+    shapes = ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H, dk), (B, T, H), (B, H, dk, dv))
+    if out is None:
+        out = tuple(torch.empty(s, dtype=torch.float32, device=dev) for s in shapes)
+        if not return_dS0:
+            out = out[:5] + (None,)
+    else:
+        for name, t, s in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), out, shapes):
+            if t is not None:
+                _want(t, name, s, torch.float32, dev)
+    return (B, T, H, dk, dv), code, tuple(out)
+
+
+def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=None):
+    """Gradients of <dO, o> + <dS_T, S_T> through chunk_fwd.  Inputs as chunk_fwd plus
+    dO [B,T,H,dv] (input dtype) and dS_T [B,H,dk,dv] fp32 or None (zero).  Returns fp32
+    (dq, dk, dv, dg, dbeta, dS0); dS0 is None when return_dS0 is False.  `workspace`
+    may supply a uint8 device tensor of at least workspace_size(...) bytes."""
+    (B, T, H, dk, dv), code, (dq, dk_, dv_, dg, db, dS0) = _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T,
+                                                                          return_dS0, None)
+    dev = q.device
     need = workspace_size(B, T, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -206,6 +222,21 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=No
     rc = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
                              _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace),
                              int(workspace.numel()), B, T, H, dk, dv, code, _stream(dev))
+    _check(rc)
+    return dq, dk_, dv_, dg, db, dS0
+
+
+def chunk_bwd_noalloc(q, k, v, g, beta, S0, dO, dS_T=None, out=None, return_dS0=True):
+    """chunk_bwd through kda_chunk_bwd_noalloc: the library's per-GPU scratch array in
+    place of a workspace (sizes needing more than NOALLOC_SCRATCH_BYTES raise
+    KdaError with code KDA_ERR_TOO_LARGE).  `out` = (dq, dk, dv, dg, dbeta, dS0)
+    supplies preallocated fp32 outputs (dS0 may be None); without it they are
+    allocated here, as in chunk_bwd."""
+    (B, T, H, dk, dv), code, (dq, dk_, dv_, dg, db, dS0) = _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T,
+                                                                          return_dS0, out)
+    rc = lib().kda_chunk_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO),
+                                     _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db),
+                                     _ptr(dS0), B, T, H, dk, dv, code, _stream(q.device))
     _check(rc)
     return dq, dk_, dv_, dg, db, dS0
 

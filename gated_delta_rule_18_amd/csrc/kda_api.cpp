@@ -1,11 +1,14 @@
 // kda_api.cpp -- the C ABI declared in include/kda.h: argument validation,
-// error mapping and dispatch to the HIP launchers.  No allocation, no global
-// state, no host synchronisation.
+// error mapping and dispatch to the HIP launchers.  No allocation and no host
+// synchronisation; the only global state is the per-device address of the
+// allocation-free backward's scratch array.
 #include "kda.h"
 
 #include <cstdint>
 
 #include "kda_internal.h"
+
+static_assert(kda::kNoallocScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "scratch size");
 
 namespace {
 
@@ -103,6 +106,73 @@ int decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const f
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+              const float *S0, const void *dO, const float *dS_T, float *dq, float *dk, float *dv,
+              float *dg, float *dbeta, float *dS0, void *workspace, size_t workspace_bytes, int B,
+              int T, int H, int dk_size, int dv_size, int dtype, void *stream, bool library_scratch)
+{
+    if (B < 0 || T < 0 || H < 0 || dk_size <= 0 || dv_size <= 0)
+        return KDA_ERR_INVALID;
+    if (dtype != KDA_BF16 && dtype != KDA_FP32)
+        return KDA_ERR_INVALID;
+    if (!head_ok(dk_size) || !head_ok(dv_size))
+        return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * T * H * (dk_size > dv_size ? dk_size : dv_size) > (1LL << 40) || B > kMaxBH ||
+        H > kMaxBH || (long long)B * H > kMaxHeads)
+        return KDA_ERR_INVALID;
+    if ((long long)B * H == 0)
+        return KDA_OK;
+    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, dk_size, dv_size);
+    if (library_scratch) {
+        if (need > kda::kNoallocScratchBytes)
+            return KDA_ERR_TOO_LARGE;
+    } else if (workspace_bytes < need || (need > 0 && !workspace) ||
+               (reinterpret_cast<std::uintptr_t>(workspace) & 255u)) {
+        return KDA_ERR_INVALID;
+    }
+    const bool has_tokens = T > 0;
+    if (has_tokens && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDA_ERR_INVALID;
+    if (library_scratch) {
+        // the library's per-device array in place of a caller's workspace; its
+        // address belongs to the current device, so the stream must too
+        int cur = 0, sdev = 0;
+        if (hipGetDevice(&cur) != hipSuccess ||
+            hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &sdev) != hipSuccess || cur != sdev)
+            return KDA_ERR_INVALID;
+        float *scratch = nullptr;
+        if (kda::noalloc_scratch(&scratch) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+        workspace = scratch;
+    }
+    const long long es = dtype == KDA_FP32 ? 4 : 2;
+    const long long rows = (long long)B * T * H;
+    const long long sb = (long long)B * H * dk_size * dv_size * 4;
+    const void *in[] = {q, k, v, g, beta, S0, dO, dS_T, workspace};
+    const long long in_n[] = {rows * dk_size * es, rows * dk_size * es, rows * dv_size * es,
+                              rows * dk_size * es, rows * es, sb, rows * dv_size * es, sb,
+                              (long long)need};
+    const void *out[] = {dq, dk, dv, dg, dbeta, dS0};
+    const long long out_n[] = {rows * dk_size * 4, rows * dk_size * 4, rows * dv_size * 4,
+                               rows * dk_size * 4, rows * 4, sb};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 9; ++j)
+            if (overlap(out[i], out_n[i], in[j], in_n[j]))
+                return KDA_ERR_INVALID;
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out_n[i], out[j], out_n[j]))
+                return KDA_ERR_INVALID;
+    }
+    hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0,
+                                         static_cast<float *>(workspace), B, T, H, dk_size, dv_size,
+                                         dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 } // namespace
 
 extern "C" {
@@ -120,6 +190,9 @@ const char *kda_strerror(int status)
         return "unsupported head size (dk and dv must be 64 or 128)";
     case KDA_ERR_LAUNCH:
         return "HIP kernel launch failed";
+    case KDA_ERR_TOO_LARGE:
+        return "sizes need more workspace than the library's scratch array holds "
+               "(KDA_NOALLOC_SCRATCH_BYTES)";
     default:
         return "unknown kda status";
     }
@@ -256,50 +329,17 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, co
                   size_t workspace_bytes, int B, int T, int H, int dk_size, int dv_size, int dtype,
                   void *stream)
 {
-    if (B < 0 || T < 0 || H < 0 || dk_size <= 0 || dv_size <= 0)
-        return KDA_ERR_INVALID;
-    if (dtype != KDA_BF16 && dtype != KDA_FP32)
-        return KDA_ERR_INVALID;
-    if (!head_ok(dk_size) || !head_ok(dv_size))
-        return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * T * H * (dk_size > dv_size ? dk_size : dv_size) > (1LL << 40) || B > kMaxBH ||
-        H > kMaxBH || (long long)B * H > kMaxHeads)
-        return KDA_ERR_INVALID;
-    if ((long long)B * H == 0)
-        return KDA_OK;
-    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, dk_size, dv_size);
-    if (workspace_bytes < need || (need > 0 && !workspace) ||
-        (reinterpret_cast<std::uintptr_t>(workspace) & 255u))
-        return KDA_ERR_INVALID;
-    const bool has_tokens = T > 0;
-    if (has_tokens && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
-        return KDA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p))
-            return KDA_ERR_INVALID;
-    const long long es = dtype == KDA_FP32 ? 4 : 2;
-    const long long rows = (long long)B * T * H;
-    const long long sb = (long long)B * H * dk_size * dv_size * 4;
-    const void *in[] = {q, k, v, g, beta, S0, dO, dS_T, workspace};
-    const long long in_n[] = {rows * dk_size * es, rows * dk_size * es, rows * dv_size * es,
-                              rows * dk_size * es, rows * es, sb, rows * dv_size * es, sb,
-                              (long long)need};
-    const void *out[] = {dq, dk, dv, dg, dbeta, dS0};
-    const long long out_n[] = {rows * dk_size * 4, rows * dk_size * 4, rows * dv_size * 4,
-                               rows * dk_size * 4, rows * 4, sb};
-    for (int i = 0; i < 6; ++i) {
-        for (int j = 0; j < 9; ++j)
-            if (overlap(out[i], out_n[i], in[j], in_n[j]))
-                return KDA_ERR_INVALID;
-        for (int j = 0; j < i; ++j)
-            if (overlap(out[i], out_n[i], out[j], out_n[j]))
-                return KDA_ERR_INVALID;
-    }
-    hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0,
-                                         static_cast<float *>(workspace), B, T, H, dk_size, dv_size,
-                                         dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+                     workspace_bytes, B, T, H, dk_size, dv_size, dtype, stream, false);
+}
+
+int kda_chunk_bwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                          const void *beta, const float *S0, const void *dO, const float *dS_T,
+                          float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0, int B,
+                          int T, int H, int dk_size, int dv_size, int dtype, void *stream)
+{
+    return chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, nullptr, 0, B, T,
+                     H, dk_size, dv_size, dtype, stream, true);
 }
 
 int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,

@@ -44,6 +44,13 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <mutex>
+
+// The workspace of the allocation-free backward entry point.  In host code the
+// name stands for a host-side symbol, not the device address: kernels receive
+// the address noalloc_scratch looked up for the current device.
+static __device__ __align__(256) float scratch[kda::kNoallocScratchBytes / sizeof(float)];
+
 namespace kda {
 namespace {
 
@@ -805,6 +812,30 @@ size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv)
     const long parts = nsl > 1 ? nsl * (long)B * T * H * (3L * dk + 1) : 0;
     // each region rounded up to 64 floats (256 bytes)
     return (size_t)(((states + 63) / 64) * 64 + ((parts + 63) / 64) * 64);
+}
+
+hipError_t noalloc_scratch(float **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // with `dev` current: every device holds its own copy at its own address
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,

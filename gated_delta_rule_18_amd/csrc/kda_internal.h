@@ -68,6 +68,13 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
                             float *dv, float *dg, float *dbeta, float *dS0, float *workspace, int B, int T,
                             int H, int DK, int DV, bool fp32, hipStream_t stream);
 
+// The library's own backward workspace, for callers that cannot allocate: a
+// device array of kNoallocScratchBytes in every GPU's memory (one copy per
+// device, held until the process ends).  noalloc_scratch returns the current
+// device's copy, looked up once per device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(float **ptr);
+
 // The output exposure gate alone over `units` (row, head) rows of dv elements.
 hipError_t launch_output_gate(const void *o, const void *gate, const float *w, void *y, long units,
                               int dv, float eps, bool fp32, hipStream_t stream);

@@ -18,7 +18,8 @@
  *   - All tensor arguments are DEVICE pointers, row-major and contiguous, with
  *     16-byte aligned base addresses.  The caller allocates and frees them; the
  *     library allocates nothing and keeps no global state, so concurrent calls
- *     on different buffers are safe.
+ *     on different buffers are safe -- except kda_chunk_bwd_noalloc, which
+ *     works in a device array the library holds (one per GPU).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it; the call returns without synchronising.  Kernel
  *     faults surface on the stream, not in the return code; a prefill whose
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 110 /* 1.1.0 */
+#define KDA_VERSION 120 /* 1.2.0 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -52,7 +53,8 @@ enum kda_status {
     KDA_OK = 0,
     KDA_ERR_INVALID = -1,     /* null required pointer, bad size, bad dtype/chunk/width/misalignment */
     KDA_ERR_UNSUPPORTED = -2, /* a head size the library has no kernel for (dk, dv not in {64, 128}) */
-    KDA_ERR_LAUNCH = -3       /* the HIP runtime rejected the launch */
+    KDA_ERR_LAUNCH = -3,      /* the HIP runtime rejected the launch */
+    KDA_ERR_TOO_LARGE = -4    /* kda_chunk_bwd_noalloc: the sizes need more than its scratch array */
 };
 
 /*
@@ -301,6 +303,34 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
 
 /* Bytes of workspace kda_chunk_bwd needs for these sizes (0 for invalid sizes). */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk_size, int dv_size);
+
+/*
+ * kda_chunk_bwd_noalloc -- kda_chunk_bwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight training loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, with the workspace
+ * taken from a device array the library holds instead of a caller's buffer.
+ *
+ *   Arguments, layouts and gradients as kda_chunk_bwd, without the workspace
+ *   arguments.  The call allocates nothing and frees nothing.
+ *   Scratch: a static device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) in
+ *     every GPU's memory, reserved when the library's code is loaded on that
+ *     GPU and held until the process ends; its address is looked up once per
+ *     device, on the first call with that device current.  Sizes whose
+ *     kda_chunk_bwd_workspace_size exceeds it are rejected with
+ *     KDA_ERR_TOO_LARGE (e.g. dk = dv = 128 with B*H*T up to about 8192
+ *     token-heads fits).  The array's contents on entry are ignored.
+ *   Concurrency: every call on one GPU uses that GPU's single array, so calls
+ *     whose work can overlap on one GPU (different streams, or different
+ *     host threads, without ordering between them) race and give wrong
+ *     gradients; calls ordered on one stream are safe.
+ *   stream: must belong to the current device (KDA_ERR_INVALID otherwise).
+ * Errors: as kda_chunk_bwd, plus KDA_ERR_TOO_LARGE.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_chunk_bwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                          const void *beta, const float *S0, const void *dO, const float *dS_T,
+                          float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                          int B, int T, int H, int dk_size, int dv_size, int dtype, void *stream);
 
 /*
  * kda_validate_inputs -- debug check of the value domains the kernels assume

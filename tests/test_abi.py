@@ -28,9 +28,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 110
+    assert binding.version() == 120
     L = binding.lib()
-    for code in (0, -1, -2, -3, 17):
+    for code in (0, -1, -2, -3, -4, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
 
 
@@ -279,6 +279,45 @@ def test_bwd_rejects(kw, code):
 
 def test_bwd_empty_batch_is_a_no_op():
     assert _bwd(B=0, q=None, ws=None, wsb=0) == 0
+
+
+def _bwd_noalloc(**kw):
+    args = dict(q=A, k=A, v=A, g=A, beta=A, S0=A, dO=A, dST=A, dq=A + (1 << 26), dk=A + (2 << 26),
+                dv=A + (3 << 26), dg=A + (4 << 26), db=A + (5 << 26), dS0=A + (6 << 26),
+                B=1, T=40, H=2, dk_=64, dv_=128, dtype=0, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    n = ("q", "k", "v", "g", "beta", "S0", "dO", "dST", "dq", "dk", "dv", "dg", "db", "dS0")
+    return binding.lib().kda_chunk_bwd_noalloc(*(vp(args[a]) for a in n), args["B"], args["T"], args["H"],
+                                               args["dk_"], args["dv_"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -1), (dict(T=-1), -1), (dict(dk_=96), -2), (dict(dv_=32), -2),
+    (dict(q=None), -1), (dict(dO=None), -1), (dict(dq=None), -1), (dict(dq=MIS), -1),
+    (dict(B=65536, T=1), -1),
+    # more workspace than the library's scratch array holds
+    (dict(B=1, T=65536, H=8, dk_=128, dv_=128), -4),
+    (dict(B=4, T=4096, H=32, dk_=128, dv_=128), -4),
+])
+def test_bwd_noalloc_rejects(kw, code):
+    assert _bwd_noalloc(**kw) == code
+
+
+def test_bwd_noalloc_scratch_limit():
+    """Sizes at the scratch array's limit: at dk = dv = 128 a token-head takes 4 KiB of
+    chunk states (64 KiB per 16 tokens) and 3080 bytes of the two slices' partials, so
+    8192 token-heads (56 MiB) fit and 16384 do not."""
+    lim = binding.NOALLOC_SCRATCH_BYTES
+    assert lim == 64 << 20
+    assert binding.workspace_size(1, 4096, 2, 128, 128) == 4096 * 2 * (4096 + 3080)
+    assert binding.workspace_size(1, 4096, 2, 128, 128) <= lim
+    assert binding.workspace_size(1, 8192, 2, 128, 128) > lim
+    assert binding.workspace_size(1, 8192, 4, 64, 64) <= lim
+
+
+def test_bwd_noalloc_empty_batch_is_a_no_op():
+    assert _bwd_noalloc(B=0, q=None) == 0
 
 
 def _validate(**kw):
