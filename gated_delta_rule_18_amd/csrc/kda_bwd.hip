@@ -38,9 +38,13 @@
 // dV and dS0 are per value column and written directly.  dq, dk, dg and dbeta
 // are sums over all value columns, and every expression above after the column
 // contractions (dM, dTm, dQt, dKe, dKt and rowsum(D S)) is linear in them, so
-// each slice computes the whole chain on its own columns and writes a partial;
-// a second kernel adds the slices' partials in slice order (no atomics: the
-// result is deterministic).
+// each slice computes the whole chain on its own columns.  The two slices of a
+// head run on one XCD: slice 0 writes its partials and, chunk by chunk,
+// publishes them with a flag in global memory; slice 1 keeps its own partials
+// of a chunk in registers, and two chunks later, once the flag shows slice 0's
+// partials of that chunk are in the shared L2, loads them (bypassing its own
+// L1), adds them in slice order and writes the gradients (no atomics: the
+// result is deterministic and the same as summing the slices afterwards).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -75,6 +79,13 @@ template <typename E> __device__ __forceinline__ float rcp_e(float x)
 }
 
 constexpr int kBT = 256;        // threads per workgroup
+// s_waitcnt operand: vector-memory count 0, the other counters unconstrained
+constexpr int kVmcntZero = 0x0F70;
+// cache policy of a buffer load at device scope (sc1): bypasses this CU's L1,
+// so values another CU of the XCD stored are read from the shared L2
+constexpr int kLoadDevice = 16;
+// polls of a slice-0 flag before slice 1 gives up and marks its sums NaN
+constexpr int kBwdSpinLimit = 1 << 18;
 constexpr int kNV = 64;         // value columns per workgroup
 constexpr int kC = 16;          // tokens per chunk
 constexpr int kXCDs = 8;
@@ -112,7 +123,8 @@ struct BwdL {
     static constexpr int oGam = oDB + kC * MS;  // Gam [DK]
     static constexpr int oGd = oGam + DK;       // rowsum(D S) [DK]
     static constexpr int oBeta = oGd + DK;      // beta [16]
-    static constexpr int floats = oBeta + kC;
+    static constexpr int oAbort = oBeta + kC;   // int: slice 1 gave up waiting for slice 0
+    static constexpr int floats = oAbort + 4;
     static constexpr int bytes = floats * 4;
 };
 
@@ -224,6 +236,11 @@ __device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, int voff, float
 {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
 }
+__device__ __forceinline__ void st_out4(__amdgpu_buffer_rsrc_t r, int voff, f32x4 x)
+{
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff, 0, 0);
+}
 
 template <typename E, int DK>
 struct Pre {
@@ -318,13 +335,90 @@ struct Pre {
     }
 };
 
+// A flag or float stored by another CU of this XCD: device-scope load.
+__device__ __forceinline__ int ld_flag_dev(const int *f)
+{
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(bwd_buffer(f, 4), 0, 0, kLoadDevice);
+}
+
+// One thread's share of a chunk's dq, dk, dg and dbeta, in the order the
+// kernel produces them: dbeta of token `lane` (wave 1, lanes < 16), dq and dk of
+// rows 4 g4 + j and key channel 16 ct + l16 for the wave's tiles ct = w + 4 i,
+// dg of key channel pc for tokens pr0 .. pr0 + TPP - 1.
+template <int DK>
+struct Part {
+    static constexpr int NCW = DK / 64;              // key-channel tiles per wave
+    static constexpr int TPP = kC / (kBT / DK);      // dg tokens per thread
+    float b, g[TPP];
+    f32x4 q[NCW], k[NCW];            // key channels 16 (w + 4 i) + 4 g4 + j of token l16
+
+    // this thread's values of chunk t0 .. t0 + n - 1 from slice 0's partials
+    // (device-scope loads; rows past n read 0), or NaN when slice 0 never
+    // published them
+    __device__ __forceinline__ void load(const float *pq, const float *pk, const float *pg, const float *pb,
+                                         long tokb, int t0, int n, int H, int h, int t, bool nan)
+    {
+        const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
+        const int pc = t % DK, pr0 = (t / DK) * TPP;
+        const long rowb = ((tokb + t0) * H + h) * DK;
+        const __amdgpu_buffer_rsrc_t rq = rows_out(const_cast<float *>(pq) + rowb, n, (long)H * DK * 4, DK * 4);
+        const __amdgpu_buffer_rsrc_t rk = rows_out(const_cast<float *>(pk) + rowb, n, (long)H * DK * 4, DK * 4);
+        const __amdgpu_buffer_rsrc_t rg = rows_out(const_cast<float *>(pg) + rowb, n, (long)H * DK * 4, DK * 4);
+        const __amdgpu_buffer_rsrc_t rb = rows_out(const_cast<float *>(pb) + (tokb + t0) * H + h, n, (long)H * 4, 4);
+        const float nanv = __builtin_nanf("");
+        auto ld = [&](__amdgpu_buffer_rsrc_t r, int voff) {
+            return nan ? nanv : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kLoadDevice));
+        };
+        auto ld4 = [&](__amdgpu_buffer_rsrc_t r, int voff) {
+            typedef unsigned u4 __attribute__((ext_vector_type(4)));
+            return nan ? f32x4{nanv, nanv, nanv, nanv}
+                       : __builtin_bit_cast(f32x4, (u4)__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadDevice));
+        };
+        b = ld(rb, (lane & 15) * H * 4);
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) {
+            const int off = (l16 * H * DK + 16 * (w + 4 * i) + 4 * g4) * 4;
+            q[i] = ld4(rq, off);
+            k[i] = ld4(rk, off);
+        }
+#pragma unroll
+        for (int u = 0; u < TPP; ++u)
+            g[u] = ld(rg, ((pr0 + u) * H * DK + pc) * 4);
+    }
+    // the gradients of that chunk: slice 0's values (this) + slice 1's (own)
+    __device__ __forceinline__ void store_sum(const Part &own, float *oq, float *ok, float *og, float *ob,
+                                              long tokb, int t0, int n, int H, int h, int t) const
+    {
+        const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
+        const int pc = t % DK, pr0 = (t / DK) * TPP;
+        const long rowb = ((tokb + t0) * H + h) * DK;
+        const __amdgpu_buffer_rsrc_t rq = rows_out(oq + rowb, n, (long)H * DK * 4, DK * 4);
+        const __amdgpu_buffer_rsrc_t rk = rows_out(ok + rowb, n, (long)H * DK * 4, DK * 4);
+        const __amdgpu_buffer_rsrc_t rg = rows_out(og + rowb, n, (long)H * DK * 4, DK * 4);
+        if (w == 1 && lane < kC) {
+            const __amdgpu_buffer_rsrc_t rb = rows_out(ob + (tokb + t0) * H + h, n, (long)H * 4, 4);
+            st_out(rb, lane * H * 4, b + own.b);
+        }
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) {
+            const int off = (l16 * H * DK + 16 * (w + 4 * i) + 4 * g4) * 4;
+            st_out4(rq, off, q[i] + own.q[i]);
+            st_out4(rk, off, k[i] + own.k[i]);
+        }
+#pragma unroll
+        for (int u = 0; u < TPP; ++u)
+            st_out(rg, ((pr0 + u) * H * DK + pc) * 4, g[u] + own.g[u]);
+    }
+};
+
 template <typename E, int DK>
 __global__ __launch_bounds__(kBT) void bwd_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const E *__restrict__ g,
     const E *__restrict__ beta, const E *__restrict__ dO,
     const float *__restrict__ dST, const E *__restrict__ states, float *__restrict__ dv_out,
-    float *__restrict__ dS0_out, float *__restrict__ pq, float *__restrict__ pk, float *__restrict__ pg,
-    float *__restrict__ pb, int T, int H, int DV, int nbh, int nsl)
+    float *__restrict__ dS0_out, float *pq, float *pk, float *pg, float *pb, float *__restrict__ oq,
+    float *__restrict__ ok, float *__restrict__ og, float *__restrict__ ob, int *flags, int T, int H, int DV,
+    int nbh, int nsl, int spin_limit)
 {
     typedef BwdL<DK> L;
     extern __shared__ __align__(16) float sm[];
@@ -335,6 +429,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     float *Bm = sm + L::oB, *Lm = sm + L::oL, *Tm = sm + L::oTm, *Mm = sm + L::oM;
     float *dM = sm + L::oDM, *dT = sm + L::oDT, *dB = sm + L::oDB;
     float *Gam = sm + L::oGam, *Gd = sm + L::oGd, *bet = sm + L::oBeta;
+    int *abort_flag = reinterpret_cast<int *>(sm + L::oAbort);
 
     // workgroup -> (head, value slice); slices of a head share an XCD's L2
     const int id = blockIdx.x, xcd = id % kXCDs, rr = id / kXCDs;
@@ -347,6 +442,16 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     const long tokb = (long)b * T;
     const int nchunks = (T + kC - 1) / kC;
     const long sbase = (long)bh * DK * DV;                 // this head's state in [B,H,DK,DV]
+    // with two value slices, slice 0 publishes partials (pq, pk, pg, pb) and
+    // slice 1 sums them with its own into the gradients (oq, ok, og, ob); a single
+    // slice writes the gradients directly (pq .. pb are then the gradients)
+    const bool publisher = nsl > 1 && slice == 0, summer = nsl > 1 && slice == 1;
+    // slice 1: this chunk's values, those of the two chunks before it in the walk,
+    // and slice 0's; the flag poll of thread 0
+    Part<DK> own, prev1, prev2, part;
+    int flagv = 0;
+    if (t == 0)
+        *abort_flag = 0;
 
     // D <- dS_T (slice columns)
     for (int e = t; e < DK * kNV; e += kBT) {
@@ -363,8 +468,18 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         const int t0 = ci * kC;
         const int n = T - t0 < kC ? T - t0 : kC;
         __syncthreads();   // previous chunk's readers of every array are done
+        // slice 0: every thread's stores of chunk ci + 1 have completed (waited at
+        // the end of that chunk): publish the count of finished chunks
+        if (publisher && t == 0 && ci + 1 < nchunks)
+            __builtin_amdgcn_raw_buffer_store_b32(nchunks - 1 - ci, bwd_buffer(flags + bh, 4), 0, 0, 0);
         // ---- the chunk's incoming state and inputs (rows r >= n are zero) ---------
         pre.store(Ss, Qt, Kt, Pm, Xs, dOs, bet, t);
+        // slice 1: poll slice 0's flag for chunk ci + 2 (published a chunk ago), the
+        // load issued before the prefetch so that waiting for it later does not
+        // wait for the prefetch too
+        if (summer && t == 0 && ci + 2 < nchunks)
+            flagv = ld_flag_dev(flags + bh);
+        __builtin_amdgcn_sched_barrier(0);
         if (ci > 0)
             pre.load(q, k, v, g, beta, dO, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
         __syncthreads();
@@ -508,7 +623,21 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 dUs[(4 * g4 + j) * L::CS + 16 * w + l16] = du[j];
             }
         }
+        // slice 1: chunk ci + 2 must be published (poll again, bounded, if the
+        // early read missed it); then load slice 0's partials of that chunk
+        if (summer && ci + 2 < nchunks && t == 0) {
+            int spins = 0;
+            while (*abort_flag == 0 && flagv < nchunks - 2 - ci) {
+                if (++spins > spin_limit)
+                    *abort_flag = 1;
+                __builtin_amdgcn_s_sleep(2);
+                flagv = ld_flag_dev(flags + bh);
+            }
+        }
         __syncthreads();
+        if (summer && ci + 2 < nchunks)
+            part.load(pq, pk, pg, pb, tokb, t0 + 2 * kC, T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t,
+                      *abort_flag != 0);
         // ---- dX = Tm^T dU (= dV) -----------------------------------------------------
         {
             const f32x4 dx = mmk<kC, 2>(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -572,19 +701,22 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                              __shfl(pr[1], 16 * (lane >> 2), 64) * ((lane & 3) == 1) +
                              __shfl(pr[2], 16 * (lane >> 2), 64) * ((lane & 3) == 2) +
                              __shfl(pr[3], 16 * (lane >> 2), 64) * ((lane & 3) == 3);
-            if (lane < kC && lane < n) {
-                const long bo = (long)slice * ((long)nbh / H * T * H) + (tokb + t0 + lane) * H + h;
-                pb[bo] = dbd + pa;
-            }
+            own.b = dbd + pa;
+            if (!summer && lane < kC && lane < n)
+                pb[(tokb + t0 + lane) * H + h] = own.b;
         }
         __syncthreads();
 
         // ---- parameter gradients: wave w owns key-channel tiles ct = w, w + 4 -------
+        //      Every product is formed transposed (operands of each MFMA swapped):
+        //      lane (l16, g4) then holds key channels 16 ct + 4 g4 + j, j < 4, of
+        //      token l16, so its LDS operands and its dq, dk values are 16-byte pieces
         {
-            const long so = (long)slice * ((long)nbh / H * T * H) * DK;
+            // (a rolled loop: unrolled, its two iterations' loads and products
+            // would all be live at once)
 #pragma unroll 1
-            for (int ct = w; ct < DK / 16; ct += 4) {
-                const int c = 16 * ct + l16;
+            for (int ci4 = 0; ci4 < DK / 64; ++ci4) {
+                const int ct = w + 4 * ci4;
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
                 f32x4 aq = z, ae = z, ax = z, aq2 = z, ae2 = z, ax2 = z;
@@ -605,9 +737,9 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb) {
                         const auto vs = rd8(ps + 8 * hb);
-                        aq = mma32(rd8(pdo + 8 * hb), vs, aq);
-                        ax = mma32(rd8(pdx + 8 * hb), vs, ax);
-                        ae = mma32(rd8(pu + 8 * hb), rd8(pd + 8 * hb), ae);
+                        aq = mma32(vs, rd8(pdo + 8 * hb), aq);
+                        ax = mma32(vs, rd8(pdx + 8 * hb), ax);
+                        ae = mma32(rd8(pd + 8 * hb), rd8(pu + 8 * hb), ae);
                     }
                 } else {
                     // fp32: dO S^T, U D^T, dX S^T over the slice's 64 value columns: lane
@@ -626,12 +758,12 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                         const f32x4 vd = *reinterpret_cast<const f32x4 *>(pd + 4 * qq);
 #pragma unroll
                         for (int e = 0; e < 4; e += 2) {
-                            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(vo[e], vs[e], aq, 0, 0, 0);
-                            ae = __builtin_amdgcn_mfma_f32_16x16x4f32(vu[e], vd[e], ae, 0, 0, 0);
-                            ax = __builtin_amdgcn_mfma_f32_16x16x4f32(vx[e], vs[e], ax, 0, 0, 0);
-                            aq2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vo[e + 1], vs[e + 1], aq2, 0, 0, 0);
-                            ae2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vu[e + 1], vd[e + 1], ae2, 0, 0, 0);
-                            ax2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vx[e + 1], vs[e + 1], ax2, 0, 0, 0);
+                            aq = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[e], vo[e], aq, 0, 0, 0);
+                            ae = __builtin_amdgcn_mfma_f32_16x16x4f32(vd[e], vu[e], ae, 0, 0, 0);
+                            ax = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[e], vx[e], ax, 0, 0, 0);
+                            aq2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[e + 1], vo[e + 1], aq2, 0, 0, 0);
+                            ae2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vd[e + 1], vu[e + 1], ae2, 0, 0, 0);
+                            ax2 = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[e + 1], vx[e + 1], ax2, 0, 0, 0);
                         }
                     }
                 }
@@ -645,31 +777,47 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
 #pragma unroll
                     for (int st = 0; st < kC / 4; ++st) {
                         const float kc = pkc[4 * st * L::OS];
-                        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(pm[4 * st], kc, aq, 0, 0, 0);
-                        ab = __builtin_amdgcn_mfma_f32_16x16x4f32(pb2[4 * st], kc, ab, 0, 0, 0);
-                        ac = __builtin_amdgcn_mfma_f32_16x16x4f32(pmt[4 * st * L::MS], pqt[4 * st * L::OS], ac, 0, 0, 0);
-                        ac2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pbt[4 * st * L::MS], pkt[4 * st * L::OS], ac2, 0, 0, 0);
+                        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, pm[4 * st], aq, 0, 0, 0);
+                        ab = __builtin_amdgcn_mfma_f32_16x16x4f32(kc, pb2[4 * st], ab, 0, 0, 0);
+                        ac = __builtin_amdgcn_mfma_f32_16x16x4f32(pqt[4 * st * L::OS], pmt[4 * st * L::MS], ac, 0, 0, 0);
+                        ac2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pkt[4 * st * L::OS], pbt[4 * st * L::MS], ac2, 0, 0, 0);
                     }
                 }
                 aq += aq2;
                 ae += ae2;
                 ax += ax2;
                 ac += ac2;
-                const float gm = Gam[c];
-                const long rowb = ((tokb + t0) * H + h) * DK;
-                const __amdgpu_buffer_rsrc_t rq = rows_out(pq + so + rowb, n, (long)H * DK * 4, DK * 4);
-                const __amdgpu_buffer_rsrc_t rk = rows_out(pk + so + rowb, n, (long)H * DK * 4, DK * 4);
+                // token r = l16, key channels cc + j
+                const int r = l16, cc = 16 * ct + 4 * g4, o = r * L::OS + cc;
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gam + cc);
+                const f32x4 pp = *reinterpret_cast<const f32x4 *>(Pm + o);
+                const f32x4 vke = *reinterpret_cast<const f32x4 *>(Ke + o);
+                const f32x4 vkt = *reinterpret_cast<const f32x4 *>(Kt + o);
+                const f32x4 vqt = *reinterpret_cast<const f32x4 *>(Qt + o);
+                const f32x4 vkc = *reinterpret_cast<const f32x4 *>(Kc + o);
+                f32x4 vq, vk, t1, t2;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g4 + j;
                     const float qt = aq[j], ke = ae[j], ktt = ab[j] - ax[j], kcc = ac[j];
-                    const float p = Pm[r * L::OS + c], ip = rcp_e<E>(p);
-                    const float keke = ke * Ke[r * L::OS + c];
-                    st_out(rq, (r * H * DK + c) * 4, qt * p);
-                    st_out(rk, (r * H * DK + c) * 4, ktt * p + kcc * ip + ke * (gm * ip));
-                    T1[r * L::OS + c] = ktt * Kt[r * L::OS + c] + qt * Qt[r * L::OS + c] -
-                                        kcc * Kc[r * L::OS + c] - keke;
-                    T2[r * L::OS + c] = keke;
+                    const float p = pp[j], ip = rcp_e<E>(p);
+                    const float keke = ke * vke[j];
+                    vq[j] = qt * p;
+                    vk[j] = ktt * p + kcc * ip + ke * (gm[j] * ip);
+                    t1[j] = ktt * vkt[j] + qt * vqt[j] - kcc * vkc[j] - keke;
+                    t2[j] = keke;
+                }
+                *reinterpret_cast<f32x4 *>(T1 + o) = t1;
+                *reinterpret_cast<f32x4 *>(T2 + o) = t2;
+                // kept by register index, without indexing by the loop counter
+#pragma unroll
+                for (int i = 0; i < DK / 64; ++i) {
+                    own.q[i] = ci4 == i ? vq : own.q[i];
+                    own.k[i] = ci4 == i ? vk : own.k[i];
+                }
+                if (!summer) {
+                    const long rowb = ((tokb + t0) * H + h) * DK;
+                    st_out4(rows_out(pq + rowb, n, (long)H * DK * 4, DK * 4), (r * H * DK + cc) * 4, vq);
+                    st_out4(rows_out(pk + rowb, n, (long)H * DK * 4, DK * 4), (r * H * DK + cc) * 4, vk);
                 }
             }
         }
@@ -691,15 +839,23 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
 #pragma unroll
             for (int r = 0; r < kC; ++r)
                 acc += T2[r * L::OS + pc] + (r >= pr0 + TPP ? T1[r * L::OS + pc] : 0.f);
-            const long so = (long)slice * ((long)nbh / H * T * H) * DK;
             const __amdgpu_buffer_rsrc_t rg =
-                rows_out(pg + so + ((tokb + t0) * H + h) * DK, n, (long)H * DK * 4, DK * 4);
+                rows_out(pg + ((tokb + t0) * H + h) * DK, summer ? 0 : n, (long)H * DK * 4, DK * 4);
 #pragma unroll
             for (int u = TPP - 1; u >= 0; --u) {
                 const int r = pr0 + u;
                 acc += T1[r * L::OS + pc];
+                own.g[u] = acc;
                 st_out(rg, (r * H * DK + pc) * 4, acc);
             }
+        }
+        // slice 1: the gradients of chunk ci + 2, then keep this chunk's values
+        if (summer) {
+            if (ci + 2 < nchunks)
+                part.store_sum(prev2, oq, ok, og, ob, tokb, t0 + 2 * kC,
+                               T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t);
+            prev2 = prev1;
+            prev1 = own;
         }
         // ---- D <- Diag(Gam) D + Qt^T dO - Kt^T dX: wave w owns the key-channel tiles
         //      ct = w, w + 4 over all 64 value columns, as four column-interleaved
@@ -745,8 +901,37 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 *reinterpret_cast<f32x4 *>(Ds + (16 * ct + 4 * g4 + jj) * L::SS + 4 * l16) =
                     f32x4{acc[0][jj], acc[1][jj], acc[2][jj], acc[3][jj]};
         }
+        // slice 0: this chunk's partial stores complete before its flag goes out
+        // (at the next chunk's top, after the barrier)
+        if (publisher)
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
     }
     __syncthreads();
+    if (nchunks > 0) {
+        // the last published chunk (chunk 0), and slice 1's sums of chunks 1 and 0
+        if (publisher && t == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(nchunks, bwd_buffer(flags + bh, 4), 0, 0, 0);
+        if (summer) {
+            if (t == 0) {
+                int spins = 0;
+                while (*abort_flag == 0 && ld_flag_dev(flags + bh) < nchunks) {
+                    if (++spins > spin_limit)
+                        *abort_flag = 1;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+            const bool ab = *abort_flag != 0;
+            if (nchunks > 1) {
+                const int n1 = T - kC < kC ? T - kC : kC;
+                part.load(pq, pk, pg, pb, tokb, kC, n1, H, h, t, ab);
+                part.store_sum(prev2, oq, ok, og, ob, tokb, kC, n1, H, h, t);
+            }
+            const int n0 = T < kC ? T : kC;
+            part.load(pq, pk, pg, pb, tokb, 0, n0, H, h, t, ab);
+            part.store_sum(prev1, oq, ok, og, ob, tokb, 0, n0, H, h, t);
+        }
+    }
     if (dS0_out)
         for (int e = t; e < DK * kNV; e += kBT) {
             const int c = e / kNV, j = e % kNV;
@@ -754,16 +939,12 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
 }
 
-// out[i] = sum over slices s of part[s * n + i], s in order
-__global__ __launch_bounds__(256) void sum_slices(const float *__restrict__ part, float *__restrict__ out, long n,
-                                                  int nsl)
+// flags[i] = 0 for i < n (the slice-0 publication counters of one call)
+__global__ __launch_bounds__(256) void zero_flags(int *flags, int n)
 {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
-        float s = part[i];
-        for (int k2 = 1; k2 < nsl; ++k2)
-            s += part[(long)k2 * n + i];
-        out[i] = s;
-    }
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        flags[i] = 0;
 }
 
 template <typename E, int DK>
@@ -781,24 +962,23 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g
         return e;
     const int nbh = B * H, nsl = DV / kNV;
     const long rows = (long)B * T * H;
+    // two slices: slice 0's partials, then the flags; one slice: the gradients
     float *pq = nsl > 1 ? partials : dq;
-    float *pk = nsl > 1 ? partials + (long)nsl * rows * DK : dk;
-    float *pg = nsl > 1 ? partials + 2L * nsl * rows * DK : dg;
-    float *pb = nsl > 1 ? partials + 3L * nsl * rows * DK : dbeta;
+    float *pk = nsl > 1 ? partials + rows * DK : dk;
+    float *pg = nsl > 1 ? partials + 2 * rows * DK : dg;
+    float *pb = nsl > 1 ? partials + 3 * rows * DK : dbeta;
+    int *flags = nsl > 1 && rows > 0 ? reinterpret_cast<int *>(partials + ((rows * (3L * DK + 1) + 63) / 64) * 64) : nullptr;
+    if (flags) {
+        hipLaunchKernelGGL(zero_flags, dim3((nbh + 255) / 256), dim3(256), 0, stream, flags, nbh);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     hipLaunchKernelGGL((bwd_kernel<E, DK>), dim3(grid), dim3(kBT), L::bytes, stream, (const E *)q,
                        (const E *)k, (const E *)v, (const E *)g, (const E *)beta, (const E *)dO, dST,
-                       (const E *)states, dv, dS0, pq, pk, pg, pb, T, H, DV, nbh, nsl);
-    e = hipGetLastError();
-    if (e != hipSuccess || nsl == 1 || rows == 0)
-        return e;
-    const long nk = rows * DK;
-    const int blocks = (int)((nk + 255) / 256 < 4096 ? (nk + 255) / 256 : 4096);
-    hipLaunchKernelGGL(sum_slices, dim3(blocks), dim3(256), 0, stream, pq, dq, nk, nsl);
-    hipLaunchKernelGGL(sum_slices, dim3(blocks), dim3(256), 0, stream, pk, dk, nk, nsl);
-    hipLaunchKernelGGL(sum_slices, dim3(blocks), dim3(256), 0, stream, pg, dg, nk, nsl);
-    const int bb = (int)((rows + 255) / 256 < 4096 ? (rows + 255) / 256 : 4096);
-    hipLaunchKernelGGL(sum_slices, dim3(bb), dim3(256), 0, stream, pb, dbeta, rows, nsl);
+                       (const E *)states, dv, dS0, pq, pk, pg, pb, dq, dk, dg, dbeta, flags, T, H, DV, nbh, nsl,
+                       kBwdSpinLimit);
     return hipGetLastError();
 }
 
@@ -809,9 +989,11 @@ size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv)
     const long nchunks = (T + kC - 1) / kC;
     const long nsl = dv / kNV;
     const long states = nchunks * B * H * (long)dk * dv;      // fp32-sized: either dtype fits
-    const long parts = nsl > 1 ? nsl * (long)B * T * H * (3L * dk + 1) : 0;
+    // two value slices: slice 0's partial dq, dk, dg, dbeta and one flag per head
+    const long parts = nsl > 1 ? (long)B * T * H * (3L * dk + 1) : 0;
+    const long flags = nsl > 1 && T > 0 ? (long)B * H : 0;
     // each region rounded up to 64 floats (256 bytes)
-    return (size_t)(((states + 63) / 64) * 64 + ((parts + 63) / 64) * 64);
+    return (size_t)(((states + 63) / 64) * 64 + ((parts + 63) / 64) * 64 + ((flags + 63) / 64) * 64);
 }
 
 hipError_t noalloc_scratch(float **ptr)

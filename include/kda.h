@@ -288,8 +288,10 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
  *               bytes (may be NULL when that size is 0, i.e. T = 0), 256-byte
  *               aligned; its contents on entry are ignored and on return
  *               unspecified.  It holds every chunk's incoming state (sized as
- *               fp32 for either dtype) and, for dv = 128, the two value slices'
- *               partial dq, dk, dg, dbeta
+ *               fp32 for either dtype) and, for dv = 128, the first value
+ *               slice's partial dq, dk, dg, dbeta and one flag per (sequence,
+ *               head) through which the second slice's workgroup learns that
+ *               they are complete
  *   dk, dv (sizes) : 64 or 128
  * Gradients are fp32 in both dtype modes.  No output may overlap an input or
  * another output.  Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size,
@@ -317,8 +319,8 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk_size, int dv_siz
  *     GPU and held until the process ends; its address is looked up once per
  *     device, on the first call with that device current.  Sizes whose
  *     kda_chunk_bwd_workspace_size exceeds it are rejected with
- *     KDA_ERR_TOO_LARGE (e.g. dk = dv = 128 with B*H*T up to about 8192
- *     token-heads fits).  The array's contents on entry are ignored.
+ *     KDA_ERR_TOO_LARGE (at dk = dv = 128 up to about 11900 token-heads,
+ *     B*H*T, fit).  The array's contents on entry are ignored.
  *   Concurrency: every call on one GPU uses that GPU's single array, so calls
  *     whose work can overlap on one GPU (different streams, or different
  *     host threads, without ordering between them) race and give wrong

@@ -252,11 +252,12 @@ def _bwd(**kw):
 
 def test_bwd_workspace_size():
     # two slices of 64 value columns: the incoming state of chunks 0, 1, 2 (sized
-    # as fp32 for either dtype) and the slice partials
+    # as fp32 for either dtype), slice 0's partials and one flag per head
     want_states = 3 * 2 * 64 * 128 * 4
-    want_parts = 2 * 1 * 40 * 2 * (3 * 64 + 1) * 4
+    want_parts = 1 * 40 * 2 * (3 * 64 + 1) * 4
     rnd = lambda b: (b + 255) // 256 * 256
-    assert binding.workspace_size(1, 40, 2, 64, 128) == rnd(want_states) + rnd(want_parts)
+    assert binding.workspace_size(1, 40, 2, 64, 128) == rnd(want_states) + rnd(want_parts) + rnd(2 * 4)
+    assert binding.workspace_size(1, 0, 2, 64, 128) == 0                            # no tokens, no flags
     assert binding.workspace_size(1, 40, 2, 64, 64) == rnd(3 * 2 * 64 * 64 * 4)    # one slice: no partials
     assert binding.workspace_size(1, 16, 2, 64, 64) == 2 * 64 * 64 * 4              # one chunk: its S0
     assert binding.workspace_size(1, 0, 2, 64, 64) == 0                             # no tokens: nothing
@@ -306,11 +307,11 @@ def test_bwd_noalloc_rejects(kw, code):
 
 def test_bwd_noalloc_scratch_limit():
     """Sizes at the scratch array's limit: at dk = dv = 128 a token-head takes 4 KiB of
-    chunk states (64 KiB per 16 tokens) and 3080 bytes of the two slices' partials, so
-    8192 token-heads (56 MiB) fit and 16384 do not."""
+    chunk states (64 KiB per 16 tokens) and 1540 bytes of slice 0's partials, plus a flag
+    per head, so 8192 token-heads (44 MiB) fit and 16384 do not."""
     lim = binding.NOALLOC_SCRATCH_BYTES
     assert lim == 64 << 20
-    assert binding.workspace_size(1, 4096, 2, 128, 128) == 4096 * 2 * (4096 + 3080)
+    assert binding.workspace_size(1, 4096, 2, 128, 128) == 4096 * 2 * (4096 + 1540) + 256
     assert binding.workspace_size(1, 4096, 2, 128, 128) <= lim
     assert binding.workspace_size(1, 8192, 2, 128, 128) > lim
     assert binding.workspace_size(1, 8192, 4, 64, 64) <= lim

@@ -42,7 +42,7 @@ def _check(spec, gpu, T=None, ds_std=1.0, heads=None, tol=None, what="", x=None,
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
-@pytest.mark.parametrize("T", [1, 16, 40])
+@pytest.mark.parametrize("T", [1, 16, 32, 40])
 def test_backward_small(gpu, dtype, dk, dv, T):
     spec = PrefillSpec(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype, seed=90 + T, s0_std=0.3)
     _check(spec, gpu, what=f"{dtype} dk{dk} dv{dv} T{T}")

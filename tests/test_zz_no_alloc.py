@@ -44,9 +44,9 @@ def _oracle_check(x, gr, got, b, h, dtype, what):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_noalloc_backward_matches_workspace_entry_twice(gpu, dtype):
-    # first call: 8000 token-heads at dk = dv = 128 (57.6 MB of the 64 MiB array: chunk
-    # states and both value slices' partials); second call smaller, with a ragged chunk
-    first = PrefillSpec(B=2, H=4, T=1000, dk=128, dv=128, dtype=dtype, seed=301, s0_std=0.3)
+    # first call: 11500 token-heads at dk = dv = 128 (64.8 MB of the 64 MiB array: chunk
+    # states, slice 0's partials, flags); second call smaller, with a ragged chunk
+    first = PrefillSpec(B=2, H=5, T=1150, dk=128, dv=128, dtype=dtype, seed=301, s0_std=0.3)
     second = PrefillSpec(B=1, H=3, T=77, dk=128, dv=128, dtype=dtype, seed=302, s0_std=0.3)
     for n, spec in enumerate((first, second)):
         what = f"noalloc call {n + 1} {dtype} B{spec.B} H{spec.H} T{spec.T}"
