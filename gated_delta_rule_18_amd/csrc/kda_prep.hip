@@ -25,14 +25,17 @@
 //   wavefronts 2, 3 also map beta of the tile's tokens (lane = token mod 64) for h0
 //                    and h0 + 1 respectively.
 // A conv lane walks the tile token by token keeping its last three inputs in
-// registers; loads run 8 tokens ahead.
+// registers; loads run 8 tokens ahead.  Workgroups are numbered head pair
+// first, so the workgroups in flight at any time cover whole token rows of
+// every tensor (all heads of the same tokens) and the device reads and writes
+// long contiguous runs instead of 512-byte pieces scattered over the sequence.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int kTT = 256;                 // tokens per tile
+constexpr int kTT = 128;                 // tokens per tile
 constexpr int kW = 4;                    // conv width
 constexpr int kU = 8;                    // tokens loaded ahead
 constexpr float kL2Eps = 1e-6f;
@@ -133,7 +136,9 @@ __global__ __launch_bounds__(256) void prep_kernel(
     constexpr int NCH = 2 * DK + DV;
     constexpr int QK = DK / 4, VQ = DV / 4;     // 4-channel lanes per tensor
     static_assert(2 * QK <= 64 && VQ <= 32 && QK <= 32, "lane budget");
-    const int tile = blockIdx.x, b = blockIdx.z;
+    // head pair fastest (one-dimensional numbering: no 65535 limit on tiles)
+    const int npairs = (H + 1) / 2;
+    const int hp = (int)(blockIdx.x % npairs), tile = (int)(blockIdx.x / npairs), b = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int t0 = tile * kTT;
     const int n = T - t0 < kTT ? T - t0 : kTT;           // tokens in this tile (0 only when T == 0)
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
     E *dst;
     bool active;
     if (wave < 2) {
-        h = 2 * blockIdx.y + wave;
+        h = 2 * hp + wave;
         const bool isk = lane >= QK;
         c4 = 4 * (isk ? lane - QK : lane);
         cc = isk ? DK + c4 : c4;
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
         dst = isk ? k : q;
         active = lane < 2 * QK;
     } else {
-        h = 2 * blockIdx.y + (lane >> 5);
+        h = 2 * hp + (lane >> 5);
         c4 = 4 * (lane & 31);
         cc = 2 * DK + c4;
         src = wave == 2 ? v_pre : z;
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(256) void prep_kernel(
 
     // ---- beta = Sigmoid(logit): wavefront 2 for h0, 3 for h0 + 1, lane = token --
     if (wave >= 2) {
-        const int hb = 2 * blockIdx.y + wave - 2;
+        const int hb = 2 * hp + wave - 2;
         if (hb < H) {
             for (int tt = lane; tt < n; tt += 64) {
                 const long r = (tokb + t0 + tt) * H + hb;
@@ -244,7 +249,7 @@ hipError_t launch(const void *q_pre, const void *k_pre, const void *v_pre, const
     if ((long)B * H == 0)
         return hipSuccess;
     const int tiles = T > 0 ? (T + kTT - 1) / kTT : 1;
-    hipLaunchKernelGGL((prep_kernel<E, DK, DV>), dim3(tiles, (H + 1) / 2, B), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prep_kernel<E, DK, DV>), dim3((unsigned)(((H + 1) / 2) * (long)tiles), 1, B), dim3(256), 0, stream,
                        (const E *)q_pre, (const E *)k_pre, (const E *)v_pre, conv_w,
                        (const E *)conv_init, (const E *)z, A, (const E *)beta_logit, (E *)q, (E *)k,
                        (E *)v, (E *)g, (E *)beta, (E *)conv_final, T, H);
