@@ -322,8 +322,21 @@ def main():
         s2 = torch.empty((c2.B, c2.H, c2.dk, c2.dv), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
+        # a 0.2 ms launch: the C entry point is called directly with its arguments
+        # marshalled once, so the host keeps ahead of the device and each event pair
+        # brackets one kernel (through the checking Python wrapper the host needs
+        # ~0.27 ms per call and the device would idle between launches)
+        import ctypes
+        lib = binding.lib()
+        c2_args = [ctypes.c_void_p(t.data_ptr()) for t in (x2["q"], x2["k"], x2["v"], x2["g"], x2["beta"],
+                                                          x2["S0"], o2, s2)]
+        c2_args += [c2.B, c2.T, c2.H, c2.dk, c2.dv, binding.KDA_BF16, C,
+                    ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)]
+
         def c2_step(i=0):
-            binding.chunk_fwd(x2["q"], x2["k"], x2["v"], x2["g"], x2["beta"], x2["S0"], chunk=C, o=o2, S_T=s2)
+            rc = lib.kda_chunk_fwd(*c2_args)
+            if rc != binding.KDA_OK:
+                raise binding.KdaError(rc, lib.kda_strerror(rc).decode())
 
         w2, k2 = _timed(c2_step, args.steps, args.warmup, torch)
         b2 = prefill_bytes(c2.B, c2.T, c2.H, c2.dk, c2.dv)
