@@ -24,7 +24,7 @@ torch.cuda.synchronize():
            dk=dv=128 bf16 prefill shape (gradients fp32).
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
 Kernel durations come from HIP events recorded on the stream the kernels are
-launched on.  The CPU baselines time the fp64 oracle (as it stands) on the host
+launched on, at the two ends of the K timed steps (their interval divided by K).  The CPU baselines time the fp64 oracle (as it stands) on the host
 cores: the whole K3-shaped prefill (cpu_baseline), the whole B4 H32 T4096
 prefill, and a sample of the decode batch; each records the host it ran on.
 
@@ -122,19 +122,21 @@ def measured_traffic(profile, sources):
 
 def _timed(fn, steps, warmup, torch):
     """W warmups, then K steps between synchronisations.  Returns (wall ms/step,
-    mean kernel ms from events on the current stream)."""
+    mean kernel ms per step: the interval between two events recorded on the current
+    stream at the two ends of the K steps, divided by K -- the launches run back to
+    back, so an event between every two launches does not add its own dispatch gap)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        ev[i][0].record()
         fn(i)
-        ev[i][1].record()
+    end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(a.elapsed_time(b) for a, b in ev) / steps
+    kern = start.elapsed_time(end) / steps
     return wall, kern
 
 
@@ -323,9 +325,9 @@ def main():
         torch.cuda.synchronize()
 
         # a 0.2 ms launch: the C entry point is called directly with its arguments
-        # marshalled once, so the host keeps ahead of the device and each event pair
-        # brackets one kernel (through the checking Python wrapper the host needs
-        # ~0.27 ms per call and the device would idle between launches)
+        # marshalled once, so the host keeps ahead of the device and the launches run
+        # back to back (through the checking Python wrapper the host needs ~0.27 ms per
+        # call and the device would idle between launches)
         import ctypes
         lib = binding.lib()
         c2_args = [ctypes.c_void_p(t.data_ptr()) for t in (x2["q"], x2["k"], x2["v"], x2["g"], x2["beta"],
