@@ -720,6 +720,9 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 // dQt = dO S^T + dM Kc;  dKe = U D^T;  dKt = dB Kc - dX S^T;  dKc = dM^T Qt + dB^T Kt
                 f32x4 aq = z, ae = z, ax = z, aq2 = z, ae2 = z, ax2 = z;
+                // rowsum(D (.) S) of key channel 16 ct + l16 over the lane group's 16
+                // value columns, from the fp32 S and D rows these products read
+                f32x4 sd = z;
                 if constexpr (sizeof(E) == 2) {
                     // bf16 mode: dO S^T, U D^T, dX S^T as 32-deep bf16 MFMAs (operands
                     // rounded to bf16, as the forward pass rounds S for its products;
@@ -729,17 +732,18 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                     const float *pdo = dOs + l16 * L::CS + k0, *pu = Us + l16 * L::CS + k0;
                     const float *pdx = dXs + l16 * L::CS + k0;
                     const float *ps = Ss + (16 * ct + l16) * L::SS + k0, *pd = Ds + (16 * ct + l16) * L::SS + k0;
-                    auto rd8 = [](const float *p) {
-                        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-                        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-                        return cat8(cvt4<__bf16>(a), cvt4<__bf16>(b));
-                    };
+                    auto ld4 = [](const float *p) { return *reinterpret_cast<const f32x4 *>(p); };
+                    auto rd8 = [&](const float *p) { return cat8(cvt4<__bf16>(ld4(p)), cvt4<__bf16>(ld4(p + 4))); };
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb) {
-                        const auto vs = rd8(ps + 8 * hb);
+                        const f32x4 s0 = ld4(ps + 8 * hb), s1 = ld4(ps + 8 * hb + 4);
+                        const f32x4 d0 = ld4(pd + 8 * hb), d1 = ld4(pd + 8 * hb + 4);
+                        sd += s0 * d0;
+                        sd += s1 * d1;
+                        const auto vs = cat8(cvt4<__bf16>(s0), cvt4<__bf16>(s1));
                         aq = mma32(vs, rd8(pdo + 8 * hb), aq);
                         ax = mma32(vs, rd8(pdx + 8 * hb), ax);
-                        ae = mma32(rd8(pd + 8 * hb), rd8(pu + 8 * hb), ae);
+                        ae = mma32(cat8(cvt4<__bf16>(d0), cvt4<__bf16>(d1)), rd8(pu + 8 * hb), ae);
                     }
                 } else {
                     // fp32: dO S^T, U D^T, dX S^T over the slice's 64 value columns: lane
@@ -756,6 +760,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                         const f32x4 vx = *reinterpret_cast<const f32x4 *>(pdx + 4 * qq);
                         const f32x4 vs = *reinterpret_cast<const f32x4 *>(ps + 4 * qq);
                         const f32x4 vd = *reinterpret_cast<const f32x4 *>(pd + 4 * qq);
+                        sd += vs * vd;
 #pragma unroll
                         for (int e = 0; e < 4; e += 2) {
                             aq = __builtin_amdgcn_mfma_f32_16x16x4f32(vs[e], vo[e], aq, 0, 0, 0);
@@ -787,6 +792,13 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 ae += ae2;
                 ax += ax2;
                 ac += ac2;
+                {
+                    float gs = (sd[0] + sd[1]) + (sd[2] + sd[3]);
+                    gs += __shfl_xor(gs, 16, 64);
+                    gs += __shfl_xor(gs, 32, 64);
+                    if (g4 == 0)
+                        Gd[16 * ct + l16] = gs;
+                }
                 // token r = l16, key channels cc + j
                 const int r = l16, cc = 16 * ct + 4 * g4, o = r * L::OS + cc;
                 const f32x4 gm = *reinterpret_cast<const f32x4 *>(Gam + cc);
@@ -821,15 +833,6 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 }
             }
         }
-        // rowsum(D (.) S) per key channel
-        if (t < DK) {
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < kNV; j += 4)
-                sacc += *reinterpret_cast<const f32x4 *>(Ds + t * L::SS + j) *
-                        *reinterpret_cast<const f32x4 *>(Ss + t * L::SS + j);
-            Gd[t] = (sacc[0] + sacc[1]) + (sacc[2] + sacc[3]);
-        }
         __syncthreads();
         // dg: the last token's extra terms, then a reverse cumulative sum; thread
         // (c, part) writes the part's tokens and first sums the tokens after them
@@ -861,8 +864,8 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         //      ct = w, w + 4 over all 64 value columns, as four column-interleaved
         //      16 x 16 tiles (tile e: columns 4 n + e, n = l16), so one 16-byte read
         //      of a dO or dX row feeds four MFMAs and D moves 16 bytes at a time.
-        //      (rowsum above read D; every row below is read and rewritten by one wave)
-        __syncthreads();
+        //      No barrier: the parameter gradients read these D rows in this same
+        //      wave, and nothing between them writes what this update reads.
 #pragma unroll 1
         for (int ct = w; ct < DK / 16; ct += 4) {
             f32x4 acc[4];                                 // acc[e][jj] = D[16 ct + 4 g4 + jj][4 l16 + e]
