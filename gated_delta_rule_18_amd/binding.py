@@ -29,7 +29,7 @@ KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 NOALLOC_SCRATCH_BYTES = 64 << 20      # KDA_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
-           "kda_chunk_fwd_snapshots",
+           "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size", "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
            "kda_validate_inputs", "kda_version")
 
@@ -62,6 +62,11 @@ def lib():
         L.kda_chunk_fwd_snapshots.argtypes = [vp] * 9 + [i] * 9 + [vp]
         L.kda_chunk_fwd_ex.restype = i
         L.kda_chunk_fwd_ex.argtypes = [vp] * 9 + [i] * 9 + [ctypes.POINTER(FwdOptions), vp]
+        L.kda_chunk_fwd_gated.restype = i
+        L.kda_chunk_fwd_gated.argtypes = ([vp] * 8 + [ctypes.c_float] + [vp] * 3 + [ctypes.c_size_t] + [i] * 6
+                                          + [ctypes.POINTER(FwdOptions), vp])
+        L.kda_chunk_fwd_gated_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_fwd_gated_workspace_size.argtypes = [i] * 3
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
         L.kda_decode_step_gated.restype = i
@@ -179,6 +184,50 @@ def _chunk_fwd(q, k, v, g, beta, S0, chunk, o, S_T, return_state, snaps, snap_ev
                                  _ptr(S_T), B, T, H, dk, dv, code, int(chunk), _stream(dev))
     _check(rc)
     return o, S_T, snaps
+
+
+def chunk_fwd_gated(q, k, v, g, beta, S0, gate, norm_w=None, eps=1e-6, y=None, S_T=None, return_state=True,
+                    workspace=None, spin_limit=None):
+    """Prefill with the output exposure gate fused: returns (y [B,T,H,dv], S_T or None),
+    y = Sigmoid(gate) * RMSNorm(o) * norm_w with o the prefill's readout -- the same
+    bits as output_gate(chunk_fwd(...)[0], gate, norm_w, eps).  gate [B,T,H,dv] like v;
+    norm_w fp32 [dv] or None (ones).  workspace: a uint8 device tensor of at least
+    gated_workspace_size(B, H, dv) bytes, or None (allocated here).  spin_limit
+    (testing): see kda_chunk_fwd_ex."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for name, t, shp in (("q", q, (B, T, H, dk)), ("k", k, (B, T, H, dk)), ("g", g, (B, T, H, dk)),
+                         ("v", v, (B, T, H, dv)), ("beta", beta, (B, T, H)), ("gate", gate, (B, T, H, dv))):
+        _want(t, name, shp, dt, dev)
+    if S0 is not None:
+        _want(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if norm_w is not None:
+        _want(norm_w, "norm_w", (dv,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _want(y, "y", (B, T, H, dv), dt, dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _want(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    need = gated_workspace_size(B, H, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    opts = FwdOptions(spin_limit=int(spin_limit)) if spin_limit is not None else None
+    rc = lib().kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(gate),
+                                   _ptr(norm_w), float(eps), _ptr(y), _ptr(S_T), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), B, T, H, dk, dv, code,
+                                   ctypes.byref(opts) if opts is not None else None, _stream(dev))
+    _check(rc)
+    return y, S_T
+
+
+def gated_workspace_size(B, H, dv):
+    """Bytes of workspace chunk_fwd_gated needs (kda_chunk_fwd_gated_workspace_size)."""
+    return int(lib().kda_chunk_fwd_gated_workspace_size(int(B), int(H), int(dv)))
 
 
 def _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T, return_dS0, out):

@@ -27,15 +27,14 @@ bool overlap(const void *a, long long na, const void *b, long long nb)
     return a && b && x < y + nb && y < x + na;
 }
 
-int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-              const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv, int dtype,
-              int chunk, const kda::Snapshots &snap, const kda::FwdOptions &opt, void *stream)
+// The checks every prefill entry shares (o: the output rows, o or y).
+int check_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+              const float *S0, const void *o, const float *S_T, int B, int T, int H, int dk, int dv,
+              int dtype)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return KDA_ERR_INVALID;
     if (dtype != KDA_BF16 && dtype != KDA_FP32)
-        return KDA_ERR_INVALID;
-    if (chunk != 16 && chunk != 32 && chunk != 64)
         return KDA_ERR_INVALID;
     if (!head_ok(dk) || !head_ok(dv))
         return KDA_ERR_UNSUPPORTED;
@@ -47,7 +46,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
     const bool has_tokens = (long long)B * T * H > 0;
     if (has_tokens && (!q || !k || !v || !g || !beta || !o))
         return KDA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, g, o, S0, S_T, snap.out};
+    const void *ptrs[] = {q, k, v, g, o, S0, S_T};
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return KDA_ERR_INVALID;
@@ -56,6 +55,21 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
     const long long state_bytes = (long long)B * H * dk * dv * 4;
     if (S0 != S_T && overlap(S0, state_bytes, S_T, state_bytes))
         return KDA_ERR_INVALID;
+    return KDA_OK;
+}
+
+int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+              const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv, int dtype,
+              int chunk, const kda::Snapshots &snap, const kda::FwdOptions &opt, void *stream)
+{
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return KDA_ERR_INVALID;
+    const int st = check_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype);
+    if (st != KDA_OK)
+        return st;
+    if (snap.out && !aligned16(snap.out))
+        return KDA_ERR_INVALID;
+    const long long state_bytes = (long long)B * H * dk * dv * 4;
     if (snap.count < 0)
         return KDA_ERR_INVALID;
     if (snap.count > 0) {
@@ -74,6 +88,49 @@ int chunk_fwd(const void *q, const void *k, const void *v, const void *g, const 
     hipError_t e = kda::launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
                                          dtype == KDA_FP32, ks, opt,
                                          reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int chunk_fwd_gated(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    const float *S0, const void *gate, const float *norm_w, float eps, void *y, float *S_T,
+                    void *workspace, size_t workspace_bytes, int B, int T, int H, int dk, int dv,
+                    int dtype, const kda::FwdOptions &opt, void *stream)
+{
+    const int st = check_fwd(q, k, v, g, beta, S0, y, S_T, B, T, H, dk, dv, dtype);
+    if (st != KDA_OK)
+        return st;
+    if (!(eps > 0.f) || !(eps < 1e30f))
+        return KDA_ERR_INVALID;
+    const long long rows = (long long)B * T * H;
+    if (rows == 0)
+        return kda::launch_chunk_fwd_gated(q, k, v, g, beta, S0, kda::OutputGate{}, y, S_T, nullptr, B, T, H,
+                                           dk, dv, dtype == KDA_FP32, opt,
+                                           reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                   ? KDA_OK
+                   : KDA_ERR_LAUNCH;
+    const size_t need = kda_chunk_fwd_gated_workspace_size(B, H, dv);
+    if (!gate || !aligned16(gate) || (norm_w && !aligned16(norm_w)) || !workspace || !aligned16(workspace) ||
+        workspace_bytes < need)
+        return KDA_ERR_INVALID;
+    // y is written while the inputs are still being read: it may overlap none of
+    // them, nor the workspace or the states
+    const long long es = dtype == KDA_FP32 ? 4 : 2;
+    const long long sb = (long long)B * H * dk * dv * 4;
+    const void *in[] = {q, k, v, g, beta, gate, norm_w, S0, S_T};
+    const long long in_n[] = {rows * dk * es, rows * dk * es, rows * dv * es, rows * dk * es, rows * es,
+                              rows * dv * es, (long long)dv * 4, sb, sb};
+    for (int j = 0; j < 9; ++j)
+        if (overlap(y, rows * dv * es, in[j], in_n[j]) || overlap(workspace, (long long)need, in[j], in_n[j]))
+            return KDA_ERR_INVALID;
+    if (overlap(y, rows * dv * es, workspace, (long long)need))
+        return KDA_ERR_INVALID;
+    kda::OutputGate og;
+    og.gate = gate;
+    og.w = norm_w;
+    og.eps = eps;
+    hipError_t e = kda::launch_chunk_fwd_gated(q, k, v, g, beta, S0, og, y, S_T, static_cast<int *>(workspace), B,
+                                               T, H, dk, dv, dtype == KDA_FP32, opt,
+                                               reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -237,6 +294,28 @@ int kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const void *g,
         opt.spin_limit = opts->spin_limit;
     }
     return chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype, chunk, snap, opt, stream);
+}
+
+size_t kda_chunk_fwd_gated_workspace_size(int B, int H, int dv)
+{
+    if (B < 0 || H < 0 || !head_ok(dv))
+        return 0;
+    return (size_t)B * H * (dv / 64) * 4 * sizeof(int);
+}
+
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                        const float *S0, const void *gate, const float *norm_w, float eps, void *y,
+                        float *S_T, void *workspace, size_t workspace_bytes, int B, int T, int H, int dk,
+                        int dv, int dtype, const kda_fwd_options *opts, void *stream)
+{
+    kda::FwdOptions opt;
+    if (opts) {
+        if (opts->spin_limit < -1)
+            return KDA_ERR_INVALID;
+        opt.spin_limit = opts->spin_limit;
+    }
+    return chunk_fwd_gated(q, k, v, g, beta, S0, gate, norm_w, eps, y, S_T, workspace, workspace_bytes, B, T,
+                           H, dk, dv, dtype, opt, stream);
 }
 
 int kda_decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,

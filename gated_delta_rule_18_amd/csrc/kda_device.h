@@ -99,6 +99,16 @@ __device__ __forceinline__ float rcp_acc(float x)
     return __builtin_fmaf(__builtin_fmaf(-x, r, 1.f), r, r);
 }
 
+// The output exposure gate (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读",
+// section 3.2, output equation), as every kernel that applies it evaluates it:
+// r = 1 / sqrt(ss / n + eps) for a (row, head) whose n readout values have the
+// sum of squares ss, then y = Sigmoid(gate) * o * r * w per element.
+__device__ __forceinline__ float gate_rms(float ss, float inv_n, float eps) { return rsqrtf(ss * inv_n + eps); }
+__device__ __forceinline__ float gate_elem(float o, float gt, float r, float w)
+{
+    return __builtin_amdgcn_rcpf(1.0f + exp_f(-gt)) * o * r * w;
+}
+
 // Sum over the 64 lanes of a wavefront (result valid in every lane).
 __device__ __forceinline__ float wave_sum(float x)
 {

@@ -84,13 +84,11 @@ __device__ __forceinline__ void gate_unit(const Oct<E> &xo, const Oct<E> &xg, co
 #pragma unroll
     for (int off = LPU / 2; off > 0; off >>= 1)
         ss += __shfl_xor(ss, off, 64);
-    const float r = rsqrtf(ss * (1.0f / DV) + eps);
+    const float r = gate_rms(ss, 1.0f / DV, eps);
     float yv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float s = __builtin_amdgcn_rcpf(1.0f + exp_f(-xg.get(i)));
-        yv[i] = s * x[i] * r * wv[i];
-    }
+    for (int i = 0; i < 8; ++i)
+        yv[i] = gate_elem(x[i], xg.get(i), r, wv[i]);
     Oct<E>::store(dst, yv);
 }
 

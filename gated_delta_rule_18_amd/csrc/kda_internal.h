@@ -60,6 +60,15 @@ hipError_t launch_decode_step(const void *q_pre, const void *k_pre, const void *
                               int N, int H, int dk, int dv, bool fp32, const OutputGate &og,
                               hipStream_t stream);
 
+// The prefill with the output exposure gate fused (kda_chunk_fwd_gated): y
+// receives Sigmoid(gate) * o / sqrt(mean o^2 + eps) * w per (token, head) in
+// place of o; pub holds B * H * (dv / 64) * 4 ints of scratch (the consumers'
+// progress words, cleared by the launch).
+hipError_t launch_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, const float *S0, const OutputGate &og, void *y,
+                                  float *S_T, int *pub, int B, int T, int H, int dk, int dv, bool fp32,
+                                  const FwdOptions &opt, hipStream_t stream);
+
 // Backward pass: gradients (fp32) of <dO, o> + <dS_T, S_T> through kda_chunk_fwd.
 // workspace holds chunk_bwd_workspace_floats(...) floats.
 size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);

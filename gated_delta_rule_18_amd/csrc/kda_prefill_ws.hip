@@ -65,9 +65,15 @@ template <typename E> struct Np { static constexpr int v = sizeof(E) == 2 ? 8 : 
 constexpr int kC = 16;                 // tokens per chunk
 constexpr int kVS = 64;                // value columns per workgroup
 constexpr int kXCDs = 8;
+constexpr int kCUs = 256;
 constexpr int kSpinLimit = 1 << 22;     // polls before a hand-off wait gives up
 // s_waitcnt operand: vector-memory count 0, the other counters unconstrained
 constexpr int kVmcntZero = 0x0F70;
+// the same with at most 10 vector-memory operations outstanding (see kPubLag)
+constexpr int kVmcntPub = 0x0F70 | 10;
+// buffer-load cache policy of the gate workers' reads of what other CUs wrote:
+// device scope, so the CU's own L1 never serves them
+constexpr int kLoadDevice = 16;
 
 // LDS layout.  Every MFMA operand is stored as the register image the reading
 // wavefront loads (one contiguous 16- or 8-byte piece per lane), padded so that
@@ -399,12 +405,152 @@ __device__ __forceinline__ void load_chunk(RawC<E> &R, const E *q, const E *k, c
     R.b = load_bits(rb, (lane & 15) * H * ES, 0, (E *)nullptr);
 }
 
-template <typename E, int DK>
+// ---- the fused output gate (kda_chunk_fwd_gated) ------------------------------
+// Page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 3.2, output
+// equation: y = Sigmoid(gate) * RMSNorm(o~) * w per (token, head), the norm over
+// the head's dv readout columns -- which two value-slice workgroups produce.
+// Consumer wavefront w of (head bh, slice) publishes in
+// pub[(bh * nsl + slice) * 4 + w] how many of its chunks' o tiles have reached
+// the L2, two chunks behind its stores (kPubLag).  Workgroups past the prefill
+// grid are gate workers: each of their wavefronts takes (chunk, head) items of
+// the heads whose workgroups run on its own XCD (the L2 that holds their tiles),
+// in chunk order, waits until every consumer of the item's head has published
+// the chunk, and overwrites the chunk's 16 rows of o with y in place.  The
+// workers fill CUs the prefill grid leaves idle, and on each XCD they are
+// dispatched after every prefill workgroup (workgroups start in index order),
+// so the heads they wait for are already running and every wait ends; the
+// waits are bounded all the same, and an item whose wait gives up is written
+// as NaN (as is every later item of that wavefront).
+constexpr int kPubLag = 2;
+
+// One row piece of 8 elements (16 bytes in bf16, 32 in fp32).
+template <typename E> struct Oct8;
+template <> struct Oct8<__bf16> {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    u4 r;
+    template <int AUX>
+    static __device__ __forceinline__ Oct8 load(__amdgpu_buffer_rsrc_t rs, int voff)
+    {
+        return Oct8{(u4)__builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, AUX)};
+    }
+    __device__ __forceinline__ float get(int i) const
+    {
+        const unsigned x = r[i >> 1];
+        return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int voff, const float *v)
+    {
+        u4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = Pair<__bf16>::pack(v[2 * i], v[2 * i + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rs, voff, 0, 0);
+    }
+};
+template <> struct Oct8<float> {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    u4 a, b;
+    template <int AUX>
+    static __device__ __forceinline__ Oct8 load(__amdgpu_buffer_rsrc_t rs, int voff)
+    {
+        return Oct8{(u4)__builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, AUX),
+                    (u4)__builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, 0, AUX)};
+    }
+    __device__ __forceinline__ float get(int i) const { return __uint_as_float(i < 4 ? a[i] : b[i - 4]); }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t rs, int voff, const float *v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(u4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                  __float_as_uint(v[3])},
+                                               rs, voff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                                  __float_as_uint(v[7])},
+                                               rs, voff + 16, 0, 0);
+    }
+};
+
+// Gate wavefront jw of the nw on XCD xcd.  Lane (sub, slot): LPU = DV / 8 lanes
+// own one row, 8 contiguous elements each; a wavefront covers UPW rows at a
+// time, NPASS passes per 16-row item, all loads of an item issued first.  The
+// row's sum of squares is reduced over its LPU lanes with xor shuffles (which
+// stay inside the row's aligned lane group).  Rows past T fall outside the
+// item's buffers: their loads read 0 and their stores are dropped.
+template <typename E, int DV>
+__device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w, float eps, const int *pub,
+                                            int jw, int nw, int xcd, int nbh, int H, int T, int nsl,
+                                            int spin_limit)
+{
+    constexpr int ES = (int)sizeof(E), LPU = DV / 8, UPW = 64 / LPU, NPASS = kC / UPW;
+    const int lane = threadIdx.x & 63, sub = lane % LPU, slot = lane / LPU;
+    float wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        wv[i] = w ? w[8 * sub + i] : 1.f;
+    const int nhx = nbh > xcd ? (nbh - xcd + kXCDs - 1) / kXCDs : 0;   // heads on this XCD
+    const int nchunks = (T + kC - 1) / kC;
+    const long items = (long)nhx * nchunks;
+    const int nf = 4 * nsl;                                            // consumers per head
+    const int rs = H * DV * ES;                                        // bytes between token rows
+    const float nanv = __builtin_nanf("");
+    bool aborted = false;
+    for (long it = jw; it < items; it += nw) {
+        const int c = (int)(it / nhx), bh = xcd + kXCDs * (int)(it % nhx);
+        const int b = bh / H, h = bh % H;
+        const int t0 = c * kC, n = T - t0 < kC ? T - t0 : kC;
+        if (!aborted) {
+            const __amdgpu_buffer_rsrc_t rp = buffer(pub + (long)bh * nf, nf * 4);
+            int spins = 0;
+            for (;;) {
+                const int f = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, lane * 4, 0, kLoadDevice);
+                if (__builtin_amdgcn_ballot_w64(lane < nf && f <= c) == 0)
+                    break;
+                if (++spins > spin_limit) {
+                    aborted = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        const long row0 = ((long)b * T + t0) * H + h;
+        const __amdgpu_buffer_rsrc_t ry = buffer(y + row0 * DV, rows_bytes(n, rs, DV * ES));
+        const __amdgpu_buffer_rsrc_t rg = buffer(gate + row0 * DV, rows_bytes(n, rs, DV * ES));
+        Oct8<E> xo[NPASS], xg[NPASS];
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int voff = (slot + UPW * p) * rs + 8 * sub * ES;
+            xo[p] = Oct8<E>::template load<kLoadDevice>(ry, voff);
+            xg[p] = Oct8<E>::template load<2>(rg, voff);     // read once: non-temporal
+        }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            float x[8], ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = xo[p].get(i);
+                ss += x[i] * x[i];
+            }
+#pragma unroll
+            for (int off = LPU / 2; off > 0; off >>= 1)
+                ss += __shfl_xor(ss, off, 64);
+            const float rr = gate_rms(ss, 1.0f / DV, eps);
+            float yv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                yv[i] = aborted ? nanv : gate_elem(x[i], xg[p].get(i), rr, wv[i]);
+            Oct8<E>::store(ry, (slot + UPW * p) * rs + 8 * sub * ES, yv);
+        }
+    }
+}
+
+// GATED: the fused output gate -- o is y's buffer (the consumers' tiles, gated
+// in place by the workers), the consumers publish their progress in pub, and the
+// workgroups from grid_p on are gate workers (ngate of them, a multiple of 8).
+template <typename E, int DK, bool GATED>
 __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
-    const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *__restrict__ o,
+    const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *o,
     float *S_T, float *snaps, int snap_chunks, int n_snaps, int snap_packed, int T, int H, int DV, int nbh,
-    int nsl, int spin_limit)
+    int nsl, int spin_limit, int *pub, const E *gate, const float *gate_w, float gate_eps, int grid_p,
+    int ngate)
 {
     typedef WsL<E, DK> L;
     typedef typename Vec<E>::v4 V4;
@@ -421,6 +567,19 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
 
     // workgroup -> (head, value slice); slices of a head share an XCD's L2
     const int id = blockIdx.x, xcd = id % kXCDs, rr = id / kXCDs;
+    if constexpr (GATED) {
+        if (id >= grid_p) {
+            // grid_p is a multiple of 8: worker j = id - grid_p runs on XCD j % 8
+            const int waves = 4 + L::NP, j = id - grid_p;
+            const int jw = (j / kXCDs) * waves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+            const int nw = (ngate / kXCDs) * waves;
+            if (DV == 128)
+                gate_worker<E, 128>(o, gate, gate_w, gate_eps, pub, jw, nw, xcd, nbh, H, T, nsl, spin_limit);
+            else
+                gate_worker<E, 64>(o, gate, gate_w, gate_eps, pub, jw, nw, xcd, nbh, H, T, nsl, spin_limit);
+            return;
+        }
+    }
     const int bh = (rr / nsl) * kXCDs + xcd, slice = rr % nsl;
     if (bh >= nbh)
         return;
@@ -466,6 +625,11 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         // falls outside an empty buffer and is dropped
         const int ofull = o ? rows_bytes(kC, rso, 16 * L::ES) : 0;
         const int olast = o ? rows_bytes(T - (nchunks - 1) * kC, rso, 16 * L::ES) : 0;
+        // gated: this wavefront's progress word (lane 0 writes it; the other
+        // lanes' offsets fall outside the 4-byte buffer)
+        __amdgpu_buffer_rsrc_t rpub;
+        if constexpr (GATED)
+            rpub = buffer(pub + ((long)bh * nsl + slice) * 4 + w, 4);
 
         // this lane's byte offsets inside a slot: image16 pieces (Kt, Qt),
         // image4 pieces (Ke^T, V^T, T, M) and the Gam pair (see decay_rows)
@@ -595,6 +759,18 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
             const __amdgpu_buffer_rsrc_t ro = buffer(o ? o + ooff : o, c + 1 < nchunks ? ofull : olast);
             store_o(ro, ovo, rso, aborted ? nan4 : O, (E *)nullptr);
             ooff += ostep;
+            if constexpr (GATED) {
+                // Per chunk this wavefront issues 4 o stores and this 1 progress
+                // store (and no other vector-memory operation: the gated entry
+                // writes no snapshots), so once at most 10 are outstanding the
+                // o tiles of chunk c - 2 and all before it are in the L2.
+                __builtin_amdgcn_s_waitcnt(kVmcntPub);
+                __builtin_amdgcn_raw_buffer_store_b32(c + 1 - kPubLag > 0 ? c + 1 - kPubLag : 0, rpub, 4 * lane, 0, 0);
+            }
+        }
+        if constexpr (GATED) {
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            __builtin_amdgcn_raw_buffer_store_b32(nchunks, rpub, 4 * lane, 0, 0);
         }
         if (S_T) {
             aborted |= ld_flag(abort_flag) != 0;
@@ -851,27 +1027,48 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         produce(raw, c);
 }
 
-template <typename E, int DK>
+// pub[i] = 0 for i < n (the consumers' progress words of one gated call)
+__global__ __launch_bounds__(256) void zero_pub(int *pub, long n)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        pub[i] = 0;
+}
+
+// The launch: og == nullptr for the plain prefill, else the gated one (o is then
+// y's buffer and pub the caller's nbh * nsl * 4 progress words).
+template <typename E, int DK, bool GATED>
 hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g, const void *beta,
                      const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
-                     const Snapshots &snap, int spin_limit, hipStream_t stream)
+                     const Snapshots &snap, int spin_limit, const OutputGate *og, int *pub, hipStream_t stream)
 {
     typedef WsL<E, DK> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    // above half the LDS: one workgroup per CU, so a gate worker never shares a
+    // CU with a prefill workgroup
     constexpr int lds = L::bytes > 81 * 1024 ? L::bytes : 81 * 1024;
     // a per-device function attribute: set on every call (cheap, and correct
     // whichever device and thread the call comes from)
-    hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK>,
+    hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK, GATED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess)
         return e;
     const int nbh = B * H, nsl = dv / kVS;
-    const int grid = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
-    hipLaunchKernelGGL((prefill_ws_kernel<E, DK>), dim3(grid), dim3(64 * (4 + L::NP)), lds, stream,
-                       (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
+    const int grid_p = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
+    int ngate = 0;
+    if constexpr (GATED) {
+        // the CUs the prefill grid leaves idle, at least 8 per XCD (which start as
+        // prefill workgroups finish when the grid fills the chip)
+        ngate = kCUs - grid_p > 64 ? ((kCUs - grid_p) / kXCDs) * kXCDs : 64;
+        const long npub = (long)nbh * nsl * 4;
+        hipLaunchKernelGGL(zero_pub, dim3((unsigned)((npub + 255) / 256)), dim3(256), 0, stream, pub, npub);
+    }
+    hipLaunchKernelGGL((prefill_ws_kernel<E, DK, GATED>), dim3(grid_p + ngate), dim3(64 * (4 + L::NP)), lds,
+                       stream, (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
                        (E *)o, S_T, snap.count > 0 || snap.packed ? snap.out : nullptr, snap.every_chunks,
                        snap.count, snap.packed ? 1 : 0, T, H, dv, nbh, nsl,
-                       spin_limit < 0 ? kSpinLimit : spin_limit);
+                       spin_limit < 0 ? kSpinLimit : spin_limit, pub, og ? (const E *)og->gate : nullptr,
+                       og ? og->w : nullptr, og ? og->eps : 0.f, grid_p, ngate);
     return hipGetLastError();
 }
 
@@ -891,10 +1088,14 @@ hipError_t launch_chunk16(const void *q, const void *k, const void *v, const voi
                           int spin_limit)
 {
     if (fp32)
-        return dk == 128 ? launch_ws<float, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream)
-                         : launch_ws<float, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream);
-    return dk == 128 ? launch_ws<__bf16, 128>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream)
-                     : launch_ws<__bf16, 64>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit, stream);
+        return dk == 128 ? launch_ws<float, 128, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                        nullptr, nullptr, stream)
+                         : launch_ws<float, 64, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                       nullptr, nullptr, stream);
+    return dk == 128 ? launch_ws<__bf16, 128, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                     nullptr, nullptr, stream)
+                     : launch_ws<__bf16, 64, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                    nullptr, nullptr, stream);
 }
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -913,6 +1114,26 @@ hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const v
         return hipGetLastError();
     }
     return launch_chunk16(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, snap, stream, opt.spin_limit);
+}
+
+hipError_t launch_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, const float *S0, const OutputGate &og, void *y,
+                                  float *S_T, int *pub, int B, int T, int H, int dk, int dv, bool fp32,
+                                  const FwdOptions &opt, hipStream_t stream)
+{
+    if ((long)B * H == 0)
+        return hipSuccess;
+    if (T == 0) {
+        const Snapshots none;
+        return launch_chunk_fwd(q, k, v, g, beta, S0, y, S_T, B, T, H, dk, dv, fp32, none, opt, stream);
+    }
+    const Snapshots none;
+    const int sl = opt.spin_limit;
+    if (fp32)
+        return dk == 128 ? launch_ws<float, 128, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream)
+                         : launch_ws<float, 64, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream);
+    return dk == 128 ? launch_ws<__bf16, 128, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream)
+                     : launch_ws<__bf16, 64, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream);
 }
 
 } // namespace kda

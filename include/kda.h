@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 120 /* 1.2.0 */
+#define KDA_VERSION 130 /* 1.3.0 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -264,6 +264,44 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
                           const void *gate, const float *norm_w, float eps, void *y,
                           int N, int H, int dk, int dv, int width, int dtype,
                           void *stream);
+
+/*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd with the output exposure gate fused: the
+ * call writes y = Sigmoid(gate) * RMSNorm(o~) * w (as kda_output_gate defines
+ * it, page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 3.2,
+ * output equation) for every (token, head), bit for bit what kda_chunk_fwd
+ * followed by kda_output_gate writes.  The prefill writes each 16-token block
+ * of o~ into y, and workgroups of the same launch, on CUs the prefill leaves
+ * idle, gate the block in place once both value halves of its head are there,
+ * reading it back from the L2 rather than from HBM.
+ *
+ * Arguments as kda_chunk_fwd (the 16-token kernel; there is no chunk argument),
+ * with o replaced by
+ *   gate      : [B, T, H, dv] (dtype)   gate pre-activation W_g x_t
+ *   norm_w    : [dv] fp32               RMSNorm weight; NULL = all ones
+ *   eps       : > 0
+ *   y         : [B, T, H, dv] (dtype)   written; must not overlap any other buffer
+ *   workspace : device memory of at least kda_chunk_fwd_gated_workspace_size(B, H, dv)
+ *               bytes (the prefill's progress counters), 16-byte aligned, owned by
+ *               the caller; its contents before the call do not matter and after it
+ *               are unspecified.  Calls that may run at the same time need separate
+ *               workspaces.
+ *   opts      : NULL = defaults, else as kda_chunk_fwd_ex; spin_limit bounds the
+ *               gate's waits for the prefill too, and a block whose wait gave up
+ *               is written as NaN.
+ * Errors: as kda_chunk_fwd; KDA_ERR_INVALID also for a null or misaligned gate or
+ * workspace, a workspace below the size above, a misaligned norm_w, a bad eps,
+ * spin_limit < -1 or overlapping buffers.
+ */
+int kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const void *g,
+                        const void *beta, const float *S0, const void *gate,
+                        const float *norm_w, float eps, void *y, float *S_T,
+                        void *workspace, size_t workspace_bytes,
+                        int B, int T, int H, int dk, int dv, int dtype,
+                        const kda_fwd_options *opts, void *stream);
+
+/* Bytes of workspace kda_chunk_fwd_gated needs for these sizes (0 for invalid sizes). */
+size_t kda_chunk_fwd_gated_workspace_size(int B, int H, int dv);
 
 /*
  * kda_chunk_bwd -- backward pass of one KDA layer's recurrence (training).

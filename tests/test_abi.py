@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 120
+    assert binding.version() == 130
     L = binding.lib()
     for code in (0, -1, -2, -3, -4, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
@@ -211,6 +211,52 @@ def test_output_gate_rejects(kw, code):
 def test_output_gate_in_place_and_empty_are_accepted():
     assert _gate(rows=0, o=None, gate=None, y=None) == 0
     assert _gate(H=0) == 0
+
+
+def _fwd_gated(**kw):
+    big = 1 << 24
+    args = dict(q=A, k=A + big, v=A + 2 * big, g=A + 3 * big, beta=A + 4 * big, S0=A + 5 * big,
+                gate=A + 6 * big, w=A + 7 * big, eps=1e-6, y=A + 8 * big, S_T=A + 9 * big, ws=A + 10 * big,
+                wsb=1 << 12, B=1, T=8, H=2, dk=64, dv=64, dtype=0, spin=None, stream=None)
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    opts = ctypes.byref(binding.FwdOptions(spin_limit=args["spin"])) if args["spin"] is not None else None
+    return binding.lib().kda_chunk_fwd_gated(
+        vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]), vp(args["beta"]), vp(args["S0"]),
+        vp(args["gate"]), vp(args["w"]), args["eps"], vp(args["y"]), vp(args["S_T"]), vp(args["ws"]),
+        args["wsb"], args["B"], args["T"], args["H"], args["dk"], args["dv"], args["dtype"], opts,
+        args["stream"])
+
+
+def test_fwd_gated_workspace_size():
+    # one progress counter per (sequence, head, 64-column value slice, consumer wavefront)
+    assert binding.gated_workspace_size(2, 3, 128) == 2 * 3 * 2 * 4 * 4
+    assert binding.gated_workspace_size(2, 3, 64) == 2 * 3 * 1 * 4 * 4
+    L = binding.lib()
+    assert L.kda_chunk_fwd_gated_workspace_size(2, 3, 96) == 0
+    assert L.kda_chunk_fwd_gated_workspace_size(-1, 3, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate=None), -1), (dict(gate=MIS), -1), (dict(w=MIS), -1), (dict(eps=0.0), -1),
+    (dict(eps=float("inf")), -1), (dict(y=None), -1), (dict(y=MIS), -1), (dict(ws=None), -1),
+    (dict(ws=MIS), -1), (dict(wsb=2 * 4 * 4 - 1), -1), (dict(spin=-2), -1), (dict(dtype=2), -1),
+    (dict(dk=96), -2), (dict(dv=32), -2), (dict(B=65536), -1), (dict(H=70000), -1),
+    (dict(y=A + 64), -1),                        # y overlapping q
+    (dict(y=A + 6 * (1 << 24) + 16), -1),        # y overlapping gate
+    (dict(ws=A + 8 * (1 << 24) + 16), -1),       # the workspace inside y
+    (dict(ws=A + 5 * (1 << 24)), -1),            # the workspace over S0
+    (dict(S_T=A + 5 * (1 << 24) + 64), -1),      # S_T partly overlapping S0
+])
+def test_fwd_gated_rejects(kw, code):
+    assert _fwd_gated(**kw) == code
+
+
+def test_fwd_gated_smallest_workspace_and_empty_calls():
+    # exactly the workspace size passes validation; nothing is launched for an empty batch
+    # or (S_T = S0, T = 0) an empty sequence
+    assert _fwd_gated(B=0, wsb=0, ws=None, gate=None) == 0
+    assert _fwd_gated(T=0, S_T=A + 5 * (1 << 24), ws=None, gate=None) == 0
 
 
 def _decode_gated(**kw):
