@@ -353,10 +353,11 @@ struct Part {
     f32x4 q[NCW], k[NCW];            // key channels 16 (w + 4 i) + 4 g4 + j of token l16
 
     // this thread's values of chunk t0 .. t0 + n - 1 from slice 0's partials
-    // (device-scope loads; rows past n read 0), or NaN when slice 0 never
-    // published them
+    // (device-scope loads; rows past n read 0).  The loads are unconditional and
+    // land straight in the registers that hold them until the sum: a value chosen
+    // after the load (NaN or the load) would be a copy that waits for it.
     __device__ __forceinline__ void load(const float *pq, const float *pk, const float *pg, const float *pb,
-                                         long tokb, int t0, int n, int H, int h, int t, bool nan)
+                                         long tokb, int t0, int n, int H, int h, int t)
     {
         const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
         const int pc = t % DK, pr0 = (t / DK) * TPP;
@@ -365,14 +366,12 @@ struct Part {
         const __amdgpu_buffer_rsrc_t rk = rows_out(const_cast<float *>(pk) + rowb, n, (long)H * DK * 4, DK * 4);
         const __amdgpu_buffer_rsrc_t rg = rows_out(const_cast<float *>(pg) + rowb, n, (long)H * DK * 4, DK * 4);
         const __amdgpu_buffer_rsrc_t rb = rows_out(const_cast<float *>(pb) + (tokb + t0) * H + h, n, (long)H * 4, 4);
-        const float nanv = __builtin_nanf("");
         auto ld = [&](__amdgpu_buffer_rsrc_t r, int voff) {
-            return nan ? nanv : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kLoadDevice));
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kLoadDevice));
         };
         auto ld4 = [&](__amdgpu_buffer_rsrc_t r, int voff) {
             typedef unsigned u4 __attribute__((ext_vector_type(4)));
-            return nan ? f32x4{nanv, nanv, nanv, nanv}
-                       : __builtin_bit_cast(f32x4, (u4)__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadDevice));
+            return __builtin_bit_cast(f32x4, (u4)__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kLoadDevice));
         };
         b = ld(rb, (lane & 15) * H * 4);
 #pragma unroll
@@ -385,9 +384,10 @@ struct Part {
         for (int u = 0; u < TPP; ++u)
             g[u] = ld(rg, ((pr0 + u) * H * DK + pc) * 4);
     }
-    // the gradients of that chunk: slice 0's values (this) + slice 1's (own)
+    // the gradients of that chunk: slice 0's values (this) + slice 1's (own),
+    // + mark: 0, or NaN once slice 1 gave up waiting for slice 0's partials
     __device__ __forceinline__ void store_sum(const Part &own, float *oq, float *ok, float *og, float *ob,
-                                              long tokb, int t0, int n, int H, int h, int t) const
+                                              long tokb, int t0, int n, int H, int h, int t, float mark) const
     {
         const int w = t >> 6, lane = t & 63, l16 = lane & 15, g4 = lane >> 4;
         const int pc = t % DK, pr0 = (t / DK) * TPP;
@@ -397,17 +397,18 @@ struct Part {
         const __amdgpu_buffer_rsrc_t rg = rows_out(og + rowb, n, (long)H * DK * 4, DK * 4);
         if (w == 1 && lane < kC) {
             const __amdgpu_buffer_rsrc_t rb = rows_out(ob + (tokb + t0) * H + h, n, (long)H * 4, 4);
-            st_out(rb, lane * H * 4, b + own.b);
+            st_out(rb, lane * H * 4, b + own.b + mark);
         }
 #pragma unroll
         for (int i = 0; i < NCW; ++i) {
             const int off = (l16 * H * DK + 16 * (w + 4 * i) + 4 * g4) * 4;
-            st_out4(rq, off, q[i] + own.q[i]);
-            st_out4(rk, off, k[i] + own.k[i]);
+            const f32x4 m4 = {mark, mark, mark, mark};
+            st_out4(rq, off, q[i] + own.q[i] + m4);
+            st_out4(rk, off, k[i] + own.k[i] + m4);
         }
 #pragma unroll
         for (int u = 0; u < TPP; ++u)
-            st_out(rg, ((pr0 + u) * H * DK + pc) * 4, g[u] + own.g[u]);
+            st_out(rg, ((pr0 + u) * H * DK + pc) * 4, g[u] + own.g[u] + mark);
     }
 };
 
@@ -636,8 +637,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
         __syncthreads();
         if (summer && ci + 2 < nchunks)
-            part.load(pq, pk, pg, pb, tokb, t0 + 2 * kC, T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t,
-                      *abort_flag != 0);
+            part.load(pq, pk, pg, pb, tokb, t0 + 2 * kC, T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t);
         // ---- dX = Tm^T dU (= dV) -----------------------------------------------------
         {
             const f32x4 dx = mmk<kC, 2>(Tm, 1, L::MS, dUs + 16 * w, L::CS, 1, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -856,7 +856,8 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         if (summer) {
             if (ci + 2 < nchunks)
                 part.store_sum(prev2, oq, ok, og, ob, tokb, t0 + 2 * kC,
-                               T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t);
+                               T - t0 - 2 * kC < kC ? T - t0 - 2 * kC : kC, H, h, t,
+                               *abort_flag != 0 ? __builtin_nanf("") : 0.f);
             prev2 = prev1;
             prev1 = own;
         }
@@ -924,15 +925,15 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                 }
             }
             __syncthreads();
-            const bool ab = *abort_flag != 0;
+            const float mark = *abort_flag != 0 ? __builtin_nanf("") : 0.f;
             if (nchunks > 1) {
                 const int n1 = T - kC < kC ? T - kC : kC;
-                part.load(pq, pk, pg, pb, tokb, kC, n1, H, h, t, ab);
-                part.store_sum(prev2, oq, ok, og, ob, tokb, kC, n1, H, h, t);
+                part.load(pq, pk, pg, pb, tokb, kC, n1, H, h, t);
+                part.store_sum(prev2, oq, ok, og, ob, tokb, kC, n1, H, h, t, mark);
             }
             const int n0 = T < kC ? T : kC;
-            part.load(pq, pk, pg, pb, tokb, 0, n0, H, h, t, ab);
-            part.store_sum(prev1, oq, ok, og, ob, tokb, 0, n0, H, h, t);
+            part.load(pq, pk, pg, pb, tokb, 0, n0, H, h, t);
+            part.store_sum(prev1, oq, ok, og, ob, tokb, 0, n0, H, h, t, mark);
         }
     }
     if (dS0_out)
