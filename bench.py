@@ -20,6 +20,9 @@ torch.cuda.synchronize():
   gate     kda_output_gate on the prefill output shape (65536 tokens x 96 heads
            x 128, bf16), and kda_decode_step_gated on the decode batch (under
            "decode.gated");
+  gated    kda_chunk_fwd_gated, the prefill with the output gate fused, on the
+           prefill workload, next to kda_chunk_fwd + kda_output_gate on the same
+           inputs (each timed on its own);
   bwd      kda_chunk_bwd, the backward pass, on the B=4, H=32, T=4096,
            dk=dv=128 bf16 prefill shape (gradients fp32).
 Inputs are synthetic, seeded, and resident in HBM before the timed region.
@@ -310,6 +313,44 @@ def main():
                          "frac": s_gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": s_bytes},
         }
         del snaps
+    gated = None
+    if not args.skip_gate:
+        gk = GATE_K3
+        gi = gate_inputs(gk["rows"], gk["H"], gk["dv"], dtype=gk["dtype"], seed=gk["seed"], device=dev)
+        gate_t = gi["gate"].view(B, T, H, dv)
+        y = torch.empty_like(o)
+        gws = torch.empty(max(binding.gated_workspace_size(B, H, dv), 16), dtype=torch.uint8, device=dev)
+        del gi["o"]
+        torch.cuda.synchronize()
+
+        def gated_step(i=0):
+            binding.chunk_fwd_gated(x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gate_t, gi["norm_w"],
+                                    y=y, S_T=S_T, workspace=gws)
+
+        def gate_only(i=0):
+            binding.output_gate(o, gate_t, gi["norm_w"], y=y)
+
+        f_wall, f_kern = _timed(gated_step, args.steps, args.warmup, torch)
+        _, g_only = _timed(gate_only, args.steps, args.warmup, torch)
+        _, p_again = _timed(prefill_step, args.steps, args.warmup, torch)
+        f_bytes = p_bytes + gate_bytes(B * T, H, dv) - 2 * (B * T * H * dv * 2)   # o stays on chip
+        f_gbps = f_bytes / (f_kern * 1e-3) / 1e9
+        gated = {
+            "workload": f"k3_prefill with the output gate fused (kda_chunk_fwd_gated), gate ~ 2 N(0,1), "
+                        f"RMSNorm weight ~ 1 + 0.1 N(0,1), eps 1e-6",
+            "ms_per_step": f_wall,
+            "kernel_ms": f_kern,
+            "tokens_per_s": B * T / (f_wall * 1e-3),
+            "two_pass_kernel_ms": p_again + g_only,
+            "two_pass_parts_ms": {"prefill": p_again, "gate": g_only},
+            "speedup_vs_two_pass": (p_again + g_only) / f_kern,
+            "roofline": {"bound": "hbm", "achieved": f_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": f_gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("prefill_gated_k3_hbm_counters.txt",
+                                                     ["kda_prefill_ws.hip", "kda_device.h"]),
+                         "bytes_per_launch": f_bytes},
+        }
+        del gi, gate_t, y, gws
     cpu = None if args.no_cpu else cpu_baseline(x, H)
     del x, o
 
@@ -572,6 +613,7 @@ def main():
         "snapshots": snapshots,
         "prep": prep,
         "gate": gate,
+        "gated": gated,
         "bwd": bwd,
         "configs": configs,
     }

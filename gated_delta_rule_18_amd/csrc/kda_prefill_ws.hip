@@ -470,10 +470,11 @@ template <> struct Oct8<float> {
 
 // Gate wavefront jw of the nw on XCD xcd.  Lane (sub, slot): LPU = DV / 8 lanes
 // own one row, 8 contiguous elements each; a wavefront covers UPW rows at a
-// time, NPASS passes per 16-row item, all loads of an item issued first.  The
-// row's sum of squares is reduced over its LPU lanes with xor shuffles (which
-// stay inside the row's aligned lane group).  Rows past T fall outside the
-// item's buffers: their loads read 0 and their stores are dropped.
+// time, NPASS passes per 16-row item.  The row's sum of squares is reduced over
+// its LPU lanes with xor shuffles (which stay inside the row's aligned lane
+// group).  Rows past T fall outside the item's buffers: their loads read 0 and
+// their stores are dropped.  Software-pipelined by one item: the progress words
+// and the gate rows of the next item are loaded before this item's y is stored.
 template <typename E, int DV>
 __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w, float eps, const int *pub,
                                             int jw, int nw, int xcd, int nbh, int H, int T, int nsl,
@@ -481,44 +482,79 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
 {
     constexpr int ES = (int)sizeof(E), LPU = DV / 8, UPW = 64 / LPU, NPASS = kC / UPW;
     const int lane = threadIdx.x & 63, sub = lane % LPU, slot = lane / LPU;
+    const int nhx = nbh > xcd ? (nbh - xcd + kXCDs - 1) / kXCDs : 0;   // heads on this XCD
+    const int nchunks = (T + kC - 1) / kC;
+    const long items = (long)nhx * nchunks;
+    if (jw >= items)
+        return;
     float wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         wv[i] = w ? w[8 * sub + i] : 1.f;
-    const int nhx = nbh > xcd ? (nbh - xcd + kXCDs - 1) / kXCDs : 0;   // heads on this XCD
-    const int nchunks = (T + kC - 1) / kC;
-    const long items = (long)nhx * nchunks;
     const int nf = 4 * nsl;                                            // consumers per head
     const int rs = H * DV * ES;                                        // bytes between token rows
+    const int lane_off = slot * rs + 8 * sub * ES;
     const float nanv = __builtin_nanf("");
+
+    // item it: chunk c of head bh, buffers over its n <= 16 rows
+    struct Item {
+        int c, bh;
+        __amdgpu_buffer_rsrc_t ry, rg, rp;
+    };
+    auto item = [&](long it) {
+        Item m;
+        m.c = (int)(it / nhx);
+        m.bh = xcd + kXCDs * (int)(it % nhx);
+        const int b = m.bh / H, h = m.bh % H, t0 = m.c * kC, n = T - t0 < kC ? T - t0 : kC;
+        const long row0 = ((long)b * T + t0) * H + h;
+        m.ry = buffer(y + row0 * DV, rows_bytes(n, rs, DV * ES));
+        m.rg = buffer(gate + row0 * DV, rows_bytes(n, rs, DV * ES));
+        m.rp = buffer(pub + (long)m.bh * nf, nf * 4);
+        return m;
+    };
+    auto ld_pub = [&](const Item &m) {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(m.rp, lane * 4, 0, kLoadDevice);
+    };
+
     bool aborted = false;
-    for (long it = jw; it < items; it += nw) {
-        const int c = (int)(it / nhx), bh = xcd + kXCDs * (int)(it % nhx);
-        const int b = bh / H, h = bh % H;
-        const int t0 = c * kC, n = T - t0 < kC ? T - t0 : kC;
-        if (!aborted) {
-            const __amdgpu_buffer_rsrc_t rp = buffer(pub + (long)bh * nf, nf * 4);
+    long it = jw;
+    Item m = item(it);
+    int f = ld_pub(m);
+    Oct8<E> xg[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+        xg[p] = Oct8<E>::template load<2>(m.rg, lane_off + UPW * p * rs);     // read once: non-temporal
+    for (;;) {
+        // every consumer of the head has published chunk c (the first test, of the
+        // words loaded one item ahead, sits outside the polling loop, so that it
+        // waits only for those loads, not for everything issued since)
+        if (!aborted && __builtin_amdgcn_ballot_w64(lane < nf && f <= m.c) != 0) {
             int spins = 0;
-            for (;;) {
-                const int f = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, lane * 4, 0, kLoadDevice);
-                if (__builtin_amdgcn_ballot_w64(lane < nf && f <= c) == 0)
-                    break;
+            do {
                 if (++spins > spin_limit) {
                     aborted = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(8);
-            }
+                f = ld_pub(m);
+            } while (__builtin_amdgcn_ballot_w64(lane < nf && f <= m.c) != 0);
         }
-        const long row0 = ((long)b * T + t0) * H + h;
-        const __amdgpu_buffer_rsrc_t ry = buffer(y + row0 * DV, rows_bytes(n, rs, DV * ES));
-        const __amdgpu_buffer_rsrc_t rg = buffer(gate + row0 * DV, rows_bytes(n, rs, DV * ES));
-        Oct8<E> xo[NPASS], xg[NPASS];
+        Oct8<E> xo[NPASS];
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int voff = (slot + UPW * p) * rs + 8 * sub * ES;
-            xo[p] = Oct8<E>::template load<kLoadDevice>(ry, voff);
-            xg[p] = Oct8<E>::template load<2>(rg, voff);     // read once: non-temporal
+        for (int p = 0; p < NPASS; ++p)
+            xo[p] = Oct8<E>::template load<kLoadDevice>(m.ry, lane_off + UPW * p * rs);
+        // the next item's progress words and gate rows
+        const long nx = it + nw;
+        const bool more = nx < items;
+        Item mn = m;
+        int fn = 0;
+        Oct8<E> xgn[NPASS];
+        if (more) {
+            mn = item(nx);
+            fn = ld_pub(mn);
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p)
+                xgn[p] = Oct8<E>::template load<2>(mn.rg, lane_off + UPW * p * rs);
         }
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -536,8 +572,16 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 yv[i] = aborted ? nanv : gate_elem(x[i], xg[p].get(i), rr, wv[i]);
-            Oct8<E>::store(ry, (slot + UPW * p) * rs + 8 * sub * ES, yv);
+            Oct8<E>::store(m.ry, lane_off + UPW * p * rs, yv);
         }
+        if (!more)
+            break;
+        it = nx;
+        m = mn;
+        f = fn;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+            xg[p] = xgn[p];
     }
 }
 
