@@ -20,6 +20,9 @@ torch.cuda.synchronize():
   gate     kda_output_gate on the prefill output shape (65536 tokens x 96 heads
            x 128, bf16), and kda_decode_step_gated on the decode batch (under
            "decode.gated");
+  from_proj  kda_chunk_fwd_from_proj (preprocessing and prefill in one call) on the
+           prep shape and on half of its heads (H48), next to kda_prefill_prep +
+           kda_chunk_fwd on the same inputs;
   gated    kda_chunk_fwd_gated, the prefill with the output gate fused, on the
            prefill workload, next to kda_chunk_fwd + kda_output_gate on the same
            inputs (each timed on its own);
@@ -255,7 +258,8 @@ def main():
     import torch
 
     from gated_delta_rule_18_amd import binding
-    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, STREAM_1M, WORKLOADS, backward_inputs,
+    from gated_delta_rule_18_amd.inputs import (DECODE, GATE_K3, PREP_K3, STREAM_1M, WORKLOADS, PrepSpec,
+                                                backward_inputs,
                                                 decode_gate_inputs,
                                                 decode_state, decode_step_inputs, gate_inputs,
                                                 prefill_inputs, prep_inputs)
@@ -518,10 +522,60 @@ def main():
             "tokens_per_s": ps.B * ps.T / (r_wall * 1e-3),
             "roofline": {"bound": "hbm", "achieved": r_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": r_gbps / HBM_PEAK_GBPS,
-                         "traffic": measured_traffic("prep_k3_hbm_counters.txt", ["kda_prep.hip", "kda_device.h"]),
+                         "traffic": measured_traffic("prep_k3_hbm_counters.txt",
+                                                     ["kda_prep.hip", "kda_prep_unit.h", "kda_device.h"]),
                          "bytes_per_launch": r_bytes},
         }
         del xp, outs, fin
+
+    # ---------------- preprocessing and prefill in one call ------------------------
+    from_proj = None
+    if not args.skip_prep:
+        from_proj = {}
+        for hh in (PREP_K3.H, PREP_K3.H // 2):
+            sp = PrepSpec(B=PREP_K3.B, T=PREP_K3.T, H=hh, dk=PREP_K3.dk, dv=PREP_K3.dv, seed=PREP_K3.seed)
+            xp = prep_inputs(sp, device=dev)
+            bf = dict(dtype=torch.bfloat16, device=dev)
+            outs = dict(q=torch.empty((sp.B, sp.T, hh, sp.dk), **bf), k=torch.empty((sp.B, sp.T, hh, sp.dk), **bf),
+                        v=torch.empty((sp.B, sp.T, hh, sp.dv), **bf), g=torch.empty((sp.B, sp.T, hh, sp.dk), **bf),
+                        beta=torch.empty((sp.B, sp.T, hh), **bf), conv_final=torch.empty_like(xp["conv_init"]))
+            of = torch.empty((sp.B, sp.T, hh, sp.dv), **bf)
+            sf = torch.empty((sp.B, hh, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+            pws = torch.empty(max(binding.from_proj_workspace_size(sp.B, sp.T, hh), 16), dtype=torch.uint8,
+                              device=dev)
+            torch.cuda.synchronize()
+
+            def fused_step(i=0):
+                binding.chunk_fwd_from_proj(xp["q_pre"], xp["k_pre"], xp["v_pre"], xp["conv_w"], xp["conv_init"],
+                                            xp["z"], xp["A"], xp["beta_logit"], None, out=outs, o=of, S_T=sf,
+                                            workspace=pws)
+
+            def prep_only(i=0):
+                binding.prefill_prep(xp["q_pre"], xp["k_pre"], xp["v_pre"], xp["conv_w"], xp["conv_init"], xp["z"],
+                                     xp["A"], xp["beta_logit"],
+                                     out=(outs["q"], outs["k"], outs["v"], outs["g"], outs["beta"]),
+                                     conv_final=outs["conv_final"])
+
+            def prefill_only(i=0):
+                binding.chunk_fwd(outs["q"], outs["k"], outs["v"], outs["g"], outs["beta"], None, chunk=16, o=of,
+                                  S_T=sf)
+
+            u_wall, u_kern = _timed(fused_step, args.steps, args.warmup, torch)
+            _, u_prep = _timed(prep_only, args.steps, args.warmup, torch)
+            _, u_pre = _timed(prefill_only, args.steps, args.warmup, torch)
+            grid = -(-sp.B * hh // 8) * 8 * (sp.dv // 64)
+            from_proj[f"H{hh}"] = {
+                "workload": f"kda_chunk_fwd_from_proj B{sp.B} H{hh} T{sp.T} dk=dv={sp.dk} bf16 "
+                            f"(pre-activations as prep, S0 = 0)",
+                "launch": "fused" if grid <= 160 else "prep pass, then prefill",
+                "ms_per_step": u_wall,
+                "kernel_ms": u_kern,
+                "tokens_per_s": sp.B * sp.T / (u_wall * 1e-3),
+                "two_pass_kernel_ms": u_prep + u_pre,
+                "two_pass_parts_ms": {"prep": u_prep, "prefill": u_pre},
+                "speedup_vs_two_pass": (u_prep + u_pre) / u_kern,
+            }
+            del xp, outs, of, sf, pws
 
     # ---------------- output exposure gate --------------------------------------
     gate = None
@@ -614,6 +668,7 @@ def main():
         "prep": prep,
         "gate": gate,
         "gated": gated,
+        "from_proj": from_proj,
         "bwd": bwd,
         "configs": configs,
     }

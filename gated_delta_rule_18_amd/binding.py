@@ -29,7 +29,8 @@ KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 NOALLOC_SCRATCH_BYTES = 64 << 20      # KDA_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
-           "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size", "kda_chunk_fwd_snapshots",
+           "kda_chunk_fwd_from_proj", "kda_chunk_fwd_from_proj_workspace_size", "kda_chunk_fwd_gated",
+           "kda_chunk_fwd_gated_workspace_size", "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
            "kda_validate_inputs", "kda_version")
 
@@ -67,6 +68,11 @@ def lib():
                                           + [ctypes.POINTER(FwdOptions), vp])
         L.kda_chunk_fwd_gated_workspace_size.restype = ctypes.c_size_t
         L.kda_chunk_fwd_gated_workspace_size.argtypes = [i] * 3
+        L.kda_chunk_fwd_from_proj.restype = i
+        L.kda_chunk_fwd_from_proj.argtypes = ([vp] * 17 + [vp, ctypes.c_size_t] + [i] * 7
+                                              + [ctypes.POINTER(FwdOptions), vp])
+        L.kda_chunk_fwd_from_proj_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_fwd_from_proj_workspace_size.argtypes = [i] * 3
         L.kda_decode_step.restype = i
         L.kda_decode_step.argtypes = [vp] * 5 + [i] + [vp] * 4 + [i] * 6 + [vp]
         L.kda_decode_step_gated.restype = i
@@ -223,6 +229,60 @@ def chunk_fwd_gated(q, k, v, g, beta, S0, gate, norm_w=None, eps=1e-6, y=None, S
                                    ctypes.byref(opts) if opts is not None else None, _stream(dev))
     _check(rc)
     return y, S_T
+
+
+def chunk_fwd_from_proj(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, S0=None, out=None, o=None,
+                        S_T=None, return_state=True, workspace=None, spin_limit=None):
+    """prefill_prep and chunk_fwd in one launch.  Arguments as prefill_prep (whose
+    outputs q, k, v, g, beta, conv_final are returned too, in `out` if given), then
+    S0, o, S_T as chunk_fwd.  Returns (o, S_T or None, dict(q, k, v, g, beta,
+    conv_final)): the same bits as prefill_prep followed by chunk_fwd.  workspace: a
+    uint8 device tensor of at least from_proj_workspace_size(B, T, H) bytes, or None
+    (allocated here).  spin_limit (testing): see kda_chunk_fwd_ex."""
+    B, T, H, dk = q_pre.shape
+    dv = v_pre.shape[-1]
+    dev, dt = q_pre.device, q_pre.dtype
+    code = _dtype_code(q_pre)
+    W = conv_w.shape[-1]
+    nch = 2 * dk + dv
+    for name, t, shp in (("q_pre", q_pre, (B, T, H, dk)), ("k_pre", k_pre, (B, T, H, dk)),
+                         ("v_pre", v_pre, (B, T, H, dv)), ("z", z, (B, T, H, dk)),
+                         ("beta_logit", beta_logit, (B, T, H))):
+        _want(t, name, shp, dt, dev)
+    _want(conv_w, "conv_w", (H, nch, W), torch.float32, dev)
+    _want(A, "A", (H,), torch.float32, dev)
+    if conv_init is not None:
+        _want(conv_init, "conv_init", (B, H, W - 1, nch), dt, dev)
+    if out is None:
+        out = dict(q=torch.empty((B, T, H, dk), dtype=dt, device=dev), k=torch.empty((B, T, H, dk), dtype=dt, device=dev),
+                   v=torch.empty((B, T, H, dv), dtype=dt, device=dev), g=torch.empty((B, T, H, dk), dtype=dt, device=dev),
+                   beta=torch.empty((B, T, H), dtype=dt, device=dev),
+                   conv_final=torch.empty((B, H, W - 1, nch), dtype=dt, device=dev))
+    if S0 is not None:
+        _want(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    else:
+        _want(o, "o", (B, T, H, dv), dt, dev)
+    if S_T is None and return_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _want(S_T, "S_T", (B, H, dk, dv), torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(from_proj_workspace_size(B, T, H), 16), dtype=torch.uint8, device=dev)
+    opts = FwdOptions(spin_limit=int(spin_limit)) if spin_limit is not None else None
+    rc = lib().kda_chunk_fwd_from_proj(
+        _ptr(q_pre), _ptr(k_pre), _ptr(v_pre), _ptr(conv_w), _ptr(conv_init), _ptr(z), _ptr(A), _ptr(beta_logit),
+        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["g"]), _ptr(out["beta"]), _ptr(out.get("conv_final")),
+        _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        B, T, H, dk, dv, W, code, ctypes.byref(opts) if opts is not None else None, _stream(dev))
+    _check(rc)
+    return o, S_T, out
+
+
+def from_proj_workspace_size(B, T, H):
+    """Bytes of workspace chunk_fwd_from_proj needs (kda_chunk_fwd_from_proj_workspace_size)."""
+    return int(lib().kda_chunk_fwd_from_proj_workspace_size(int(B), int(T), int(H)))
 
 
 def gated_workspace_size(B, H, dv):

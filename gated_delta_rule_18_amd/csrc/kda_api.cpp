@@ -421,10 +421,16 @@ int kda_chunk_bwd_noalloc(const void *q, const void *k, const void *v, const voi
                      H, dk_size, dv_size, dtype, stream, true);
 }
 
-int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
-                     const void *conv_init, const void *z, const float *A, const void *beta_logit,
-                     void *q, void *k, void *v, void *g, void *beta, void *conv_final, int B, int T,
-                     int H, int dk, int dv, int width, int dtype, void *stream)
+} // extern "C"
+
+namespace {
+
+// The checks of the preprocessing's arguments (shared by kda_prefill_prep and
+// kda_chunk_fwd_from_proj).  KDA_OK with B*H == 0 means there is nothing to do.
+int check_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+               const void *conv_init, const void *z, const float *A, const void *beta_logit, void *q, void *k,
+               void *v, void *g, void *beta, void *conv_final, int B, int T, int H, int dk, int dv, int width,
+               int dtype)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return KDA_ERR_INVALID;
@@ -463,9 +469,94 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, co
             if (overlap(out[i], out_n[i], out[j], out_n[j]))
                 return KDA_ERR_INVALID;
     }
+    return KDA_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                     const void *conv_init, const void *z, const float *A, const void *beta_logit,
+                     void *q, void *k, void *v, void *g, void *beta, void *conv_final, int B, int T,
+                     int H, int dk, int dv, int width, int dtype, void *stream)
+{
+    const int st = check_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, q, k, v, g, beta,
+                              conv_final, B, T, H, dk, dv, width, dtype);
+    if (st != KDA_OK || (long long)B * H == 0)
+        return st;
     hipError_t e = kda::launch_prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit,
                                             q, k, v, g, beta, conv_final, B, T, H, dk, dv,
                                             dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+size_t kda_chunk_fwd_from_proj_workspace_size(int B, int T, int H)
+{
+    if (B < 0 || T < 0 || H < 0)
+        return 0;
+    return (size_t)B * H * (((size_t)T + 127) / 128) * sizeof(int);
+}
+
+int kda_chunk_fwd_from_proj(const void *q_pre, const void *k_pre, const void *v_pre, const float *conv_w,
+                            const void *conv_init, const void *z, const float *A, const void *beta_logit,
+                            void *q, void *k, void *v, void *g, void *beta, void *conv_final, const float *S0,
+                            void *o, float *S_T, void *workspace, size_t workspace_bytes, int B, int T, int H,
+                            int dk, int dv, int width, int dtype, const kda_fwd_options *opts, void *stream)
+{
+    int st = check_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, q, k, v, g, beta, conv_final,
+                        B, T, H, dk, dv, width, dtype);
+    if (st != KDA_OK)
+        return st;
+    st = check_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, dtype);
+    if (st != KDA_OK)
+        return st;
+    kda::FwdOptions opt;
+    if (opts) {
+        if (opts->spin_limit < -1)
+            return KDA_ERR_INVALID;
+        opt.spin_limit = opts->spin_limit;
+    }
+    if ((long long)B * H == 0)
+        return KDA_OK;
+    const size_t need = kda_chunk_fwd_from_proj_workspace_size(B, T, H);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+        return KDA_ERR_INVALID;
+    // o, S_T and the workspace are written while everything else is read or written
+    const long long es = dtype == KDA_FP32 ? 4 : 2;
+    const long long rows = (long long)B * T * H;
+    const long long nk = rows * dk * es, nv = rows * dv * es, sb = (long long)B * H * dk * dv * 4;
+    const long long nc = (long long)B * H * (width - 1) * (2 * dk + dv) * es;
+    const void *all[] = {q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, q, k, v, g, beta, conv_final, S0};
+    const long long all_n[] = {nk, nk, nv, (long long)H * (2 * dk + dv) * width * 4, nc, nk, (long long)H * 4,
+                               rows * es, nk, nk, nv, nk, rows * es, nc, sb};
+    // the preprocessing's outputs (checked against its inputs above) against S0
+    for (int j = 8; j < 14; ++j)
+        if (overlap(all[j], all_n[j], S0, sb))
+            return KDA_ERR_INVALID;
+    const void *out[] = {o, S_T, workspace};
+    const long long out_n[] = {nv, sb, (long long)need};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 15; ++j)
+            if (!(i == 1 && j == 14 && out[i] == all[j]) && overlap(out[i], out_n[i], all[j], all_n[j]))
+                return KDA_ERR_INVALID;
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out_n[i], out[j], out_n[j]))
+                return KDA_ERR_INVALID;
+    }
+    kda::PrepInputs pi;
+    pi.q_pre = q_pre;
+    pi.k_pre = k_pre;
+    pi.v_pre = v_pre;
+    pi.z = z;
+    pi.beta_logit = beta_logit;
+    pi.conv_init = conv_init;
+    pi.conv_w = conv_w;
+    pi.A = A;
+    pi.conv_final = conv_final;
+    hipError_t e = kda::launch_chunk_fwd_from_proj(pi, q, k, v, g, beta, S0, o, S_T, static_cast<int *>(workspace),
+                                                   B, T, H, dk, dv, dtype == KDA_FP32, opt,
+                                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -69,6 +69,20 @@ hipError_t launch_chunk_fwd_gated(const void *q, const void *k, const void *v, c
                                   float *S_T, int *pub, int B, int T, int H, int dk, int dv, bool fp32,
                                   const FwdOptions &opt, hipStream_t stream);
 
+// The prefill with the preprocessing fused (kda_chunk_fwd_from_proj): the
+// pre-activations of kda_prefill_prep in, its outputs q, k, v, g, beta (written,
+// then read by the prefill in the same launch), o and S_T out.  done holds
+// B * H * ceil(T / 128) ints of scratch (tile flags, cleared by the launch).
+struct PrepInputs {
+    const void *q_pre = nullptr, *k_pre = nullptr, *v_pre = nullptr, *z = nullptr, *beta_logit = nullptr,
+               *conv_init = nullptr;
+    const float *conv_w = nullptr, *A = nullptr;
+    void *conv_final = nullptr;
+};
+hipError_t launch_chunk_fwd_from_proj(const PrepInputs &pi, void *q, void *k, void *v, void *g, void *beta,
+                                      const float *S0, void *o, float *S_T, int *done, int B, int T, int H,
+                                      int dk, int dv, bool fp32, const FwdOptions &opt, hipStream_t stream);
+
 // Backward pass: gradients (fp32) of <dO, o> + <dS_T, S_T> through kda_chunk_fwd.
 // workspace holds chunk_bwd_workspace_floats(...) floats.
 size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);

@@ -55,6 +55,7 @@
 // steps, and every LDS operand read uses one base register plus an immediate.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_prep_unit.h"
 
 namespace kda {
 namespace {
@@ -585,17 +586,80 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
     }
 }
 
-// GATED: the fused output gate -- o is y's buffer (the consumers' tiles, gated
-// in place by the workers), the consumers publish their progress in pub, and the
-// workgroups from grid_p on are gate workers (ngate of them, a multiple of 8).
-template <typename E, int DK, bool GATED>
+// ---- the fused preprocessing (kda_chunk_fwd_from_proj) --------------------------
+// Page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 3.2, input
+// branches, and section 3.3, lower-bounded decay: the preprocessing of
+// kda_prefill_prep (kda_prep_unit.h) runs in the prefill's own launch.  The first
+// nprep workgroups are prep workers: in rounds, each group of four wavefronts
+// maps one unit (two heads of this XCD over a 128-token tile), the round ends
+// with every store acknowledged and a barrier, and then one tile flag per head
+// goes out.  Units are dealt tile-major, so the workers sweep the sequence in
+// step with the prefill, whose producers wait for the flag of a chunk's tile
+// before loading the chunk (the flag is read one chunk ahead, so a set flag
+// costs no wait).  The prep workers wait for nothing and are dispatched before
+// every prefill workgroup, so the producers' waits end; they are bounded all
+// the same (a give-up marks the workgroup's results NaN like any hand-off).
+constexpr int kPrepKU = 16;            // tokens a prep lane loads ahead
+constexpr int kMinPrepCUs = 96;        // fewest idle CUs the fused launch is used with
+
+template <typename E> struct PrepArgs {
+    const E *q_pre, *k_pre, *v_pre, *z, *beta_logit, *conv_init;
+    const float *conv_w, *A;
+    E *conv_final;
+    int *done;          // [B*H][tiles]: 1 once the tile's outputs are in the L2
+    int nprep;          // prep workgroups, a multiple of 8, numbered before the prefill's
+};
+
+template <typename E, int DK, int DV>
+__device__ __forceinline__ void prep_worker(E *q, E *k, E *v, E *g, E *beta, const PrepArgs<E> &pa, int xcd,
+                                            int r, int nwx, int nbh, int T, int H)
+{
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int per = (int)blockDim.x / 256;                    // units per workgroup and round
+    const int slot = wave >> 2, role = wave & 3;
+    const int nhx = nbh > xcd ? (nbh - xcd + kXCDs - 1) / kXCDs : 0;   // heads on this XCD
+    const int npx = (nhx + 1) / 2;                            // their pairs
+    const int ntiles = (T + kTT - 1) / kTT;
+    const long units = (long)npx * ntiles;
+    const long nw = (long)nwx * per;
+    for (long base = (long)r * per; base < units; base += nw) {
+        const long u = base + slot;
+        int bhA = 0, bhB = -1, tile = 0;
+        if (u < units) {
+            tile = (int)(u / npx);
+            const int m = (int)(u % npx);
+            bhA = xcd + kXCDs * (2 * m);
+            bhB = 2 * m + 1 < nhx ? xcd + kXCDs * (2 * m + 1) : -1;
+            prep_unit<E, DK, DV, kPrepKU>(pa.q_pre, pa.k_pre, pa.v_pre, pa.conv_w, pa.conv_init, pa.z, pa.A,
+                                          pa.beta_logit, q, k, v, g, beta, pa.conv_final, T, H, bhA, bhB, tile,
+                                          role, lane);
+        }
+        // every store of the round acknowledged (in the L2), then the flags
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (role == 0 && u < units) {
+            __builtin_amdgcn_raw_buffer_store_b32(1, buffer(pa.done + (long)bhA * ntiles + tile, 4), 4 * lane, 0, 0);
+            if (bhB >= 0)
+                __builtin_amdgcn_raw_buffer_store_b32(1, buffer(pa.done + (long)bhB * ntiles + tile, 4), 4 * lane, 0,
+                                                      0);
+        }
+    }
+}
+
+// MODE 0: the plain prefill.  MODE 1 (GATED): the fused output gate -- o is y's
+// buffer (the consumers' tiles, gated in place by the workers), the consumers
+// publish their progress in pub, and the workgroups from grid_p on are gate
+// workers (ngate of them, a multiple of 8).  MODE 2 (PROJ): the fused
+// preprocessing -- the first pa.nprep workgroups are prep workers writing q, k,
+// v, g, beta, which the prefill workgroups after them read.
+template <typename E, int DK, int MODE>
 __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
-    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
-    const E *__restrict__ g, const E *__restrict__ beta, const float *S0, E *o,
+    const E *q, const E *k, const E *v, const E *g, const E *beta, const float *S0, E *o,
     float *S_T, float *snaps, int snap_chunks, int n_snaps, int snap_packed, int T, int H, int DV, int nbh,
     int nsl, int spin_limit, int *pub, const E *gate, const float *gate_w, float gate_eps, int grid_p,
-    int ngate)
+    int ngate, PrepArgs<E> pa)
 {
+    constexpr bool GATED = MODE == 1, PROJ = MODE == 2;
     typedef WsL<E, DK> L;
     typedef typename Vec<E>::v4 V4;
     typedef typename Vec<E>::v8 V8;
@@ -610,7 +674,23 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     int *abort_flag = flags + NS + 4 * NS;
 
     // workgroup -> (head, value slice); slices of a head share an XCD's L2
-    const int id = blockIdx.x, xcd = id % kXCDs, rr = id / kXCDs;
+    int id = blockIdx.x;
+    if constexpr (PROJ) {
+        if (id < pa.nprep) {
+            // nprep is a multiple of 8: prep worker id runs on XCD id % 8
+            if (DV == 128)
+                prep_worker<E, DK, 128>(const_cast<E *>(q), const_cast<E *>(k), const_cast<E *>(v),
+                                        const_cast<E *>(g), const_cast<E *>(beta), pa, id % kXCDs, id / kXCDs,
+                                        pa.nprep / kXCDs, nbh, T, H);
+            else
+                prep_worker<E, DK, 64>(const_cast<E *>(q), const_cast<E *>(k), const_cast<E *>(v),
+                                       const_cast<E *>(g), const_cast<E *>(beta), pa, id % kXCDs, id / kXCDs,
+                                       pa.nprep / kXCDs, nbh, T, H);
+            return;
+        }
+        id -= pa.nprep;
+    }
+    const int xcd = id % kXCDs, rr = id / kXCDs;
     if constexpr (GATED) {
         if (id >= grid_p) {
             // grid_p is a multiple of 8: worker j = id - grid_p runs on XCD j % 8
@@ -831,9 +911,35 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     E *pKc = reinterpret_cast<E *>(smem + L::oProd + pw * L::pBytes);
     const long hrow = (long)b * T * H + h;       // row of token 0 of this head
 
-    auto load = [&](RawC<E> &R, int c) {
+    auto load_raw = [&](RawC<E> &R, int c) {
         const int t0 = c * kC;
         load_chunk<E, DK>(R, q, k, g, v, beta, hrow + (long)t0 * H, T - t0 < kC ? T - t0 : kC, H, DV, slice, lane);
+    };
+    // PROJ: a chunk is loaded once its tile's flag is set.  ptile holds the flag of
+    // the chunk this producer loads next, read together with the previous chunk.
+    const int ntiles = (T + kTT - 1) / kTT;
+    int ptile = 1;
+    auto tile_flag = [&](int c) {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(buffer(pa.done + (long)bh * ntiles, ntiles * 4),
+                                                         ((c * kC) / kTT) * 4, 0, kLoadDevice);
+    };
+    auto load = [&](RawC<E> &R, int c) {
+        if constexpr (PROJ) {
+            if (c < nchunks && ptile == 0) {
+                int spins = 0;
+                while ((ptile = tile_flag(c)) == 0) {
+                    if (ld_flag(abort_flag))
+                        break;
+                    if (++spins > spin_limit) {
+                        st_flag(abort_flag, 1);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            ptile = c + L::NP < nchunks ? tile_flag(c + L::NP) : 1;
+        }
+        load_raw(R, c);
     };
 
     // One chunk from raw registers to a published slot.
@@ -1066,6 +1172,8 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     // one chunk in flight per producer: the loads for chunk c + NP are issued
     // as soon as chunk c's raw registers have been consumed
     RawC<E> raw;
+    if constexpr (PROJ)
+        ptile = pw < nchunks ? tile_flag(pw) : 1;
     load(raw, pw);
     for (int c = pw; c < nchunks; c += L::NP)
         produce(raw, c);
@@ -1079,41 +1187,88 @@ __global__ __launch_bounds__(256) void zero_pub(int *pub, long n)
         pub[i] = 0;
 }
 
-// The launch: og == nullptr for the plain prefill, else the gated one (o is then
-// y's buffer and pub the caller's nbh * nsl * 4 progress words).
-template <typename E, int DK, bool GATED>
+// What a launch fuses into the prefill: nothing (MODE 0), the output gate (og,
+// with o = y's buffer and pub the caller's nbh * nsl * 4 progress words; MODE 1)
+// or the preprocessing (prep, with q, k, v, g, beta its outputs and done the
+// caller's nbh * tiles flags; MODE 2).
+struct Fusion {
+    const OutputGate *og = nullptr;
+    int *pub = nullptr;
+    const PrepInputs *prep = nullptr;
+    int *done = nullptr;
+};
+
+template <typename E, int DK, int MODE>
 hipError_t launch_ws(const void *q, const void *k, const void *v, const void *g, const void *beta,
                      const float *S0, void *o, float *S_T, int B, int T, int H, int dv,
-                     const Snapshots &snap, int spin_limit, const OutputGate *og, int *pub, hipStream_t stream)
+                     const Snapshots &snap, int spin_limit, const Fusion &fu, hipStream_t stream)
 {
     typedef WsL<E, DK> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    // above half the LDS: one workgroup per CU, so a gate worker never shares a
-    // CU with a prefill workgroup
+    // above half the LDS: one workgroup per CU, so a gate or prep worker never
+    // shares a CU with a prefill workgroup
     constexpr int lds = L::bytes > 81 * 1024 ? L::bytes : 81 * 1024;
     // a per-device function attribute: set on every call (cheap, and correct
     // whichever device and thread the call comes from)
-    hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK, GATED>,
+    hipError_t e = hipFuncSetAttribute((const void *)prefill_ws_kernel<E, DK, MODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess)
         return e;
     const int nbh = B * H, nsl = dv / kVS;
     const int grid_p = ((nbh + kXCDs - 1) / kXCDs) * kXCDs * nsl;
     int ngate = 0;
-    if constexpr (GATED) {
+    PrepArgs<E> pa = {};
+    if constexpr (MODE == 1) {
         // the CUs the prefill grid leaves idle, at least 8 per XCD (which start as
         // prefill workgroups finish when the grid fills the chip)
         ngate = kCUs - grid_p > 64 ? ((kCUs - grid_p) / kXCDs) * kXCDs : 64;
         const long npub = (long)nbh * nsl * 4;
-        hipLaunchKernelGGL(zero_pub, dim3((unsigned)((npub + 255) / 256)), dim3(256), 0, stream, pub, npub);
+        hipLaunchKernelGGL(zero_pub, dim3((unsigned)((npub + 255) / 256)), dim3(256), 0, stream, fu.pub, npub);
     }
-    hipLaunchKernelGGL((prefill_ws_kernel<E, DK, GATED>), dim3(grid_p + ngate), dim3(64 * (4 + L::NP)), lds,
-                       stream, (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
+    if constexpr (MODE == 2) {
+        // the CUs the prefill grid leaves idle (at least kMinPrepCUs)
+        const PrepInputs &pi = *fu.prep;
+        pa.q_pre = (const E *)pi.q_pre;
+        pa.k_pre = (const E *)pi.k_pre;
+        pa.v_pre = (const E *)pi.v_pre;
+        pa.z = (const E *)pi.z;
+        pa.beta_logit = (const E *)pi.beta_logit;
+        pa.conv_init = (const E *)pi.conv_init;
+        pa.conv_w = pi.conv_w;
+        pa.A = pi.A;
+        pa.conv_final = (E *)pi.conv_final;
+        pa.done = fu.done;
+        pa.nprep = ((kCUs - grid_p) / kXCDs) * kXCDs;
+        const long ndone = (long)nbh * ((T + kTT - 1) / kTT);
+        hipLaunchKernelGGL(zero_pub, dim3((unsigned)((ndone + 255) / 256)), dim3(256), 0, stream, fu.done, ndone);
+    }
+    const OutputGate *og = fu.og;
+    hipLaunchKernelGGL((prefill_ws_kernel<E, DK, MODE>), dim3(pa.nprep + grid_p + ngate), dim3(64 * (4 + L::NP)),
+                       lds, stream, (const E *)q, (const E *)k, (const E *)v, (const E *)g, (const E *)beta, S0,
                        (E *)o, S_T, snap.count > 0 || snap.packed ? snap.out : nullptr, snap.every_chunks,
                        snap.count, snap.packed ? 1 : 0, T, H, dv, nbh, nsl,
-                       spin_limit < 0 ? kSpinLimit : spin_limit, pub, og ? (const E *)og->gate : nullptr,
-                       og ? og->w : nullptr, og ? og->eps : 0.f, grid_p, ngate);
+                       spin_limit < 0 ? kSpinLimit : spin_limit, fu.pub, og ? (const E *)og->gate : nullptr,
+                       og ? og->w : nullptr, og ? og->eps : 0.f, grid_p, ngate, pa);
     return hipGetLastError();
+}
+
+// Workgroups of the plain prefill grid for these sizes.
+int prefill_grid(int B, int H, int dv) { return ((B * H + kXCDs - 1) / kXCDs) * kXCDs * (dv / kVS); }
+
+template <int MODE>
+hipError_t launch_mode(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                       const float *S0, void *o, float *S_T, int B, int T, int H, int dk, int dv, bool fp32,
+                       const Snapshots &snap, int spin_limit, const Fusion &fu, hipStream_t stream)
+{
+    if (fp32)
+        return dk == 128 ? launch_ws<float, 128, MODE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                       fu, stream)
+                         : launch_ws<float, 64, MODE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                      fu, stream);
+    return dk == 128 ? launch_ws<__bf16, 128, MODE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                    fu, stream)
+                     : launch_ws<__bf16, 64, MODE>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
+                                                   fu, stream);
 }
 
 // T == 0: S_T = S0 (or 0).  One thread per state element.
@@ -1131,15 +1286,7 @@ hipError_t launch_chunk16(const void *q, const void *k, const void *v, const voi
                           int H, int dk, int dv, bool fp32, const Snapshots &snap, hipStream_t stream,
                           int spin_limit)
 {
-    if (fp32)
-        return dk == 128 ? launch_ws<float, 128, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
-                                                        nullptr, nullptr, stream)
-                         : launch_ws<float, 64, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
-                                                       nullptr, nullptr, stream);
-    return dk == 128 ? launch_ws<__bf16, 128, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
-                                                     nullptr, nullptr, stream)
-                     : launch_ws<__bf16, 64, false>(q, k, v, g, beta, S0, o, S_T, B, T, H, dv, snap, spin_limit,
-                                                    nullptr, nullptr, stream);
+    return launch_mode<0>(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, snap, spin_limit, Fusion{}, stream);
 }
 
 hipError_t launch_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -1167,17 +1314,41 @@ hipError_t launch_chunk_fwd_gated(const void *q, const void *k, const void *v, c
 {
     if ((long)B * H == 0)
         return hipSuccess;
-    if (T == 0) {
-        const Snapshots none;
-        return launch_chunk_fwd(q, k, v, g, beta, S0, y, S_T, B, T, H, dk, dv, fp32, none, opt, stream);
-    }
     const Snapshots none;
-    const int sl = opt.spin_limit;
-    if (fp32)
-        return dk == 128 ? launch_ws<float, 128, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream)
-                         : launch_ws<float, 64, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream);
-    return dk == 128 ? launch_ws<__bf16, 128, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream)
-                     : launch_ws<__bf16, 64, true>(q, k, v, g, beta, S0, y, S_T, B, T, H, dv, none, sl, &og, pub, stream);
+    if (T == 0)
+        return launch_chunk_fwd(q, k, v, g, beta, S0, y, S_T, B, T, H, dk, dv, fp32, none, opt, stream);
+    Fusion fu;
+    fu.og = &og;
+    fu.pub = pub;
+    return launch_mode<1>(q, k, v, g, beta, S0, y, S_T, B, T, H, dk, dv, fp32, none, opt.spin_limit, fu, stream);
+}
+
+hipError_t launch_chunk_fwd_from_proj(const PrepInputs &pi, void *q, void *k, void *v, void *g, void *beta,
+                                      const float *S0, void *o, float *S_T, int *done, int B, int T, int H,
+                                      int dk, int dv, bool fp32, const FwdOptions &opt, hipStream_t stream)
+{
+    if ((long)B * H == 0)
+        return hipSuccess;
+    const Snapshots none;
+    // fewer than kMinPrepCUs CUs left beside the prefill grid (or nothing to
+    // prefill): the preprocessing pass, then the prefill -- the same arithmetic, so
+    // the same bits.  The preprocessing streams its 2(3dk + dv) + 4 bytes per
+    // token-head at about 20 GB/s per CU whether it runs alone or beside the
+    // prefill, so it needs most of the chip to keep ahead: on B1 T65536 the fused
+    // launch beats the two passes by 15 % with 128 CUs to spare (H64) and by 6 %
+    // with 96 (H80), and takes 1.7 times as long with 64 (H96).
+    if (T == 0 || prefill_grid(B, H, dv) > kCUs - kMinPrepCUs) {
+        hipError_t e = launch_prefill_prep(pi.q_pre, pi.k_pre, pi.v_pre, pi.conv_w, pi.conv_init, pi.z, pi.A,
+                                           pi.beta_logit, q, k, v, g, beta, pi.conv_final, B, T, H, dk, dv, fp32,
+                                           stream);
+        if (e != hipSuccess)
+            return e;
+        return launch_chunk_fwd(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, none, opt, stream);
+    }
+    Fusion fu;
+    fu.prep = &pi;
+    fu.done = done;
+    return launch_mode<2>(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, fp32, none, opt.spin_limit, fu, stream);
 }
 
 } // namespace kda

@@ -15,115 +15,19 @@
 // the two L2 norms, so it is bound by HBM traffic: every pre-activation is read
 // once (plus a 3-token halo per tile, served by L2) and every output written
 // once.  A workgroup of four wavefronts owns two heads (h0, h0 + 1) of one
-// sequence over a kTT-token tile; every wavefront runs one kind of work on all
-// of its lanes (no divergent roles inside a wavefront), 4 channels per lane:
-//   wavefronts 0, 1: q (first dk/4 lanes) and k (next dk/4 lanes) of head
-//                    h0 + w: conv, Swish, then the L2 norm as a reduction over
-//                    the dk/4 lanes of the group;
-//   wavefront 2:     v of h0 (lanes 0..) and of h0 + 1 (lanes 32..): conv, Swish;
-//   wavefront 3:     the gate input z of h0 (lanes 0..) and h0 + 1 (lanes 32..);
-//   wavefronts 2, 3 also map beta of the tile's tokens (lane = token mod 64) for h0
-//                    and h0 + 1 respectively.
-// A conv lane walks the tile token by token keeping its last three inputs in
-// registers; loads run 8 tokens ahead.  Workgroups are numbered head pair
-// first, so the workgroups in flight at any time cover whole token rows of
-// every tensor (all heads of the same tokens) and the device reads and writes
-// long contiguous runs instead of 512-byte pieces scattered over the sequence.
+// sequence over a kTT-token tile (the unit of kda_prep_unit.h, which holds the
+// arithmetic).  Workgroups are numbered head pair first, so the workgroups in
+// flight at any time cover whole token rows of every tensor (all heads of the
+// same tokens) and the device reads and writes long contiguous runs instead of
+// 512-byte pieces scattered over the sequence.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_prep_unit.h"
 
 namespace kda {
 namespace {
 
-constexpr int kTT = 128;                 // tokens per tile
-constexpr int kW = 4;                    // conv width
 constexpr int kU = 8;                    // tokens loaded ahead
-constexpr float kL2Eps = 1e-6f;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kGMin = -5.0f;
-
-__device__ __forceinline__ f32x4 ld4(const __bf16 *p)
-{
-    const uint2 x = *reinterpret_cast<const uint2 *>(p);
-    return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
-                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
-}
-__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-
-__device__ __forceinline__ void st4(__bf16 *p, f32x4 x)
-{
-    *reinterpret_cast<typename Vec<__bf16>::v4 *>(p) = cvt4<__bf16>(x);
-}
-__device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
-
-// 1 / (1 + e^{-u}) with the hardware exponential and reciprocal; saturates to
-// 0 and 1 (e^{-u} = inf gives 0).
-__device__ __forceinline__ float sigmoid_f(float u)
-{
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
-}
-
-// Sum over the `n` lanes of an aligned lane group (n a power of two <= 32).
-template <int N>
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int off = N / 2; off > 0; off >>= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-// What a wavefront's lanes compute.
-enum Role { kQK = 0, kV = 1, kGate = 2 };
-
-// The token walk of one lane over its tile: 4 channels starting at element c4
-// of a row of D elements of `src`, rows t0 .. t0 + n - 1 of unit (b, h) at
-// `base` (element offset of row t0), `step` elements between token rows.
-// kQK / kV lanes: conv over (hist, x_t) with taps w, Swish, and for kQK the L2
-// norm over the lane group of NG lanes; kGate lanes: g = -5 Sigmoid(eA z).
-template <int R, int NG, typename E>
-__device__ __forceinline__ void walk(const E *src, E *dst, long base, long step, int n, const f32x4 *w,
-                                     f32x4 *hist, float eA, bool active)
-{
-    for (int tb = 0; tb < n; tb += kU) {
-        // loads first (rows past the tile are clamped to its last token and not used)
-        f32x4 xin[kU];
-#pragma unroll
-        for (int i = 0; i < kU; ++i)
-            xin[i] = ld4(src + base + (tb + i < n ? tb + i : n - 1) * step);
-#pragma unroll
-        for (int i = 0; i < kU; ++i) {
-            if (tb + i >= n)
-                break;
-            f32x4 y;
-            if constexpr (R == kGate) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = kGMin * sigmoid_f(eA * xin[i][e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // explicit fused multiply-adds in a fixed order: a token's result
-                    // must not depend on where it falls in the unrolled walk
-                    const float u = __builtin_fmaf(w[3][e], xin[i][e],
-                                    __builtin_fmaf(w[2][e], hist[2][e],
-                                    __builtin_fmaf(w[1][e], hist[1][e], w[0][e] * hist[0][e])));
-                    y[e] = u * sigmoid_f(u);
-                }
-                hist[0] = hist[1];
-                hist[1] = hist[2];
-                hist[2] = xin[i];
-                if constexpr (R == kQK) {
-                    const float ss = group_sum<NG>(__builtin_fmaf(y[3], y[3], __builtin_fmaf(y[2], y[2],
-                                                   __builtin_fmaf(y[1], y[1], y[0] * y[0]))));
-                    y *= __builtin_amdgcn_rsqf(ss + kL2Eps);
-                }
-            }
-            if (active)
-                st4(dst + base + (tb + i) * step, y);
-        }
-    }
-}
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void prep_kernel(
@@ -133,111 +37,13 @@ __global__ __launch_bounds__(256) void prep_kernel(
     E *__restrict__ k, E *__restrict__ v, E *__restrict__ g, E *__restrict__ beta, E *conv_final,
     int T, int H)
 {
-    constexpr int NCH = 2 * DK + DV;
-    constexpr int QK = DK / 4, VQ = DV / 4;     // 4-channel lanes per tensor
-    static_assert(2 * QK <= 64 && VQ <= 32 && QK <= 32, "lane budget");
     // head pair fastest (one-dimensional numbering: no 65535 limit on tiles)
     const int npairs = (H + 1) / 2;
     const int hp = (int)(blockIdx.x % npairs), tile = (int)(blockIdx.x / npairs), b = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int t0 = tile * kTT;
-    const int n = T - t0 < kTT ? T - t0 : kTT;           // tokens in this tile (0 only when T == 0)
-    const long tokb = (long)b * T;
-
-    // this lane's head, tensor and first channel
-    int h, c4, cc;                                      // cc = conv channel (order q | k | v)
-    const E *src;
-    E *dst;
-    bool active;
-    if (wave < 2) {
-        h = 2 * hp + wave;
-        const bool isk = lane >= QK;
-        c4 = 4 * (isk ? lane - QK : lane);
-        cc = isk ? DK + c4 : c4;
-        src = isk ? k_pre : q_pre;
-        dst = isk ? k : q;
-        active = lane < 2 * QK;
-    } else {
-        h = 2 * hp + (lane >> 5);
-        c4 = 4 * (lane & 31);
-        cc = 2 * DK + c4;
-        src = wave == 2 ? v_pre : z;
-        dst = wave == 2 ? v : g;
-        active = c4 < (wave == 2 ? DV : DK);
-    }
-    active = active && h < H;
-    if (!active)
-        h = 0, c4 = 0, cc = 0;                          // idle lanes read valid memory, store nothing
-    const int D = wave == 2 ? DV : DK;
-    const long bh = (long)b * H + h;
-    const long step = (long)H * D;
-    const long base = ((tokb + t0) * H + h) * (long)D + c4;
-
-    // ---- beta = Sigmoid(logit): wavefront 2 for h0, 3 for h0 + 1, lane = token --
-    if (wave >= 2) {
-        const int hb = 2 * hp + wave - 2;
-        if (hb < H) {
-            for (int tt = lane; tt < n; tt += 64) {
-                const long r = (tokb + t0 + tt) * H + hb;
-                beta[r] = (E)sigmoid_f(to_f(beta_logit[r]));
-            }
-        }
-    }
-
-    if (wave == 3) {
-        walk<kGate, 32>(src, dst, base, step, n, nullptr, nullptr, expf(A[h]), active);
-        return;
-    }
-
-    // ---- conv lanes (q, k, v): taps, history, then the token walk --------------
-    f32x4 w[kW];                                // w[j][e] = tap j of channel cc + e
-    f32x4 hist[kW - 1];                         // inputs of tokens t-3, t-2, t-1
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const f32x4 we = *reinterpret_cast<const f32x4 *>(conv_w + ((long)h * NCH + cc + e) * kW);
-#pragma unroll
-        for (int j = 0; j < kW; ++j)
-            w[j][e] = we[j];
-    }
-    const E *ci = conv_init ? conv_init + bh * (kW - 1) * NCH + cc : nullptr;
-#pragma unroll
-    for (int j = 0; j < kW - 1; ++j) {
-        const int t = t0 - (kW - 1) + j;
-        if (t >= 0)
-            hist[j] = ld4(src + base + (long)(t - t0) * step);
-        else if (ci)
-            hist[j] = ld4(ci + ((kW - 1) + t) * NCH);
-        else
-            hist[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // the history the next call continues from (tile 0 only): the last 3
-    // pre-activations, read before any of them is written (conv_final may be
-    // conv_init itself)
-    f32x4 fin[kW - 1];
-    const bool write_final = tile == 0 && conv_final;
-    if (write_final) {
-#pragma unroll
-        for (int j = 0; j < kW - 1; ++j) {
-            const int t = T - (kW - 1) + j;
-            if (t >= 0)
-                fin[j] = ld4(src + base + (long)(t - t0) * step);
-            else if (ci)
-                fin[j] = ld4(ci + ((kW - 1) + t) * NCH);
-            else
-                fin[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-
-    if (wave < 2)
-        walk<kQK, QK>(src, dst, base, step, n, w, hist, 0.f, active);
-    else
-        walk<kV, 32>(src, dst, base, step, n, w, hist, 0.f, active);
-
-    if (write_final && active) {
-#pragma unroll
-        for (int j = 0; j < kW - 1; ++j)
-            st4(conv_final + (bh * (kW - 1) + j) * NCH + cc, fin[j]);
-    }
+    const int bhA = b * H + 2 * hp, bhB = 2 * hp + 1 < H ? bhA + 1 : -1;
+    prep_unit<E, DK, DV, kU>(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, q, k, v, g, beta,
+                             conv_final, T, H, bhA, bhB, tile, wave, lane);
 }
 
 template <typename E, int DK, int DV>

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 130 /* 1.3.0 */
+#define KDA_VERSION 140 /* 1.4.0 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -217,6 +217,47 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
                      void *q, void *k, void *v, void *g, void *beta, void *conv_final,
                      int B, int T, int H, int dk, int dv, int width, int dtype,
                      void *stream);
+
+/*
+ * kda_chunk_fwd_from_proj -- kda_prefill_prep and kda_chunk_fwd in one launch:
+ * from the projected pre-activations to o and S_T.
+ *
+ * Defines (page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section
+ * 3.2, input-branch equations, and section 3.3, lower-bounded decay equation,
+ * as kda_prefill_prep; then section 3.3, chunk interface, as kda_chunk_fwd):
+ * every output is bit for bit what kda_prefill_prep followed by kda_chunk_fwd
+ * writes.  Workgroups of the launch on the CUs the prefill leaves idle run the
+ * preprocessing tile by tile (128 tokens), ahead of the prefill workgroups,
+ * which read each tile once its flag is set.  When the prefill leaves fewer
+ * than 96 of the 256 CUs idle (B*H*(dv/64), rounded up to a multiple of 8, above
+ * 160 workgroups) the preprocessing would fall behind, and the call runs the
+ * two passes one after the other instead.
+ *
+ * Arguments: those of kda_prefill_prep (q, k, v, g, beta and conv_final are
+ * written, and q, k, v, g, beta are then the prefill's inputs), then
+ *   S0, o, S_T : as kda_chunk_fwd (S_T may equal S0)
+ *   workspace  : device memory of at least
+ *                kda_chunk_fwd_from_proj_workspace_size(B, T, H) bytes (one flag
+ *                per (sequence, head, 128-token tile)), 16-byte aligned, owned by
+ *                the caller; contents before and after the call do not matter.
+ *                Calls that may run at the same time need separate workspaces.
+ *   opts       : NULL = defaults, else as kda_chunk_fwd_ex (spin_limit also bounds
+ *                the prefill's waits for the preprocessing)
+ * Errors: as kda_prefill_prep and kda_chunk_fwd; KDA_ERR_INVALID also for a null,
+ * misaligned or short workspace, spin_limit < -1, or o, S_T or the workspace
+ * overlapping any other buffer (S_T = S0 allowed).
+ */
+int kda_chunk_fwd_from_proj(const void *q_pre, const void *k_pre, const void *v_pre,
+                            const float *conv_w, const void *conv_init, const void *z,
+                            const float *A, const void *beta_logit,
+                            void *q, void *k, void *v, void *g, void *beta, void *conv_final,
+                            const float *S0, void *o, float *S_T,
+                            void *workspace, size_t workspace_bytes,
+                            int B, int T, int H, int dk, int dv, int width, int dtype,
+                            const kda_fwd_options *opts, void *stream);
+
+/* Bytes of workspace kda_chunk_fwd_from_proj needs (0 for invalid sizes). */
+size_t kda_chunk_fwd_from_proj_workspace_size(int B, int T, int H);
 
 /*
  * kda_output_gate -- the output exposure gate of a KDA layer, before W_o.

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 130
+    assert binding.version() == 140
     L = binding.lib()
     for code in (0, -1, -2, -3, -4, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
@@ -257,6 +257,45 @@ def test_fwd_gated_smallest_workspace_and_empty_calls():
     # or (S_T = S0, T = 0) an empty sequence
     assert _fwd_gated(B=0, wsb=0, ws=None, gate=None) == 0
     assert _fwd_gated(T=0, S_T=A + 5 * (1 << 24), ws=None, gate=None) == 0
+
+
+def _from_proj(**kw):
+    big = 1 << 24
+    names = ("qp", "kp", "vp", "w", "ci", "z", "A", "bl", "q", "k", "v", "g", "beta", "cf", "S0", "o", "S_T", "ws")
+    args = {n: A + i * big for i, n in enumerate(names)}
+    args["ci"] = None
+    args.update(dict(wsb=1 << 12, B=1, T=200, H=2, dk=64, dv=64, width=4, dtype=0, spin=None, stream=None))
+    args.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    opts = ctypes.byref(binding.FwdOptions(spin_limit=args["spin"])) if args["spin"] is not None else None
+    return binding.lib().kda_chunk_fwd_from_proj(*(vp(args[n]) for n in names), args["wsb"], args["B"], args["T"],
+                                                 args["H"], args["dk"], args["dv"], args["width"], args["dtype"],
+                                                 opts, args["stream"])
+
+
+def test_from_proj_workspace_size():
+    # one flag per (sequence, head, 128-token tile)
+    assert binding.from_proj_workspace_size(2, 300, 3) == 2 * 3 * 3 * 4
+    assert binding.from_proj_workspace_size(2, 0, 3) == 0
+    assert binding.lib().kda_chunk_fwd_from_proj_workspace_size(-1, 5, 3) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(width=3), -1), (dict(dtype=2), -1), (dict(dk=96), -2), (dict(B=65536), -1), (dict(spin=-2), -1),
+    (dict(ws=None), -1), (dict(ws=MIS), -1), (dict(wsb=2 * 2 * 4 - 1), -1), (dict(w=None), -1),
+    (dict(qp=None), -1), (dict(q=None), -1), (dict(o=None), -1), (dict(o=MIS), -1),
+    (dict(o=A + 64), -1),                          # o over q_pre
+    (dict(o=A + 9 * (1 << 24) + 64), -1),          # o over k (a preprocessing output)
+    (dict(S_T=A + 14 * (1 << 24) + 64), -1),       # S_T partly over S0
+    (dict(ws=A + 15 * (1 << 24) + 16), -1),        # the workspace over o
+    (dict(S0=A + 8 * (1 << 24) + 32), -1),         # S0 over q (written by the preprocessing)
+])
+def test_from_proj_rejects(kw, code):
+    assert _from_proj(**kw) == code
+
+
+def test_from_proj_empty_batch_is_a_no_op():
+    assert _from_proj(B=0, ws=None, wsb=0) == 0
 
 
 def _decode_gated(**kw):
