@@ -109,6 +109,20 @@ __device__ __forceinline__ float gate_elem(float o, float gt, float r, float w)
     return __builtin_amdgcn_rcpf(1.0f + exp_f(-gt)) * o * r * w;
 }
 
+// The XCD (accelerator complex die) the calling wavefront runs on: hardware
+// register 20 (XCC_ID), bits [3:0].  Workgroup i of a launch runs on XCD i mod 8
+// on this part (measured for every workgroup of a 1024-workgroup grid), which the
+// hand-offs between workgroups rely on to share an L2.  The prefill's hand-off
+// words carry their writer's XCD in bits [30:28] so that the reader checks the
+// assumption (and marks its results NaN) instead of reading another L2's stale
+// data.
+__device__ __forceinline__ int hw_xcd() { return (int)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); }
+constexpr int kXcdShift = 28;
+constexpr int kCountMask = (1 << kXcdShift) - 1;
+__device__ __forceinline__ int tag_xcd(int count, int xcd) { return count | (xcd << kXcdShift); }
+__device__ __forceinline__ int word_count(int w) { return w & kCountMask; }
+__device__ __forceinline__ int word_xcd(int w) { return (int)((unsigned)w >> kXcdShift); }
+
 // Sum over the 64 lanes of a wavefront (result valid in every lane).
 __device__ __forceinline__ float wave_sum(float x)
 {

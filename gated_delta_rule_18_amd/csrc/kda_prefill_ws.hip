@@ -496,6 +496,7 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
     const int rs = H * DV * ES;                                        // bytes between token rows
     const int lane_off = slot * rs + 8 * sub * ES;
     const float nanv = __builtin_nanf("");
+    const int xcd_hw = hw_xcd();
 
     // item it: chunk c of head bh, buffers over its n <= 16 rows
     struct Item {
@@ -529,7 +530,7 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
         // every consumer of the head has published chunk c (the first test, of the
         // words loaded one item ahead, sits outside the polling loop, so that it
         // waits only for those loads, not for everything issued since)
-        if (!aborted && __builtin_amdgcn_ballot_w64(lane < nf && f <= m.c) != 0) {
+        if (!aborted && __builtin_amdgcn_ballot_w64(lane < nf && word_count(f) <= m.c) != 0) {
             int spins = 0;
             do {
                 if (++spins > spin_limit) {
@@ -538,8 +539,11 @@ __device__ __forceinline__ void gate_worker(E *y, const E *gate, const float *w,
                 }
                 __builtin_amdgcn_s_sleep(8);
                 f = ld_pub(m);
-            } while (__builtin_amdgcn_ballot_w64(lane < nf && f <= m.c) != 0);
+            } while (__builtin_amdgcn_ballot_w64(lane < nf && word_count(f) <= m.c) != 0);
         }
+        // a consumer on another XCD: its tiles may sit in that XCD's L2
+        if (__builtin_amdgcn_ballot_w64(lane < nf && word_xcd(f) != xcd_hw) != 0)
+            aborted = true;
         Oct8<E> xo[NPASS];
 #pragma unroll
         for (int p = 0; p < NPASS; ++p)
@@ -638,10 +642,12 @@ __device__ __forceinline__ void prep_worker(E *q, E *k, E *v, E *g, E *beta, con
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
         if (role == 0 && u < units) {
-            __builtin_amdgcn_raw_buffer_store_b32(1, buffer(pa.done + (long)bhA * ntiles + tile, 4), 4 * lane, 0, 0);
+            const int word = tag_xcd(1, hw_xcd());
+            __builtin_amdgcn_raw_buffer_store_b32(word, buffer(pa.done + (long)bhA * ntiles + tile, 4), 4 * lane, 0,
+                                                  0);
             if (bhB >= 0)
-                __builtin_amdgcn_raw_buffer_store_b32(1, buffer(pa.done + (long)bhB * ntiles + tile, 4), 4 * lane, 0,
-                                                      0);
+                __builtin_amdgcn_raw_buffer_store_b32(word, buffer(pa.done + (long)bhB * ntiles + tile, 4), 4 * lane,
+                                                      0, 0);
         }
     }
 }
@@ -752,8 +758,11 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         // gated: this wavefront's progress word (lane 0 writes it; the other
         // lanes' offsets fall outside the 4-byte buffer)
         __amdgpu_buffer_rsrc_t rpub;
-        if constexpr (GATED)
+        int xcd_hw = 0;
+        if constexpr (GATED) {
             rpub = buffer(pub + ((long)bh * nsl + slice) * 4 + w, 4);
+            xcd_hw = hw_xcd();
+        }
 
         // this lane's byte offsets inside a slot: image16 pieces (Kt, Qt),
         // image4 pieces (Ke^T, V^T, T, M) and the Gam pair (see decay_rows)
@@ -889,12 +898,13 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
                 // writes no snapshots), so once at most 10 are outstanding the
                 // o tiles of chunk c - 2 and all before it are in the L2.
                 __builtin_amdgcn_s_waitcnt(kVmcntPub);
-                __builtin_amdgcn_raw_buffer_store_b32(c + 1 - kPubLag > 0 ? c + 1 - kPubLag : 0, rpub, 4 * lane, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(tag_xcd(c + 1 - kPubLag > 0 ? c + 1 - kPubLag : 0, xcd_hw), rpub,
+                                                      4 * lane, 0, 0);
             }
         }
         if constexpr (GATED) {
             __builtin_amdgcn_s_waitcnt(kVmcntZero);
-            __builtin_amdgcn_raw_buffer_store_b32(nchunks, rpub, 4 * lane, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(tag_xcd(nchunks, xcd_hw), rpub, 4 * lane, 0, 0);
         }
         if (S_T) {
             aborted |= ld_flag(abort_flag) != 0;
@@ -923,21 +933,27 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
         return (int)__builtin_amdgcn_raw_buffer_load_b32(buffer(pa.done + (long)bh * ntiles, ntiles * 4),
                                                          ((c * kC) / kTT) * 4, 0, kLoadDevice);
     };
+    const int xcd_hw = PROJ ? hw_xcd() : 0;
     auto load = [&](RawC<E> &R, int c) {
         if constexpr (PROJ) {
-            if (c < nchunks && ptile == 0) {
-                int spins = 0;
-                while ((ptile = tile_flag(c)) == 0) {
-                    if (ld_flag(abort_flag))
-                        break;
-                    if (++spins > spin_limit) {
-                        st_flag(abort_flag, 1);
-                        break;
+            if (c < nchunks) {
+                if (ptile == 0) {
+                    int spins = 0;
+                    while ((ptile = tile_flag(c)) == 0) {
+                        if (ld_flag(abort_flag))
+                            break;
+                        if (++spins > spin_limit) {
+                            st_flag(abort_flag, 1);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
                     }
-                    __builtin_amdgcn_s_sleep(2);
                 }
+                // written on another XCD: the tile may sit in that XCD's L2
+                if (ptile != 0 && word_xcd(ptile) != xcd_hw)
+                    st_flag(abort_flag, 1);
             }
-            ptile = c + L::NP < nchunks ? tile_flag(c + L::NP) : 1;
+            ptile = c + L::NP < nchunks ? tile_flag(c + L::NP) : tag_xcd(1, xcd_hw);
         }
         load_raw(R, c);
     };
@@ -1173,7 +1189,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     // as soon as chunk c's raw registers have been consumed
     RawC<E> raw;
     if constexpr (PROJ)
-        ptile = pw < nchunks ? tile_flag(pw) : 1;
+        ptile = pw < nchunks ? tile_flag(pw) : tag_xcd(1, xcd_hw);
     load(raw, pw);
     for (int c = pw; c < nchunks; c += L::NP)
         produce(raw, c);
