@@ -242,7 +242,10 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
  *                the caller; contents before and after the call do not matter.
  *                Calls that may run at the same time need separate workspaces.
  *   opts       : NULL = defaults, else as kda_chunk_fwd_ex (spin_limit also bounds
- *                the prefill's waits for the preprocessing)
+ *                the prefill's waits for the preprocessing; a prefill workgroup
+ *                whose tile flag shows a preprocessing workgroup on another XCD --
+ *                the launch assumes workgroup i runs on XCD i mod 8 -- marks its
+ *                outputs NaN like a wait that gave up)
  * Errors: as kda_prefill_prep and kda_chunk_fwd; KDA_ERR_INVALID also for a null,
  * misaligned or short workspace, spin_limit < -1, or o, S_T or the workspace
  * overlapping any other buffer (S_T = S0 allowed).
@@ -329,7 +332,9 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
  *               workspaces.
  *   opts      : NULL = defaults, else as kda_chunk_fwd_ex; spin_limit bounds the
  *               gate's waits for the prefill too, and a block whose wait gave up
- *               is written as NaN.
+ *               is written as NaN.  The hand-off assumes workgroup i runs on XCD
+ *               i mod 8 (so that its L2 holds what it reads); a block whose
+ *               progress words show another XCD is written as NaN too.
  * Errors: as kda_chunk_fwd; KDA_ERR_INVALID also for a null or misaligned gate or
  * workspace, a workspace below the size above, a misaligned norm_w, a bad eps,
  * spin_limit < -1 or overlapping buffers.
