@@ -32,7 +32,7 @@ EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_si
            "kda_chunk_fwd_from_proj", "kda_chunk_fwd_from_proj_workspace_size", "kda_chunk_fwd_gated",
            "kda_chunk_fwd_gated_workspace_size", "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
-           "kda_validate_inputs", "kda_version")
+           "kda_validate_inputs", "kda_version", "kda_workgroup_xcds")
 
 _lib = None
 
@@ -90,6 +90,8 @@ def lib():
         L.kda_prefill_prep.argtypes = [vp] * 14 + [i] * 7 + [vp]
         L.kda_validate_inputs.restype = i
         L.kda_validate_inputs.argtypes = [vp] * 3 + [i] * 5 + [vp]
+        L.kda_workgroup_xcds.restype = i
+        L.kda_workgroup_xcds.argtypes = [vp, i, i, vp]
         L.kda_strerror.restype = ctypes.c_char_p
         L.kda_strerror.argtypes = [i]
         L.kda_version.restype = i
@@ -442,6 +444,16 @@ def validate_inputs(g, beta):
     _check(rc)
     r = [int(x) for x in report.cpu()]
     return dict(bad_g=r[0], first_bad_g=r[1], bad_beta=r[2], first_bad_beta=r[3])
+
+
+def workgroup_xcds(n, lds_bytes=0, device=None):
+    """Debug check of the workgroup placement the fused launches assume: an int32
+    tensor [n] whose element i is the XCD workgroup i of one n-workgroup launch (each
+    workgroup requesting lds_bytes of LDS) ran on; the fused launches expect i % 8."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    xcd = torch.full((max(int(n), 0),), -1, dtype=torch.int32, device=dev)
+    _check(lib().kda_workgroup_xcds(_ptr(xcd) if n > 0 else None, int(n), int(lds_bytes), _stream(dev)))
+    return xcd
 
 
 def prefill_prep(q_pre, k_pre, v_pre, conv_w, conv_init, z, A, beta_logit, out=None,

@@ -393,6 +393,18 @@ int kda_validate_inputs(const void *g, const void *beta, long long *report, int 
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int kda_workgroup_xcds(int *xcd, int n, int lds_bytes, void *stream)
+{
+    if (n < 0 || n > (1 << 20) || lds_bytes < 0 || lds_bytes > 160 * 1024)
+        return KDA_ERR_INVALID;
+    if (n == 0)
+        return KDA_OK;
+    if (!xcd || (reinterpret_cast<std::uintptr_t>(xcd) & 3u) != 0)
+        return KDA_ERR_INVALID;
+    hipError_t e = kda::launch_workgroup_xcds(xcd, n, lds_bytes, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv)
 {
     if (B < 0 || T < 0 || H < 0 || !head_ok(dk) || !head_ok(dv))

@@ -98,6 +98,10 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
 constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(float **ptr);
 
+// Debug: workgroup i of an n-workgroup launch, each requesting lds_bytes of
+// dynamic LDS, writes the XCD it ran on to xcd[i].
+hipError_t launch_workgroup_xcds(int *xcd, int n, int lds_bytes, hipStream_t stream);
+
 // The output exposure gate alone over `units` (row, head) rows of dv elements.
 hipError_t launch_output_gate(const void *o, const void *gate, const float *w, void *y, long units,
                               int dv, float eps, bool fp32, hipStream_t stream);

@@ -1,5 +1,6 @@
-// kda_validate.hip -- debug check of the value domains the KDA kernels assume
-// (kda_validate_inputs).
+// kda_validate.hip -- debug checks: the value domains the KDA kernels assume
+// (kda_validate_inputs) and the workgroup placement the fused launches assume
+// (kda_workgroup_xcds).
 //
 // Domains: page "Kimi K3：架构、训练与百万 Token Agentic RL 技术解读", section 3.3,
 // lower-bounded decay: the log-decay g lies in [g_min, 0] with g_min = -5, which is
@@ -108,6 +109,30 @@ hipError_t launch_validate(const void *g, const void *beta, long long *report, l
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(report_finish, dim3(1), dim3(1), 0, stream, report);
+    return hipGetLastError();
+}
+
+namespace {
+
+// Workgroup i of the launch records the XCD it runs on (hardware register
+// XCC_ID).  The dynamic LDS the launch requests is never touched: it only makes
+// each workgroup take as much of a CU as the kernels whose placement is checked.
+__global__ __launch_bounds__(64) void placement_kernel(int *xcd, int n)
+{
+    const int i = blockIdx.x;
+    if (threadIdx.x == 0 && i < n)
+        xcd[i] = hw_xcd();
+}
+
+} // namespace
+
+hipError_t launch_workgroup_xcds(int *xcd, int n, int lds_bytes, hipStream_t stream)
+{
+    hipError_t e = hipFuncSetAttribute((const void *)placement_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds_bytes);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(placement_kernel, dim3((unsigned)n), dim3(64), (unsigned)lds_bytes, stream, xcd, n);
     return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 140 /* 1.4.0 */
+#define KDA_VERSION 141 /* 1.4.1 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -441,6 +441,24 @@ int kda_validate_inputs(const void *g, const void *beta, long long *report,
 
 /* Human-readable text for a kda_status code (static storage, never NULL). */
 const char *kda_strerror(int status);
+
+/*
+ * kda_workgroup_xcds -- debug check of the workgroup placement the fused
+ * launches rely on.
+ *
+ * The launches whose workgroups hand data to each other through the L2
+ * (kda_chunk_fwd_gated, kda_chunk_fwd_from_proj, and kda_chunk_bwd with dv = 128)
+ * assume that workgroup i of a launch runs on XCD (accelerator die) i mod 8, so
+ * that a writer and its readers share that die's L2.  This enqueues one launch
+ * of n workgroups, each requesting lds_bytes of dynamic LDS (as those kernels
+ * do), in which workgroup i writes the XCD it ran on to xcd[i].
+ *   xcd       : device int32 [n], written
+ *   n         : 0 .. 2^20 workgroups (0: nothing is enqueued)
+ *   lds_bytes : 0 .. 163840
+ * Errors: KDA_ERR_INVALID for sizes outside those ranges or a null or misaligned
+ * xcd; KDA_ERR_LAUNCH if the runtime rejects the launch.
+ */
+int kda_workgroup_xcds(int *xcd, int n, int lds_bytes, void *stream);
 
 /* KDA_VERSION of the loaded library. */
 int kda_version(void);

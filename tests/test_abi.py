@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 140
+    assert binding.version() == 141
     L = binding.lib()
     for code in (0, -1, -2, -3, -4, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)
@@ -420,3 +420,12 @@ def _validate(**kw):
 ])
 def test_validate_rejects(kw, code):
     assert _validate(**kw) == code
+
+
+@pytest.mark.parametrize("n,lds,ptr,code", [
+    (-1, 0, A, -1), ((1 << 20) + 1, 0, A, -1), (8, -1, A, -1), (8, 160 * 1024 + 1, A, -1),
+    (8, 0, None, -1), (8, 0, A + 2, -1), (0, 0, None, 0), (0, 160 * 1024, None, 0),
+])
+def test_workgroup_xcds_rejects(n, lds, ptr, code):
+    vp = ctypes.c_void_p(ptr) if ptr is not None else None
+    assert binding.lib().kda_workgroup_xcds(vp, n, lds, None) == code
