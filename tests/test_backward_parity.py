@@ -107,3 +107,14 @@ def test_backward_deterministic(gpu):
     torch.cuda.synchronize()
     for u, w in zip(a, b):
         assert torch.equal(u, w)
+
+
+@pytest.mark.parametrize("B,H,T", [(8, 40, 100), (3, 97, 33)])
+def test_backward_grid_larger_than_the_chip(gpu, B, H, T):
+    """640 workgroups (320 heads) and 592 (291 heads, not a multiple of 8: 582 busy) for 256 CUs: the
+    two value-slice workgroups of a head hand partial gradients to each other through the
+    L2 of their XCD, and heads run in several waves.  Heads from the first, middle and last
+    waves against the oracle."""
+    spec = PrefillSpec(B=B, H=H, T=T, dk=128, dv=128, seed=700 + H)
+    heads = [(0, 0), (0, 7), (B // 2, H // 2), (B - 1, H - 9), (B - 1, H - 1)]
+    _check(spec, gpu, heads=heads, what=f"B{B} H{H} T{T} ({B * H * 2} workgroups)")
