@@ -161,6 +161,24 @@ def test_prefill_b4h32_sampled_heads(gpu, name, chunk):
     print(f"{name} chunk {chunk}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("B,H,T,dv", [(8, 40, 100, 128), (3, 97, 33, 128), (5, 77, 50, 64)])
+def test_grid_larger_than_the_chip(gpu, B, H, T, dv):
+    """640, 592 and 392 workgroups for 256 CUs (two value slices per head, or one with
+    dv = 64; head counts 291 and 385 are not multiples of 8): heads run in waves.  Heads
+    from the first, middle and last waves against the oracle."""
+    spec = PrefillSpec(B=B, H=H, T=T, dk=128, dv=dv, seed=800 + H)
+    inp = prefill_inputs(spec, device=gpu)
+    o, st = _run(inp, 16)
+    heads = [(0, 0), (0, 7), (B // 2, H // 2), (B - 1, H - 9), (B - 1, H - 1)]
+    oo, so = oracle_prefill_heads(inp, heads)
+    og = np.stack([to_f64(o[b, :, h]) for b, h in heads])
+    sg = np.stack([to_f64(st[b, h]) for b, h in heads])
+    to, ts = TOL["bf16"]
+    eo = assert_parity(og, oo, to, f"B{B} H{H} T{T} dv{dv} o")
+    es = assert_parity(sg, so, ts, f"B{B} H{H} T{T} dv{dv} S_T")
+    print(f"B{B} H{H} T{T} dv{dv}: err_o {eo:.2e} err_S {es:.2e}", flush=True)
+
+
 # ---------------------------------------------------------------- snapshots --
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
