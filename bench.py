@@ -105,9 +105,9 @@ def gate_bytes(rows, H, dv):
     return rows * H * dv * 2 * 3 + 4 * dv
 
 
-def measured_traffic(profile, sources):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
-    kernel sources have changed since the counters were taken."""
+def measured_traffic(profile, sources, key="traffic_bytes"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (its `key:` line),
+    or None when the kernel sources have changed since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
     for f in sources:
@@ -121,7 +121,7 @@ def measured_traffic(profile, sources):
     if h.hexdigest()[:16] not in text:
         return None
     for line in text.splitlines():
-        if line.startswith("traffic_bytes:"):
+        if line.startswith(key + ":"):
             return int(line.split(":")[1])
     return None
 
@@ -314,7 +314,11 @@ def main():
             "tokens_per_s": B * T / (s_wall * 1e-3),
             "extra_ms_vs_prefill": s_kern - p_kern,
             "roofline": {"bound": "hbm", "achieved": s_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": s_gbps / HBM_PEAK_GBPS, "traffic": None, "bytes_per_launch": s_bytes},
+                         "frac": s_gbps / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("prefill_k3_hbm_counters.txt",
+                                                     ["kda_prefill_ws.hip", "kda_device.h"],
+                                                     key="snapshots_traffic_bytes"),
+                         "bytes_per_launch": s_bytes},
         }
         del snaps
     gated = None
@@ -492,7 +496,10 @@ def main():
                 "ms_per_step": g_wall, "kernel_ms": g_kern, "extra_ms_vs_decode": g_kern - d_kern,
                 "roofline": {"bound": "hbm", "achieved": g_bytes / (g_kern * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                              "unit": "GB/s", "frac": g_bytes / (g_kern * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                             "traffic": None, "bytes_per_launch": g_bytes},
+                             "traffic": measured_traffic("decode_n256_hbm_counters.txt",
+                                                         ["kda_decode.hip", "kda_device.h"],
+                                                         key="gated_traffic_bytes"),
+                             "bytes_per_launch": g_bytes},
             }
             del gates
         del st, steps_in
