@@ -45,6 +45,10 @@
 // partials of that chunk are in the shared L2, loads them (bypassing its own
 // L1), adds them in slice order and writes the gradients (no atomics: the
 // result is deterministic and the same as summing the slices afterwards).
+// Slice 1 also posts how many chunks it has finished, and slice 0 waits for it
+// to stay at most kBwdLead chunks ahead: slice 1's reads of the inputs both
+// slices load then find them in the L2 (without it slice 0, the faster of the
+// two, drifts tens of chunks ahead and slice 1 reads q, k, g again from HBM).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -86,6 +90,12 @@ constexpr int kVmcntZero = 0x0F70;
 constexpr int kLoadDevice = 16;
 // polls of a slice-0 flag before slice 1 gives up and marks its sums NaN
 constexpr int kBwdSpinLimit = 1 << 18;
+// slice 0 keeps at most this many chunks ahead of slice 1, so that slice 1's
+// reads of the chunk inputs both slices load (q, k, g) still find them in the
+// L2; a pacing wait longer than kBwdPacePolls polls ends the pacing for the
+// rest of the walk (slice 1 not running yet: the grid is larger than the chip)
+constexpr int kBwdLead = 1;
+constexpr int kBwdPacePolls = 64;
 constexpr int kNV = 64;         // value columns per workgroup
 constexpr int kC = 16;          // tokens per chunk
 constexpr int kXCDs = 8;
@@ -451,6 +461,8 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     // and slice 0's; the flag poll of thread 0
     Part<DK> own, prev1, prev2, part;
     int flagv = 0;
+    int pacing = 1;            // slice 0, thread 0: still keeping pace with slice 1
+    int *progress = flags ? flags + nbh : nullptr;   // slice 1's finished chunks, per head
     if (t == 0)
         *abort_flag = 0;
 
@@ -473,6 +485,9 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         // the end of that chunk): publish the count of finished chunks
         if (publisher && t == 0 && ci + 1 < nchunks)
             __builtin_amdgcn_raw_buffer_store_b32(nchunks - 1 - ci, bwd_buffer(flags + bh, 4), 0, 0, 0);
+        // slice 1: the count of chunks it has finished (pacing only, no ordering)
+        if (summer && t == 0 && ci + 1 < nchunks)
+            __builtin_amdgcn_raw_buffer_store_b32(nchunks - 1 - ci, bwd_buffer(progress + bh, 4), 0, 0, 0);
         // ---- the chunk's incoming state and inputs (rows r >= n are zero) ---------
         pre.store(Ss, Qt, Kt, Pm, Xs, dOs, bet, t);
         // slice 1: poll slice 0's flag for chunk ci + 2 (published a chunk ago), the
@@ -483,6 +498,17 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (ci > 0)
             pre.load(q, k, v, g, beta, dO, states, ci - 1, T, H, DV, nbh, bh, tokb, h, col0, t);
+        // slice 0: wait (briefly) until slice 1 is at most kBwdLead chunks behind
+        if (publisher && t == 0 && pacing && nchunks - 1 - ci > kBwdLead) {
+            int polls = 0;
+            while (ld_flag_dev(progress + bh) < nchunks - 1 - ci - kBwdLead) {
+                if (++polls > kBwdPacePolls) {
+                    pacing = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
         __syncthreads();
 
         // ---- decay factors and operands: thread (c, part) owns key channel c for
@@ -943,7 +969,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
         }
 }
 
-// flags[i] = 0 for i < n (the slice-0 publication counters of one call)
+// flags[i] = 0 for i < n (the publication and progress counters of one call)
 __global__ __launch_bounds__(256) void zero_flags(int *flags, int n)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -973,7 +999,7 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g
     float *pb = nsl > 1 ? partials + 3 * rows * DK : dbeta;
     int *flags = nsl > 1 && rows > 0 ? reinterpret_cast<int *>(partials + ((rows * (3L * DK + 1) + 63) / 64) * 64) : nullptr;
     if (flags) {
-        hipLaunchKernelGGL(zero_flags, dim3((nbh + 255) / 256), dim3(256), 0, stream, flags, nbh);
+        hipLaunchKernelGGL(zero_flags, dim3((2 * nbh + 255) / 256), dim3(256), 0, stream, flags, 2 * nbh);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -993,9 +1019,9 @@ size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv)
     const long nchunks = (T + kC - 1) / kC;
     const long nsl = dv / kNV;
     const long states = nchunks * B * H * (long)dk * dv;      // fp32-sized: either dtype fits
-    // two value slices: slice 0's partial dq, dk, dg, dbeta and one flag per head
+    // two value slices: slice 0's partial dq, dk, dg, dbeta and two counters per head
     const long parts = nsl > 1 ? (long)B * T * H * (3L * dk + 1) : 0;
-    const long flags = nsl > 1 && T > 0 ? (long)B * H : 0;
+    const long flags = nsl > 1 && T > 0 ? 2L * B * H : 0;
     // each region rounded up to 64 floats (256 bytes)
     return (size_t)(((states + 63) / 64) * 64 + ((parts + 63) / 64) * 64 + ((flags + 63) / 64) * 64);
 }

@@ -373,9 +373,9 @@ size_t kda_chunk_fwd_gated_workspace_size(int B, int H, int dv);
  *               aligned; its contents on entry are ignored and on return
  *               unspecified.  It holds every chunk's incoming state (sized as
  *               fp32 for either dtype) and, for dv = 128, the first value
- *               slice's partial dq, dk, dg, dbeta and one flag per (sequence,
- *               head) through which the second slice's workgroup learns that
- *               they are complete
+ *               slice's partial dq, dk, dg, dbeta and two counters per (sequence,
+ *               head): one through which the second slice's workgroup learns
+ *               that they are complete, one that paces the first slice
  *   dk, dv (sizes) : 64 or 128
  * Gradients are fp32 in both dtype modes.  No output may overlap an input or
  * another output.  Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size,
