@@ -1,6 +1,7 @@
 """Benchmark of the KDA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py --sweep-heads 1,32,96,128,144   (prefill time against the head count)
 
 Timed phases, each W untimed steps then K timed steps bracketed by
 torch.cuda.synchronize():
@@ -37,6 +38,7 @@ prefill, and a sample of the decode batch; each records the host it ran on.
 Prints one JSON line.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -246,6 +248,10 @@ def main():
     ap.add_argument("--skip-bwd", action="store_true")
     ap.add_argument("--skip-configs", action="store_true",
                     help="skip the B4 H32 T4096 prefill and the 1M-token streaming legs")
+    ap.add_argument("--sweep-heads", type=str, default="", metavar="H1,H2,...",
+                    help="only time the prefill on B1 T65536 d128 bf16 for each head count "
+                         "(two workgroups per head: how the time grows as the grid fills the chip); "
+                         "one JSON line per head count")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch's device-to-device copy of MIB MiB, --steps times "
                          "(reference kernel for scaling HBM byte counters)")
@@ -276,6 +282,24 @@ def main():
                           "launches": args.steps}), flush=True)
         return
     binding.lib()
+
+    if args.sweep_heads:
+        base = WORKLOADS["k3_prefill"]
+        for Hs in [int(h) for h in args.sweep_heads.split(",")]:
+            sp = dataclasses.replace(base, H=Hs)
+            xs = prefill_inputs(sp, device=dev)
+            os_ = torch.empty((sp.B, sp.T, Hs, sp.dv), dtype=torch.bfloat16, device=dev)
+            ss = torch.empty((sp.B, Hs, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            _, kern = _timed(lambda i=0: binding.chunk_fwd(xs["q"], xs["k"], xs["v"], xs["g"], xs["beta"], xs["S0"],
+                                                           chunk=16, o=os_, S_T=ss), args.steps, args.warmup, torch)
+            by = prefill_bytes(sp.B, sp.T, Hs, sp.dk, sp.dv)
+            print(json.dumps({"sweep_heads": Hs, "workgroups": 2 * sp.B * Hs, "kernel_ms": kern,
+                              "gbps": by / (kern * 1e-3) / 1e9, "hbm_frac": by / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS}),
+                  flush=True)
+            del xs, os_, ss
+            torch.cuda.empty_cache()
+        return
 
     # ---------------- prefill --------------------------------------------------
     spec = WORKLOADS["k3_prefill"]
