@@ -449,7 +449,8 @@ def validate_inputs(g, beta):
 def workgroup_xcds(n, lds_bytes=0, device=None):
     """Debug check of the workgroup placement the fused launches assume: an int32
     tensor [n] whose element i is the XCD workgroup i of one n-workgroup launch (each
-    workgroup requesting lds_bytes of LDS) ran on; the fused launches expect i % 8."""
+    workgroup requesting lds_bytes of LDS) ran on; the fused launches expect xcd[i] == xcd[i % 8]
+    with xcd[0..7] all different (round-robin placement from any first XCD)."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     xcd = torch.full((max(int(n), 0),), -1, dtype=torch.int32, device=dev)
     _check(lib().kda_workgroup_xcds(_ptr(xcd) if n > 0 else None, int(n), int(lds_bytes), _stream(dev)))

@@ -45,6 +45,10 @@
 // partials of that chunk are in the shared L2, loads them (bypassing its own
 // L1), adds them in slice order and writes the gradients (no atomics: the
 // result is deterministic and the same as summing the slices afterwards).
+// Slice 0's last flag word also carries its XCD (bits [30:28]); slice 1 checks
+// it against its own, and if the two ran on different XCDs (where slice 1 could
+// have read stale partials from memory) or any wait gave up, slice 1 writes NaN
+// over all of its head's dq, dk, dg and dbeta.
 // Slice 1 also posts how many chunks it has finished, and slice 0 waits for it
 // to stay at most kBwdLead chunks ahead: slice 1's reads of the inputs both
 // slices load then find them in the L2 (without it slice 0, the faster of the
@@ -940,15 +944,19 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     if (nchunks > 0) {
         // the last published chunk (chunk 0), and slice 1's sums of chunks 1 and 0
         if (publisher && t == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(nchunks, bwd_buffer(flags + bh, 4), 0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(tag_xcd(nchunks, hw_xcd()), bwd_buffer(flags + bh, 4), 0, 0, 0);
         if (summer) {
             if (t == 0) {
                 int spins = 0;
-                while (*abort_flag == 0 && ld_flag_dev(flags + bh) < nchunks) {
+                int word = ld_flag_dev(flags + bh);
+                while (*abort_flag == 0 && word_count(word) < nchunks) {
                     if (++spins > spin_limit)
                         *abort_flag = 1;
                     __builtin_amdgcn_s_sleep(2);
+                    word = ld_flag_dev(flags + bh);
                 }
+                if (*abort_flag == 0 && word_xcd(word) != hw_xcd())
+                    *abort_flag = 1;
             }
             __syncthreads();
             const float mark = *abort_flag != 0 ? __builtin_nanf("") : 0.f;
@@ -960,6 +968,21 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
             const int n0 = T < kC ? T : kC;
             part.load(pq, pk, pg, pb, tokb, 0, n0, H, h, t);
             part.store_sum(prev1, oq, ok, og, ob, tokb, 0, n0, H, h, t, mark);
+            // a hand-off that failed anywhere in the walk: NaN over every row of the
+            // head, stored once all of the sums above have been acknowledged
+            if (*abort_flag != 0) {
+                __builtin_amdgcn_s_waitcnt(kVmcntZero);
+                __syncthreads();
+                const float nan = __builtin_nanf("");
+                for (long e = t; e < (long)T * DK; e += kBT) {
+                    const long row = ((tokb + e / DK) * H + h) * DK + e % DK;
+                    oq[row] = nan;
+                    ok[row] = nan;
+                    og[row] = nan;
+                }
+                for (int e = t; e < T; e += kBT)
+                    ob[(tokb + e) * H + h] = nan;
+            }
         }
     }
     if (dS0_out)

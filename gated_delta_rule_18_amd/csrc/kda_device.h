@@ -110,12 +110,12 @@ __device__ __forceinline__ float gate_elem(float o, float gt, float r, float w)
 }
 
 // The XCD (accelerator complex die) the calling wavefront runs on: hardware
-// register 20 (XCC_ID), bits [3:0].  Workgroup i of a launch runs on XCD i mod 8
-// on this part (measured for every workgroup of a 1024-workgroup grid), which the
-// hand-offs between workgroups rely on to share an L2.  The prefill's hand-off
-// words carry their writer's XCD in bits [30:28] so that the reader checks the
-// assumption (and marks its results NaN) instead of reading another L2's stale
-// data.
+// register 20 (XCC_ID), bits [3:0].  A launch's workgroups go round-robin over
+// the 8 XCDs of this part, so workgroups i and i + 8 share one XCD and its L2,
+// which the hand-offs between workgroups rely on (which XCD takes workgroup 0
+// varies from launch to launch).  Hand-off words carry their writer's XCD in bits
+// [30:28] so that the reader checks the assumption (and marks its results NaN)
+// instead of reading another L2's stale data.
 __device__ __forceinline__ int hw_xcd() { return (int)__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); }
 constexpr int kXcdShift = 28;
 constexpr int kCountMask = (1 << kXcdShift) - 1;

@@ -683,7 +683,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     int id = blockIdx.x;
     if constexpr (PROJ) {
         if (id < pa.nprep) {
-            // nprep is a multiple of 8: prep worker id runs on XCD id % 8
+            // nprep is a multiple of 8: prep worker id shares the XCD of every id' = id mod 8
             if (DV == 128)
                 prep_worker<E, DK, 128>(const_cast<E *>(q), const_cast<E *>(k), const_cast<E *>(v),
                                         const_cast<E *>(g), const_cast<E *>(beta), pa, id % kXCDs, id / kXCDs,
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(64 * (4 + Np<E>::v)) void prefill_ws_kernel(
     const int xcd = id % kXCDs, rr = id / kXCDs;
     if constexpr (GATED) {
         if (id >= grid_p) {
-            // grid_p is a multiple of 8: worker j = id - grid_p runs on XCD j % 8
+            // grid_p is a multiple of 8: worker j = id - grid_p shares the XCD of every id' = j mod 8
             const int waves = 4 + L::NP, j = id - grid_p;
             const int jw = (j / kXCDs) * waves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
             const int nw = (ngate / kXCDs) * waves;

@@ -244,8 +244,8 @@ int kda_prefill_prep(const void *q_pre, const void *k_pre, const void *v_pre,
  *   opts       : NULL = defaults, else as kda_chunk_fwd_ex (spin_limit also bounds
  *                the prefill's waits for the preprocessing; a prefill workgroup
  *                whose tile flag shows a preprocessing workgroup on another XCD --
- *                the launch assumes workgroup i runs on XCD i mod 8 -- marks its
- *                outputs NaN like a wait that gave up)
+ *                the launch assumes workgroups i and i + 8 share an XCD -- marks
+ *                its outputs NaN like a wait that gave up)
  * Errors: as kda_prefill_prep and kda_chunk_fwd; KDA_ERR_INVALID also for a null,
  * misaligned or short workspace, spin_limit < -1, or o, S_T or the workspace
  * overlapping any other buffer (S_T = S0 allowed).
@@ -332,8 +332,8 @@ int kda_decode_step_gated(const void *q_pre, const void *k_pre, const void *v_pr
  *               workspaces.
  *   opts      : NULL = defaults, else as kda_chunk_fwd_ex; spin_limit bounds the
  *               gate's waits for the prefill too, and a block whose wait gave up
- *               is written as NaN.  The hand-off assumes workgroup i runs on XCD
- *               i mod 8 (so that its L2 holds what it reads); a block whose
+ *               is written as NaN.  The hand-off assumes workgroups i and i + 8
+ *               share an XCD (so that its L2 holds what it reads); a block whose
  *               progress words show another XCD is written as NaN too.
  * Errors: as kda_chunk_fwd; KDA_ERR_INVALID also for a null or misaligned gate or
  * workspace, a workspace below the size above, a misaligned norm_w, a bad eps,
@@ -378,8 +378,12 @@ size_t kda_chunk_fwd_gated_workspace_size(int B, int H, int dv);
  *               that they are complete, one that paces the first slice
  *   dk, dv (sizes) : 64 or 128
  * Gradients are fp32 in both dtype modes.  No output may overlap an input or
- * another output.  Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size,
- * workspace too small, overlap), KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH.
+ * another output.  With dv = 128 the two value slices of a head hand partial
+ * sums to each other through an XCD's L2; should the second find the first on
+ * another XCD, or wait for it past the built-in limit, all of that head's dq,
+ * dk, dg and dbeta are NaN (dv, dS0 stay exact).
+ * Errors: KDA_ERR_INVALID (null/misaligned pointer, bad size, workspace too
+ * small, overlap), KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH.
  */
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
                   const void *beta, const float *S0, const void *dO, const float *dS_T,
@@ -448,8 +452,11 @@ const char *kda_strerror(int status);
  *
  * The launches whose workgroups hand data to each other through the L2
  * (kda_chunk_fwd_gated, kda_chunk_fwd_from_proj, and kda_chunk_bwd with dv = 128)
- * assume that workgroup i of a launch runs on XCD (accelerator die) i mod 8, so
- * that a writer and its readers share that die's L2.  This enqueues one launch
+ * assume that a launch's workgroups go round-robin over the 8 XCDs (accelerator
+ * dies), so that workgroups i and i + 8 -- a writer and its readers -- share a
+ * die's L2; which XCD takes workgroup 0 varies between launches.  Each of them
+ * checks the assumption at run time (hand-off words carry the writer's XCD) and
+ * marks its outputs NaN where it fails.  This enqueues one launch
  * of n workgroups, each requesting lds_bytes of dynamic LDS (as those kernels
  * do), in which workgroup i writes the XCD it ran on to xcd[i].
  *   xcd       : device int32 [n], written
