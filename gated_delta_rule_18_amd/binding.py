@@ -28,7 +28,7 @@ library_path = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_FP32 = 0, 1
 KDA_OK, KDA_ERR_INVALID, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 NOALLOC_SCRATCH_BYTES = 64 << 20      # KDA_NOALLOC_SCRATCH_BYTES
-EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
+EXPORTS = ("kda_chunk_bwd", "kda_chunk_bwd_ex", "kda_chunk_bwd_noalloc", "kda_chunk_bwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_ex",
            "kda_chunk_fwd_from_proj", "kda_chunk_fwd_from_proj_workspace_size", "kda_chunk_fwd_gated",
            "kda_chunk_fwd_gated_workspace_size", "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_output_gate", "kda_prefill_prep", "kda_strerror",
@@ -40,6 +40,11 @@ _lib = None
 class FwdOptions(ctypes.Structure):
     """struct kda_fwd_options of kda.h."""
     _fields_ = [("spin_limit", ctypes.c_int)]
+
+
+class BwdOptions(ctypes.Structure):
+    """struct kda_bwd_options of kda.h."""
+    _fields_ = [("fail_xcd_check", ctypes.c_int)]
 
 
 class KdaError(RuntimeError):
@@ -80,6 +85,8 @@ def lib():
                                             + [i] * 6 + [vp])
         L.kda_chunk_bwd.restype = i
         L.kda_chunk_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t] + [i] * 6 + [vp]
+        L.kda_chunk_bwd_ex.restype = i
+        L.kda_chunk_bwd_ex.argtypes = [vp] * 15 + [ctypes.c_size_t] + [i] * 6 + [ctypes.POINTER(BwdOptions), vp]
         L.kda_chunk_bwd_noalloc.restype = i
         L.kda_chunk_bwd_noalloc.argtypes = [vp] * 14 + [i] * 6 + [vp]
         L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
@@ -317,11 +324,12 @@ def _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T, return_dS0, out):
     return (B, T, H, dk, dv), code, tuple(out)
 
 
-def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=None):
+def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=None, fail_xcd_check=False):
     """Gradients of <dO, o> + <dS_T, S_T> through chunk_fwd.  Inputs as chunk_fwd plus
     dO [B,T,H,dv] (input dtype) and dS_T [B,H,dk,dv] fp32 or None (zero).  Returns fp32
     (dq, dk, dv, dg, dbeta, dS0); dS0 is None when return_dS0 is False.  `workspace`
-    may supply a uint8 device tensor of at least workspace_size(...) bytes."""
+    may supply a uint8 device tensor of at least workspace_size(...) bytes.
+    fail_xcd_check (testing): see kda_chunk_bwd_ex."""
     (B, T, H, dk, dv), code, (dq, dk_, dv_, dg, db, dS0) = _bwd_outputs(q, k, v, g, beta, S0, dO, dS_T,
                                                                           return_dS0, None)
     dev = q.device
@@ -330,9 +338,13 @@ def chunk_bwd(q, k, v, g, beta, S0, dO, dS_T=None, return_dS0=True, workspace=No
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < need or workspace.device != dev:
         raise ValueError(f"workspace: need {need} bytes on {dev}")
-    rc = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
-                             _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace),
-                             int(workspace.numel()), B, T, H, dk, dv, code, _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_T),
+            _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(db), _ptr(dS0), _ptr(workspace),
+            int(workspace.numel()), B, T, H, dk, dv, code)
+    if fail_xcd_check:
+        rc = lib().kda_chunk_bwd_ex(*args, ctypes.byref(BwdOptions(fail_xcd_check=1)), _stream(dev))
+    else:
+        rc = lib().kda_chunk_bwd(*args, _stream(dev))
     _check(rc)
     return dq, dk_, dv_, dg, db, dS0
 

@@ -166,7 +166,8 @@ int decode_step(const void *q_pre, const void *k_pre, const void *v_pre, const f
 int chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
               const float *S0, const void *dO, const float *dS_T, float *dq, float *dk, float *dv,
               float *dg, float *dbeta, float *dS0, void *workspace, size_t workspace_bytes, int B,
-              int T, int H, int dk_size, int dv_size, int dtype, void *stream, bool library_scratch)
+              int T, int H, int dk_size, int dv_size, int dtype, void *stream, bool library_scratch,
+              int xcd_flip = 0)
 {
     if (B < 0 || T < 0 || H < 0 || dk_size <= 0 || dv_size <= 0)
         return KDA_ERR_INVALID;
@@ -226,7 +227,7 @@ int chunk_bwd(const void *q, const void *k, const void *v, const void *g, const 
     }
     hipError_t e = kda::launch_chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0,
                                          static_cast<float *>(workspace), B, T, H, dk_size, dv_size,
-                                         dtype == KDA_FP32, reinterpret_cast<hipStream_t>(stream));
+                                         dtype == KDA_FP32, xcd_flip, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -422,6 +423,17 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, co
 {
     return chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
                      workspace_bytes, B, T, H, dk_size, dv_size, dtype, stream, false);
+}
+
+int kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                     const float *S0, const void *dO, const float *dS_T, float *dq, float *dk,
+                     float *dv, float *dg, float *dbeta, float *dS0, void *workspace,
+                     size_t workspace_bytes, int B, int T, int H, int dk_size, int dv_size, int dtype,
+                     const kda_bwd_options *opts, void *stream)
+{
+    return chunk_bwd(q, k, v, g, beta, S0, dO, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+                     workspace_bytes, B, T, H, dk_size, dv_size, dtype, stream, false,
+                     opts && opts->fail_xcd_check ? 1 : 0);
 }
 
 int kda_chunk_bwd_noalloc(const void *q, const void *k, const void *v, const void *g,

@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
     const float *__restrict__ dST, const E *__restrict__ states, float *__restrict__ dv_out,
     float *__restrict__ dS0_out, float *pq, float *pk, float *pg, float *pb, float *__restrict__ oq,
     float *__restrict__ ok, float *__restrict__ og, float *__restrict__ ob, int *flags, int T, int H, int DV,
-    int nbh, int nsl, int spin_limit)
+    int nbh, int nsl, int spin_limit, int xcd_flip)
 {
     typedef BwdL<DK> L;
     extern __shared__ __align__(16) float sm[];
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(kBT) void bwd_kernel(
                     __builtin_amdgcn_s_sleep(2);
                     word = ld_flag_dev(flags + bh);
                 }
-                if (*abort_flag == 0 && word_xcd(word) != hw_xcd())
+                if (*abort_flag == 0 && word_xcd(word) != (hw_xcd() ^ xcd_flip))
                     *abort_flag = 1;
             }
             __syncthreads();
@@ -1004,7 +1004,7 @@ template <typename E, int DK>
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                       const void *dO, const float *dST, float *states, float *dq,
                       float *dk, float *dv, float *dg, float *dbeta, float *dS0, float *partials, int B,
-                      int T, int H, int DV, hipStream_t stream)
+                      int T, int H, int DV, int xcd_flip, hipStream_t stream)
 {
     typedef BwdL<DK> L;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
@@ -1031,7 +1031,7 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *g
     hipLaunchKernelGGL((bwd_kernel<E, DK>), dim3(grid), dim3(kBT), L::bytes, stream, (const E *)q,
                        (const E *)k, (const E *)v, (const E *)g, (const E *)beta, (const E *)dO, dST,
                        (const E *)states, dv, dS0, pq, pk, pg, pb, dq, dk, dg, dbeta, flags, T, H, DV, nbh, nsl,
-                       kBwdSpinLimit);
+                       kBwdSpinLimit, xcd_flip);
     return hipGetLastError();
 }
 
@@ -1076,7 +1076,7 @@ hipError_t noalloc_scratch(float **ptr)
 hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                             const float *S0, const void *dO, const float *dST, float *dq, float *dk,
                             float *dv, float *dg, float *dbeta, float *dS0, float *workspace, int B, int T,
-                            int H, int DK, int DV, bool fp32, hipStream_t stream)
+                            int H, int DK, int DV, bool fp32, int xcd_flip, hipStream_t stream)
 {
     const long nchunks = (T + kC - 1) / kC;
     const long sfl = nchunks * B * H * (long)DK * DV;
@@ -1101,13 +1101,13 @@ hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const v
     // 2. the reverse walk (and the slice sums)
     if (fp32)
         return DK == 128 ? launch_bwd<float, 128>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
-                                                   dS0, partials, B, T, H, DV, stream)
+                                                   dS0, partials, B, T, H, DV, xcd_flip, stream)
                          : launch_bwd<float, 64>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
-                                                 dS0, partials, B, T, H, DV, stream);
+                                                 dS0, partials, B, T, H, DV, xcd_flip, stream);
     return DK == 128 ? launch_bwd<__bf16, 128>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
-                                                dS0, partials, B, T, H, DV, stream)
+                                                dS0, partials, B, T, H, DV, xcd_flip, stream)
                      : launch_bwd<__bf16, 64>(q, k, v, g, beta, dO, dST, states, dq, dk, dv, dg, dbeta,
-                                              dS0, partials, B, T, H, DV, stream);
+                                              dS0, partials, B, T, H, DV, xcd_flip, stream);
 }
 
 } // namespace kda

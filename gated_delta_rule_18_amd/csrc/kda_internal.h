@@ -89,7 +89,7 @@ size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);
 hipError_t launch_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
                             const float *S0, const void *dO, const float *dST, float *dq, float *dk,
                             float *dv, float *dg, float *dbeta, float *dS0, float *workspace, int B, int T,
-                            int H, int DK, int DV, bool fp32, hipStream_t stream);
+                            int H, int DK, int DV, bool fp32, int xcd_flip, hipStream_t stream);
 
 // The library's own backward workspace, for callers that cannot allocate: a
 // device array of kNoallocScratchBytes in every GPU's memory (one copy per

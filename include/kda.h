@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 141 /* 1.4.1 */
+#define KDA_VERSION 150 /* 1.5.0 */
 
 enum kda_dtype {
     KDA_BF16 = 0, /* bf16 activations, fp32 state */
@@ -390,6 +390,26 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g,
                   float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
                   void *workspace, size_t workspace_bytes,
                   int B, int T, int H, int dk_size, int dv_size, int dtype, void *stream);
+
+/*
+ * kda_chunk_bwd_ex -- kda_chunk_bwd with options, for testing the failure
+ * marking of the two value slices' hand-off (dv = 128).
+ *   opts : NULL = kda_chunk_bwd; else fail_xcd_check != 0 makes the second
+ *          slice of every head take the first for one on another XCD, so that
+ *          all of the head's dq, dk, dg and dbeta come out NaN while dv and dS0
+ *          stay exact (the path a real mismatch or a wait that gave up takes).
+ * Errors: as kda_chunk_bwd.
+ */
+typedef struct kda_bwd_options {
+    int fail_xcd_check;
+} kda_bwd_options;
+
+int kda_chunk_bwd_ex(const void *q, const void *k, const void *v, const void *g,
+                     const void *beta, const float *S0, const void *dO, const float *dS_T,
+                     float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                     void *workspace, size_t workspace_bytes,
+                     int B, int T, int H, int dk_size, int dv_size, int dtype,
+                     const kda_bwd_options *opts, void *stream);
 
 /* Bytes of workspace kda_chunk_bwd needs for these sizes (0 for invalid sizes). */
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk_size, int dv_size);

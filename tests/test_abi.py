@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert binding.version() == 141
+    assert binding.version() == 150
     L = binding.lib()
     for code in (0, -1, -2, -3, -4, 17):
         assert isinstance(L.kda_strerror(code), bytes) and L.kda_strerror(code)

@@ -118,3 +118,24 @@ def test_backward_grid_larger_than_the_chip(gpu, B, H, T):
     spec = PrefillSpec(B=B, H=H, T=T, dk=128, dv=128, seed=700 + H)
     heads = [(0, 0), (0, 7), (B // 2, H // 2), (B - 1, H - 9), (B - 1, H - 1)]
     _check(spec, gpu, heads=heads, what=f"B{B} H{H} T{T} ({B * H * 2} workgroups)")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_failed_handoff_marks_the_head_nan(gpu, dtype):
+    """The failure path of the value slices' hand-off, forced from the host through
+    kda_chunk_bwd_ex (the second slice takes the first for one on another XCD): every
+    dq, dk, dg, dbeta of a two-slice head is NaN, while dv and dS0, which each slice
+    writes itself, equal the normal call's bit for bit; every kernel exits normally."""
+    spec = PrefillSpec(B=2, H=3, T=100, dk=128, dv=128, dtype=dtype, seed=140)
+    x = prefill_inputs(spec, device=gpu)
+    gr = backward_inputs(spec, device=gpu)
+    args = (x["q"], x["k"], x["v"], x["g"], x["beta"], x["S0"], gr["dO"], gr["dS_T"])
+    good = binding.chunk_bwd(*args)
+    bad = binding.chunk_bwd(*args, fail_xcd_check=True)
+    torch.cuda.synchronize()
+    for name, t in zip(("dq", "dk", "dg", "dbeta"), (bad[0], bad[1], bad[3], bad[4])):
+        assert torch.isnan(t).all(), f"{name}: {int((~torch.isnan(t)).sum())} values not NaN"
+    assert torch.equal(bad[2], good[2]), "dv changed"
+    assert torch.equal(bad[5], good[5]), "dS0 changed"
+    assert not any(torch.isnan(t).any() for t in good), "the normal call marked NaN"
+    print(f"failed hand-off ({dtype}): dq, dk, dg, dbeta all NaN; dv, dS0 exact", flush=True)
